@@ -1,0 +1,156 @@
+/*
+ * zc.h -- C ABI of libzc: lossless bf16 exponent-coding codec for MI355X.
+ *
+ * The operation: ZipCCL (arXiv 2604.27844), abstract, techniques (1) and (2).
+ * Each bf16 value is split into a sign+mantissa byte, stored as is, and an
+ * 8-bit exponent.  The exponent is coded, relative to the largest exponent of
+ * its 128-value group, with a fixed canonical prefix code whose lengths come
+ * from the closed-form exponent law of a zero-mean Gaussian (no run-time
+ * statistics).  An escape symbol and a per-group raw mode keep any input
+ * lossless.  A 16-bit Gaussian value shrinks to about 11 bits (pith.science,
+ * Figure 6 caption).
+ *
+ * Buffers are pre-partitioned into per-destination chunks (the pages'
+ * communication-aware layout, abstract technique (2)): chunk c holds counts[c]
+ * values, chunks lie back to back in the uncompressed buffer, and each chunk
+ * is compressed into its own self-describing ZCB1 stream, so it can be sent
+ * and decoded on its own (compress before the collective, decompress after
+ * it: shd-paper.top summary, technical framework).
+ *
+ * ZCB1 stream of one chunk of n values (offsets from the stream start, all
+ * fields little-endian; T = ceil(n / 8192) tiles, 64 groups per tile):
+ *   0          header: u32 magic 0x3142435A, u16 version 1, u16 table_id 1,
+ *              u32 flags 0, u32 reserved 0, u64 n, u64 comp_bytes
+ *   32         u32 tile_off[T]  byte offset of each tile's exponent stream
+ *   32 + 4T    u8  emax[64T]    largest exponent of each group
+ *   32 + 68T   u16 glen[64T]    bits of each group's exponent stream
+ *   R          u8  raw[n]       sign<<7 | mantissa,  R = align16(32 + 196T)
+ *   X          exponent streams, most significant bit first inside
+ *              little-endian u32 words, one zero-padded word run per tile,
+ *              X = align16(R + n)
+ * Group l of tile t owns the values 8192t + 512k + 8l + j (k = 0..15,
+ * j = 0..7) that are < n, in that order.  Gap and pad bytes are zero.
+ *
+ * Slot layout: chunk c's stream starts at
+ *   slot_off[c] = sum over c' < c of align256(zc_chunk_bound(counts[c'])).
+ *
+ * All calls are thread-safe and keep no state between calls.  The library
+ * allocates no memory: the caller owns every buffer.  GPU calls are
+ * asynchronous on the given stream (a hipStream_t; NULL is the null stream).
+ */
+#ifndef ZC_H
+#define ZC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ZC_OK = 0,
+    ZC_EINVAL = -1,    /* bad argument: null pointer, negative count,
+                          misaligned buffer, too many values per chunk     */
+    ZC_ENOSPC = -2,    /* output capacity or workspace too small          */
+    ZC_ECORRUPT = -3,  /* a stream failed validation (decoder status)     */
+    ZC_EHIP = -4       /* a HIP runtime call failed                       */
+} zc_status_t;
+
+/* Largest count per chunk (values). */
+#define ZC_MAX_CHUNK_VALUES 2147483647LL
+
+/*
+ * Worst-case bytes of the ZCB1 stream of one chunk of n values (every group
+ * in raw mode): X + n + 4T.  Host only; returns 0 for n < 0.
+ */
+size_t zc_chunk_bound(int64_t n);
+
+/*
+ * Bytes of a slot-layout buffer for num_chunks chunks: the sum of
+ * align256(zc_chunk_bound(counts[c])).  counts is a host array.  Returns 0
+ * if an argument is invalid.
+ */
+size_t zc_bound(const int64_t* counts, int32_t num_chunks);
+
+/*
+ * Device workspace bytes that zc_compress needs for these counts (look-back
+ * status words and work counters).  Host only.
+ */
+size_t zc_workspace_bytes(const int64_t* counts, int32_t num_chunks);
+
+/*
+ * Compress num_chunks chunks (ZipCCL abstract, techniques (1)-(2)).
+ *   d_in          device, bf16 bit patterns, chunks back to back in counts
+ *                 order; 2-byte aligned (16-byte aligned chunk starts take
+ *                 the vector path)
+ *   counts        host, values per chunk, 0 <= counts[c] <= ZC_MAX_CHUNK_VALUES
+ *   d_out         device, 16-byte aligned, out_capacity >= zc_bound(...);
+ *                 chunk c's stream is written at slot_off[c]; bytes after a
+ *                 stream's end inside its slot are left unwritten
+ *   d_comp_sizes  device int64[num_chunks]: comp_bytes of each stream
+ *   d_ws          device workspace of ws_bytes >= zc_workspace_bytes(...),
+ *                 4-byte aligned; its contents need not be initialised
+ *   stream        hipStream_t the work is queued on
+ * Returns ZC_OK once the work is queued, or an error before anything is
+ * queued (ZC_EINVAL, ZC_ENOSPC) or when a launch fails (ZC_EHIP).  Calls that
+ * share a workspace must be ordered on one stream.
+ */
+int zc_compress(const uint16_t* d_in, const int64_t* counts,
+                int32_t num_chunks, void* d_out, size_t out_capacity,
+                int64_t* d_comp_sizes, void* d_ws, size_t ws_bytes,
+                void* stream);
+
+/*
+ * Decompress num_chunks ZCB1 streams back to bf16 (strict: a stream is
+ * accepted only if it is the exact output of zc_compress for its values).
+ *   d_in        device, in_bytes readable bytes holding the streams
+ *   in_offsets  host int64[num_chunks]: byte offset of stream c in d_in, each
+ *               a multiple of 16; NULL means the slot layout
+ *   counts      host, expected values per chunk (must match each header)
+ *   d_out       device, sum(counts) bf16 values written back to back
+ *   d_status    device int32, must be 0 on entry.  After the stream has run
+ *               it is 0 if every stream was valid; otherwise it holds
+ *               (reason << 24) | chunk for one failed check, reason >= 1
+ *               (see zc_strerror of ZC_ECORRUPT; the reasons are listed with
+ *               ZC_REASON_*).  Output values of a corrupt chunk are undefined,
+ *               but nothing is read outside [offset, offset + comp_bytes) of
+ *               a stream (nor past in_bytes) and nothing is written outside
+ *               that chunk's part of d_out.
+ *   stream      hipStream_t
+ * Returns ZC_OK once queued; ZC_EINVAL / ZC_EHIP as for zc_compress.
+ */
+int zc_decompress(const void* d_in, size_t in_bytes,
+                  const int64_t* in_offsets, const int64_t* counts,
+                  int32_t num_chunks, uint16_t* d_out, int32_t* d_status,
+                  void* stream);
+
+/* Reasons reported through d_status (bits 24..30). */
+#define ZC_REASON_HEADER 1    /* magic, version, table, flags or n         */
+#define ZC_REASON_SIZE 2      /* comp_bytes or a stream beyond the data    */
+#define ZC_REASON_GAP 3       /* nonzero gap byte                          */
+#define ZC_REASON_TILE 4      /* tile_off is not the running sum           */
+#define ZC_REASON_GROUP 5     /* glen > 8 n_g, or empty group with emax != 0 */
+#define ZC_REASON_SYMBOL 6    /* no code word fits, or d > E_max           */
+#define ZC_REASON_ESCAPE 7    /* escaped exponent within 16 of E_max       */
+#define ZC_REASON_LENGTH 8    /* coded group does not use exactly glen bits */
+#define ZC_REASON_EMAX 9      /* decoded maximum differs from E_max        */
+#define ZC_REASON_RAWMODE 10  /* raw group whose coded form is shorter     */
+#define ZC_REASON_PADDING 11  /* nonzero pad bit                           */
+
+/* Static text for a zc_status_t value. */
+const char* zc_strerror(int code);
+
+/*
+ * The library's code table for table_id 1, regenerated on the host from the
+ * closed-form law and checked against the table compiled into the kernels.
+ * lengths[17] and codes[17] (d = 0..15, then ESC); prob[17] may be NULL.
+ * Returns ZC_OK, or ZC_EINVAL for another table_id or a self-check mismatch.
+ */
+int zc_code_table(int32_t table_id, int32_t* lengths, uint32_t* codes,
+                  double* prob);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ZC_H */

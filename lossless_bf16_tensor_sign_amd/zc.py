@@ -1,0 +1,172 @@
+"""Python binding of libzc (the C ABI in include/zc.h).
+
+Same names as the C entry points; this module only marshals pointers, sizes
+and the current HIP stream.  Every step of compression and decompression runs
+in the library's gfx950 kernels.  PyTorch provides device memory and streams.
+There is no fallback: if libzc.so is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzc.so")
+
+ZC_OK, ZC_EINVAL, ZC_ENOSPC, ZC_ECORRUPT, ZC_EHIP = 0, -1, -2, -3, -4
+REASONS = {
+    1: "HEADER", 2: "SIZE", 3: "GAP", 4: "TILE", 5: "GROUP", 6: "SYMBOL",
+    7: "ESCAPE", 8: "LENGTH", 9: "EMAX", 10: "RAWMODE", 11: "PADDING",
+}
+
+_lib = None
+
+
+class ZcError(RuntimeError):
+    def __init__(self, code, what=""):
+        super().__init__("%s: %s (%d)" % (what, zc_strerror(code), code))
+        self.code = code
+
+
+def lib():
+    """The loaded libzc.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libzc.so is not built (run __graft_entry__.build() or "
+                "python lossless_bf16_tensor_sign_amd/build.py)")
+        L = ct.CDLL(LIB_PATH)
+        i64p = ct.POINTER(ct.c_int64)
+        L.zc_chunk_bound.argtypes = [ct.c_int64]
+        L.zc_chunk_bound.restype = ct.c_size_t
+        L.zc_bound.argtypes = [i64p, ct.c_int32]
+        L.zc_bound.restype = ct.c_size_t
+        L.zc_workspace_bytes.argtypes = [i64p, ct.c_int32]
+        L.zc_workspace_bytes.restype = ct.c_size_t
+        L.zc_compress.argtypes = [ct.c_void_p, i64p, ct.c_int32, ct.c_void_p,
+                                  ct.c_size_t, ct.c_void_p, ct.c_void_p,
+                                  ct.c_size_t, ct.c_void_p]
+        L.zc_compress.restype = ct.c_int
+        L.zc_decompress.argtypes = [ct.c_void_p, ct.c_size_t, i64p, i64p,
+                                    ct.c_int32, ct.c_void_p, ct.c_void_p,
+                                    ct.c_void_p]
+        L.zc_decompress.restype = ct.c_int
+        L.zc_strerror.argtypes = [ct.c_int]
+        L.zc_strerror.restype = ct.c_char_p
+        L.zc_code_table.argtypes = [ct.c_int32, ct.POINTER(ct.c_int32),
+                                    ct.POINTER(ct.c_uint32),
+                                    ct.POINTER(ct.c_double)]
+        L.zc_code_table.restype = ct.c_int
+        _lib = L
+    return _lib
+
+
+def _counts(counts):
+    a = np.ascontiguousarray(np.asarray(counts, dtype=np.int64).reshape(-1))
+    return a, a.ctypes.data_as(ct.POINTER(ct.c_int64))
+
+
+def _ptr(t):
+    return None if t is None else ct.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ct.c_void_p(stream.cuda_stream)
+
+
+# ----------------------------------------------------------- C entry points
+
+def zc_chunk_bound(n: int) -> int:
+    return int(lib().zc_chunk_bound(int(n)))
+
+
+def zc_bound(counts) -> int:
+    a, p = _counts(counts)
+    return int(lib().zc_bound(p, len(a)))
+
+
+def zc_workspace_bytes(counts) -> int:
+    a, p = _counts(counts)
+    return int(lib().zc_workspace_bytes(p, len(a)))
+
+
+def zc_strerror(code: int) -> str:
+    return lib().zc_strerror(int(code)).decode()
+
+
+def zc_code_table(table_id: int = 1):
+    """(lengths, codes, probabilities) of the library's table."""
+    ln = (ct.c_int32 * 17)()
+    cd = (ct.c_uint32 * 17)()
+    pr = (ct.c_double * 17)()
+    r = lib().zc_code_table(table_id, ln, cd, pr)
+    if r != ZC_OK:
+        raise ZcError(r, "zc_code_table")
+    return (np.array(list(ln), np.int32), np.array(list(cd), np.uint32),
+            np.array(list(pr), np.float64))
+
+
+def zc_compress(d_in, counts, d_out, d_comp_sizes, d_ws, stream=None,
+                out_capacity=None, ws_bytes=None) -> int:
+    """Queue compression; tensors are device tensors (uint8 / int64)."""
+    a, p = _counts(counts)
+    cap = d_out.numel() * d_out.element_size() if out_capacity is None else out_capacity
+    wsb = d_ws.numel() * d_ws.element_size() if ws_bytes is None else ws_bytes
+    return int(lib().zc_compress(_ptr(d_in), p, len(a), _ptr(d_out), cap,
+                                 _ptr(d_comp_sizes), _ptr(d_ws), wsb,
+                                 _stream(stream)))
+
+
+def zc_decompress(d_in, counts, d_out, d_status, in_offsets=None,
+                  stream=None, in_bytes=None) -> int:
+    """Queue decompression; d_status (int32 device) must hold 0."""
+    a, p = _counts(counts)
+    nb = d_in.numel() * d_in.element_size() if in_bytes is None else in_bytes
+    if in_offsets is not None:
+        off, op = _counts(in_offsets)
+    else:
+        off, op = None, None
+    return int(lib().zc_decompress(_ptr(d_in), nb, op, p, len(a), _ptr(d_out),
+                                   _ptr(d_status), _stream(stream)))
+
+
+# ------------------------------------------------ allocating conveniences
+
+def compress(x, counts, stream=None):
+    """Compress a device tensor of bf16 (or its uint16/int16 bits).
+
+    Returns (slot-layout uint8 buffer, int64 device sizes)."""
+    import torch
+    a, _ = _counts(counts)
+    dev = x.device
+    out = torch.empty(max(zc_bound(a), 16), dtype=torch.uint8, device=dev)
+    sizes = torch.empty(max(len(a), 1), dtype=torch.int64, device=dev)
+    ws = torch.empty(max(zc_workspace_bytes(a), 8), dtype=torch.uint8, device=dev)
+    r = zc_compress(x, a, out, sizes, ws, stream=stream)
+    if r != ZC_OK:
+        raise ZcError(r, "zc_compress")
+    return out, sizes[:len(a)]
+
+
+def decompress(buf, counts, in_offsets=None, stream=None, check=True):
+    """Decode streams back to a uint16 device tensor of sum(counts) values."""
+    import torch
+    a, _ = _counts(counts)
+    out = torch.empty(max(int(a.sum()), 1), dtype=torch.int16, device=buf.device)
+    status = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    r = zc_decompress(buf, a, out, status, in_offsets=in_offsets, stream=stream)
+    if r != ZC_OK:
+        raise ZcError(r, "zc_decompress")
+    out = out[:int(a.sum())]
+    if check:
+        st = int(status.item())
+        if st != 0:
+            raise ZcError(ZC_ECORRUPT, "zc_decompress: %s in chunk %d"
+                          % (REASONS.get(st >> 24, st >> 24), st & 0xFFFFFF))
+    return out, status

@@ -1,0 +1,97 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point include/zc.h declares, and its host-only functions (sizes, code table,
+argument validation) agree with the oracle."""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from lossless_bf16_tensor_sign_amd import zc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "zc.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(zc_\w+)\s*\(",
+                                 src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"zc_compress", "zc_decompress", "zc_bound", "zc_chunk_bound",
+            "zc_workspace_bytes", "zc_strerror", "zc_code_table"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", zc.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    lib = zc.lib()
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_bounds_match_oracle(oracle):
+    for n in [0, 1, 7, 8, 511, 8191, 8192, 8193, 1 << 20, 1 << 22, 29_417_472,
+              (1 << 31) - 1]:
+        assert zc.zc_chunk_bound(n) == oracle.chunk_bound(n), n
+    assert zc.zc_chunk_bound(-1) == 0
+    rng = np.random.default_rng(0)
+    for _ in range(20):
+        cnt = rng.integers(0, 50000, size=int(rng.integers(1, 200)))
+        cnt[rng.random(cnt.size) < 0.2] = 0
+        assert zc.zc_bound(cnt) == oracle.slot_offsets(cnt)[1]
+    assert zc.zc_bound([5, -1]) == 0
+
+
+def test_workspace_bytes():
+    assert zc.zc_workspace_bytes([0]) == 256 + 8
+    assert zc.zc_workspace_bytes([8193, 1]) == 256 + 8 * 3
+    # more than 64 chunks: the per-launch maximum of tiles
+    cnt = [8192] * 64 + [3 * 8192]
+    assert zc.zc_workspace_bytes(cnt) == 256 + 8 * 64
+
+
+def test_code_table_matches_oracle(oracle):
+    L, C, P = zc.zc_code_table(1)
+    p, l, c = oracle.table(1)
+    assert np.array_equal(L, l) and np.array_equal(C, c)
+    assert np.allclose(P, p, rtol=1e-12, atol=0)
+    with pytest.raises(zc.ZcError):
+        zc.zc_code_table(2)
+
+
+def test_argument_errors_before_any_gpu_work():
+    lib = zc.lib()
+    import ctypes as ct
+    cnt = np.array([10, -1], np.int64)
+    p = cnt.ctypes.data_as(ct.POINTER(ct.c_int64))
+    assert lib.zc_compress(None, p, 2, None, 0, None, None, 0, None) == zc.ZC_EINVAL
+    assert lib.zc_decompress(None, 0, None, p, 2, None, None, None) == zc.ZC_EINVAL
+    assert lib.zc_compress(None, p, 0, None, 0, None, None, 0, None) == zc.ZC_OK
+    cnt = np.array([10], np.int64)
+    p = cnt.ctypes.data_as(ct.POINTER(ct.c_int64))
+    # misaligned output pointer
+    assert lib.zc_compress(ct.c_void_p(0x1000), p, 1, ct.c_void_p(0x2001), 1 << 20,
+                           ct.c_void_p(0x3000), ct.c_void_p(0x4000), 1 << 20,
+                           None) == zc.ZC_EINVAL
+    # capacity too small
+    assert lib.zc_compress(ct.c_void_p(0x1000), p, 1, ct.c_void_p(0x2000), 10,
+                           ct.c_void_p(0x3000), ct.c_void_p(0x4000), 1 << 20,
+                           None) == zc.ZC_ENOSPC
+    # workspace too small
+    assert lib.zc_compress(ct.c_void_p(0x1000), p, 1, ct.c_void_p(0x2000), 1 << 20,
+                           ct.c_void_p(0x3000), ct.c_void_p(0x4000), 8,
+                           None) == zc.ZC_ENOSPC
+    # decompress: offset not a multiple of 16, header beyond in_bytes
+    off = np.array([8], np.int64)
+    op = off.ctypes.data_as(ct.POINTER(ct.c_int64))
+    assert lib.zc_decompress(ct.c_void_p(0x1000), 4096, op, p, 1, ct.c_void_p(0x2000),
+                             ct.c_void_p(0x3000), None) == zc.ZC_EINVAL
+    assert lib.zc_decompress(ct.c_void_p(0x1000), 16, None, p, 1, ct.c_void_p(0x2000),
+                             ct.c_void_p(0x3000), None) == zc.ZC_EINVAL
+    for code in (0, -1, -2, -3, -4):
+        assert zc.zc_strerror(code) != "unknown status"

@@ -1,0 +1,254 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+The bar is bit-exactness: the compressed stream byte for byte (up to each
+chunk's comp_bytes), the sizes, and the round trip, on the same seeded inputs.
+Cross-decoding (GPU decodes oracle streams, oracle decodes GPU streams) checks
+both directions of the format.  Full-size workloads compare a sample of
+chunks with the oracle and check the round trip of every chunk.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from lossless_bf16_tensor_sign_amd import synth, zc
+from tests import golden_io
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TILE = 8192
+
+
+def say(msg):
+    print("[gpu] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(w):
+    return torch.from_numpy(np.ascontiguousarray(w).view(np.int16)).to(DEV)
+
+
+def gpu_compress(w, counts):
+    counts = np.asarray(counts, np.int64)
+    buf, sizes = zc.compress(to_dev(w), counts)
+    torch.cuda.synchronize()
+    return buf.cpu().numpy(), sizes.cpu().numpy()
+
+
+def gpu_decompress(buf_np, counts, offsets=None):
+    d = torch.from_numpy(buf_np).to(DEV)
+    out, status = zc.decompress(d, counts, in_offsets=offsets, check=False)
+    torch.cuda.synchronize()
+    return int(status.item()), out.cpu().numpy().view(np.uint16)
+
+
+def check_against_oracle(oracle, w, counts, sample=None, label=""):
+    """GPU stream == oracle stream for sampled chunks; GPU round trip of all."""
+    counts = np.asarray(counts, np.int64)
+    say("compress %s: %d chunks, %d values" % (label, len(counts), counts.sum()))
+    gbuf, gsizes = gpu_compress(w, counts)
+    off, total = oracle.slot_offsets(counts)
+    assert gbuf.size >= total
+    vo = np.concatenate([[0], np.cumsum(counts)])
+    chunks = range(len(counts)) if sample is None else sample
+    for c in chunks:
+        ref = oracle.compress_chunk(w[vo[c]:vo[c + 1]])
+        assert gsizes[c] == ref.size, (label, c, gsizes[c], ref.size)
+        got = gbuf[off[c]:off[c] + ref.size]
+        bad = np.nonzero(got != ref)[0]
+        assert bad.size == 0, "%s chunk %d: first differing byte %d" % (label, c, bad[0])
+        # oracle decodes the GPU stream
+        r, back = oracle.decompress_chunk(got, int(counts[c]))
+        assert r == 0 and np.array_equal(back, w[vo[c]:vo[c + 1]])
+    for c in range(len(counts)):
+        assert 32 <= gsizes[c] <= oracle.chunk_bound(int(counts[c]))
+    say("decompress %s" % label)
+    st, back = gpu_decompress(gbuf, counts)
+    assert st == 0, "status %#x" % st
+    assert np.array_equal(back, w)
+    return gbuf, gsizes
+
+
+# ------------------------------------------------------------ golden ---
+
+@pytest.mark.parametrize("name", golden_io.names())
+def test_golden_streams_gpu(name):
+    w, want = golden_io.load(name)
+    say("golden " + name)
+    gbuf, gsizes = gpu_compress(w, [w.size])
+    assert gsizes[0] == want.size
+    assert np.array_equal(gbuf[:want.size], want)
+    slot = np.zeros(zc.zc_bound([w.size]), np.uint8)
+    slot[:want.size] = want
+    st, back = gpu_decompress(slot, [w.size])
+    assert st == 0 and np.array_equal(back, w)
+
+
+# ------------------------------------------------------------ edges ---
+
+@pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 511, 512, 513, 8191, 8192, 8193,
+                               20000, 3 * 8192 + 17, 5 * 8192])
+def test_edge_sizes_single_chunk(oracle, n):
+    w = synth.gaussian_bits(n, 0.03, seed=1000 + n)
+    check_against_oracle(oracle, w, [n], label="n=%d" % n)
+
+
+def test_ragged_multi_chunk_with_empties(oracle):
+    cnt = np.array([0, 1, 7, 8192, 0, 8193, 13, 20000, 0, 3], np.int64)
+    w = synth.gaussian_bits(int(cnt.sum()), 0.01, seed=7)
+    w[::501] = 0x7FC0
+    check_against_oracle(oracle, w, cnt, label="ragged")
+
+
+def test_more_chunks_than_one_launch(oracle):
+    rng = np.random.default_rng(8)
+    cnt = rng.integers(0, 30000, size=200).astype(np.int64)
+    cnt[rng.random(200) < 0.15] = 0
+    w = synth.gaussian_bits(int(cnt.sum()), 0.02, seed=9)
+    check_against_oracle(oracle, w, cnt, label="200 chunks")
+
+
+@pytest.mark.parametrize("v", [0x7FC0, 0x8000, 0x0000, 0x7F7F, 0xFF80, 0x0001])
+def test_constant_special_values(oracle, v):
+    cnt = [1, 128, 8192, 8193 + 64]
+    w = np.full(sum(cnt), v, np.uint16)
+    check_against_oracle(oracle, w, cnt, label="const %#06x" % v)
+
+
+def test_all_patterns_three_layouts(oracle):
+    w = np.arange(65536, dtype=np.uint16)
+    check_against_oracle(oracle, w, [65536], label="patterns in order")
+    for seed in range(3):
+        w = np.random.default_rng(seed).permutation(65536).astype(np.uint16)
+        check_against_oracle(oracle, w, [65536], label="shuffle %d" % seed)
+    w = synth.gaussian_bits(65536 * 128, 0.02, seed=99)
+    q = np.arange(65536)
+    t, lane = np.divmod(q, 64)
+    k, j = np.divmod(q % 128, 8)
+    w[t * TILE + k * 512 + lane * 8 + j] = q.astype(np.uint16)
+    check_against_oracle(oracle, w, [w.size], label="patterns in gaussian groups")
+
+
+def test_cross_decode_oracle_streams(oracle):
+    cnt = np.array([5, 0, 8192, 9000, 1, 70000], np.int64)
+    w = synth.gaussian_bits(int(cnt.sum()), 0.005, seed=21)
+    w[::333] = 0
+    buf, sizes, _ = oracle.compress(w, cnt)
+    say("gpu decodes oracle slot buffer")
+    st, back = gpu_decompress(buf, cnt)
+    assert st == 0 and np.array_equal(back, w)
+    # packed at 16-byte boundaries, explicit offsets
+    off, _ = oracle.slot_offsets(cnt)
+    offs = np.concatenate([[0], np.cumsum((sizes + 15) // 16 * 16)])[:-1]
+    packed = np.zeros(int(offs[-1] + sizes[-1]) + 64, np.uint8)
+    for c in range(len(cnt)):
+        packed[offs[c]:offs[c] + sizes[c]] = buf[off[c]:off[c] + sizes[c]]
+    st, back = gpu_decompress(packed, cnt, offsets=offs)
+    assert st == 0 and np.array_equal(back, w)
+
+
+def test_unaligned_chunk_starts(oracle):
+    # chunk starts at odd value offsets: the scalar load/store path
+    cnt = np.array([3, 8195, 1, 16390, 5], np.int64)
+    w = synth.gaussian_bits(int(cnt.sum()), 0.02, seed=5)
+    check_against_oracle(oracle, w, cnt, label="unaligned")
+
+
+def test_deterministic_repeat(oracle):
+    # Repeated calls give the same streams (slot bytes after a stream's end
+    # are never written, so only [slot_off, slot_off + comp_bytes) counts).
+    cnt = np.full(16, 1 << 18, np.int64)
+    w = synth.gaussian_bits(int(cnt.sum()), 0.02, seed=3)
+    x = to_dev(w)
+    off, _ = oracle.slot_offsets(cnt)
+    say("determinism x5")
+    first = None
+    for _ in range(5):
+        buf, sizes = zc.compress(x, cnt)
+        b, sz = buf.cpu().numpy(), sizes.cpu().numpy()
+        streams = [b[off[c]:off[c] + sz[c]].copy() for c in range(len(cnt))]
+        if first is None:
+            first = streams
+        else:
+            for c in range(len(cnt)):
+                assert np.array_equal(streams[c], first[c]), c
+
+
+# ------------------------------------------------------- workloads ---
+
+WORKLOAD_SAMPLES = {1: [0], 2: [0, 17, 63], 3: [0, 31, 62], 4: None, 5: [0, 40]}
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_workload_full_size(oracle, cfg):
+    w, cnt = synth.make(cfg, workers=8)
+    sample = WORKLOAD_SAMPLES[cfg]
+    if sample is None:   # variable chunks: smallest, largest and a middle one
+        order = np.argsort(cnt)
+        sample = sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])})
+    gbuf, gsizes = check_against_oracle(oracle, w, cnt, sample=sample,
+                                        label="workload %d" % cfg)
+    ratio = 2.0 * w.size / float(gsizes.sum())
+    say("workload %d ratio %.4f" % (cfg, ratio))
+    if cfg == 5:
+        assert 0.98 < ratio < 1.0
+    else:
+        assert ratio > 1.3
+
+
+# ---------------------------------------------------------- errors ---
+
+def test_capacity_and_argument_errors():
+    cnt = np.array([10000], np.int64)
+    x = to_dev(synth.gaussian_bits(10000, 0.02, seed=1))
+    out = torch.empty(zc.zc_bound(cnt) - 1, dtype=torch.uint8, device=DEV)
+    sizes = torch.empty(1, dtype=torch.int64, device=DEV)
+    ws = torch.empty(zc.zc_workspace_bytes(cnt), dtype=torch.uint8, device=DEV)
+    assert zc.zc_compress(x, cnt, out, sizes, ws) == zc.ZC_ENOSPC
+    out = torch.empty(zc.zc_bound(cnt), dtype=torch.uint8, device=DEV)
+    assert zc.zc_compress(x, cnt, out, sizes, ws[:16]) == zc.ZC_ENOSPC
+    assert zc.zc_compress(x, [-5], out, sizes, ws) == zc.ZC_EINVAL
+
+
+def _mutations(stream, rng, count):
+    for i in range(count):
+        m = stream.copy()
+        pos = int(rng.integers(0, m.size))
+        if i % 2:
+            m[pos] ^= np.uint8(1 << int(rng.integers(0, 8)))
+        else:
+            m[pos] = np.uint8(rng.integers(0, 256))
+        yield m
+
+
+def test_corrupt_streams_match_oracle_verdict(oracle):
+    # Both strict decoders must accept exactly the same mutated streams, and
+    # agree on the decoded values when they accept.
+    rng = np.random.default_rng(77)
+    n = 2 * TILE + 300
+    w = synth.gaussian_bits(n, 0.02, seed=12)
+    w[rng.integers(0, n, 30)] = rng.integers(0, 65536, 30).astype(np.uint16)
+    ref = oracle.compress_chunk(w)
+    cap = zc.zc_bound([n])
+    muts = list(_mutations(ref, rng, 300))
+    # truncations: in_bytes smaller than comp_bytes
+    say("corrupt streams: %d mutations" % len(muts))
+    agree = 0
+    for m in muts:
+        r_o, back_o = oracle.decompress_chunk(m, n)
+        slot = np.zeros(cap, np.uint8)
+        slot[:m.size] = m
+        st, back_g = gpu_decompress(slot, [n])
+        assert (r_o == 0) == (st == 0), (r_o, hex(st))
+        if st == 0:
+            assert np.array_equal(back_g, back_o)
+        agree += 1
+    assert agree == len(muts)
+    for cut in (40, ref.size // 2, ref.size - 4):
+        d = torch.from_numpy(ref[:cut].copy()).to(DEV)
+        out = torch.empty(n, dtype=torch.int16, device=DEV)
+        status = torch.zeros(1, dtype=torch.int32, device=DEV)
+        assert zc.zc_decompress(d, [n], out, status) == zc.ZC_OK
+        torch.cuda.synchronize()
+        assert int(status.item()) >> 24 == 2     # SIZE
