@@ -6,20 +6,26 @@
 // statistics); the sign+mantissa byte is stored raw, which is how a 16-bit
 // value reaches about 11 bits (pith.science, Figure 6 caption).
 //
-// GPU mapping (MI355X, wave64):
+// GPU mapping (MI355X, wave64; 4 independent waves per workgroup share the
+// code tables in LDS):
 //  * one wave owns one tile of 8192 values; lane l owns group 64t + l, whose
-//    values are 8 consecutive bf16 (one 16-byte load) at each of 16 steps,
-//    so every global load and store of the raw data is fully coalesced;
-//  * the group maximum is lane-local (no cross-lane reduction);
-//  * a wave prefix sum over the 64 group lengths places the lane streams,
-//    which are packed into an LDS copy of the tile stream (the pages stage
-//    data in shared memory, Figure 7 caption) and stored coalesced;
+//    values are 8 consecutive bf16 (one 16-byte load) at each of 16 steps, so
+//    every global load and store of the raw data is fully coalesced and the
+//    group maximum is lane-local;
+//  * a wave prefix sum over the 64 group lengths places the lane streams in
+//    an LDS copy of the tile stream (the pages stage data in shared memory,
+//    Figure 7 caption), which is stored coalesced;
 //  * the byte offset of a tile inside its chunk's exponent section is an
 //    exclusive scan over the tiles of the chunk, done in the same pass with a
 //    decoupled look-back over per-tile status words; tiles are taken from a
 //    ticket counter, so every tile a wave waits on is already running;
 //  * all chunks of a call form one flat list of tiles, so uneven chunk sizes
-//    (the imbalance of Figure 8) still fill the GPU.
+//    (the imbalance of Figure 8) still fill the GPU;
+//  * the inner loops are branch-free: the encoder appends one code word per
+//    value to a 64-bit accumulator and ORs each finished word into LDS; the
+//    decoder refills a 64-bit window from LDS every four symbols and takes
+//    one table lookup per symbol (code words longer than the lookup width,
+//    and escapes, take a rare second lookup).
 // No floating point runs on the device.
 #include <hip/hip_runtime.h>
 
@@ -35,25 +41,33 @@
 namespace {
 
 constexpr int kLanes = 64;
+constexpr int kWaves = 4;                          // waves per workgroup
+constexpr int kBlock = kLanes * kWaves;
 constexpr int kSteps = 16;
 constexpr int kTile = 8192;
-constexpr int kGroupVals = 128;
 constexpr int kTileWords = kTile * 8 / 32;        // raw tile stream: 2048 words
+constexpr int kStreamWords = kTileWords + 8;      // + guard words
 constexpr int kMaxChunks = 64;                     // chunks per launch
 constexpr uint32_t kMagic = 0x3142435Au;
 constexpr uint32_t kVerTable = 0x00010001u;        // version 1, table_id 1
 constexpr int kEsc = ZC_T1_NSYM - 1;
+constexpr int kEscLen = ZC_T1_ESC_LEN;
 constexpr int kLutBits = 10;
+constexpr int kTailBits = 4;
+constexpr int kLutTail = 1 << kLutBits;            // LDS index of the second level
+constexpr int kLutRaw = kLutTail + (1 << kTailBits);   // raw-mode byte entries
+constexpr int kLutSize = kLutRaw + 256;
 constexpr uint64_t kFlagAgg = 1ull << 62;
 constexpr uint64_t kFlagInc = 2ull << 62;
 
 static_assert(ZC_T1_NSYM == 17, "table_id 1 has 17 symbols");
-static_assert(ZC_T1_MAXLEN + 8 <= 32, "escape payload must fit the window");
+static_assert(ZC_T1_TAIL_OK == 1, "long code words must share the all-ones prefix");
+static_assert(ZC_T1_MAXLEN <= kLutBits + kTailBits, "code words must fit two lookup levels");
+static_assert(kEscLen + 8 <= 32, "escape payload must fit the window");
+static_assert(kEscLen + 8 > ZC_T1_MAXLEN, "an escape entry is told apart by its length");
 
 __constant__ uint16_t c_lut[1 << kLutBits] = ZC_T1_LUT_INIT;
-__constant__ uint32_t c_limit[25] = ZC_T1_LIMIT_INIT;
-__constant__ uint32_t c_base[25] = ZC_T1_BASE_INIT;
-__constant__ uint8_t c_sorted[ZC_T1_NSYM] = ZC_T1_SORTED_INIT;
+__constant__ uint16_t c_tail[1 << kTailBits] = ZC_T1_TAIL_INIT;
 __constant__ uint8_t c_len[ZC_T1_NSYM] = ZC_T1_LEN_INIT;
 __constant__ uint32_t c_code[ZC_T1_NSYM] = ZC_T1_CODE_INIT;
 
@@ -92,6 +106,14 @@ __host__ __device__ inline uint64_t chunk_bound(uint64_t n)
 }
 
 // ------------------------------------------------------------ wave utils
+
+// Keeps this wave's LDS accesses in program order (the LDS unit performs one
+// wave's operations in order, so no wait is needed).
+__device__ inline void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
 
 __device__ inline uint32_t wave_excl_scan(uint32_t x, uint32_t lane, uint32_t* total)
 {
@@ -152,6 +174,9 @@ __device__ inline int find_chunk(const ChunkTable& tab, uint32_t item)
     return lo;
 }
 
+__device__ inline uint32_t hi32(uint64_t x) { return static_cast<uint32_t>(x >> 32); }
+__device__ inline uint32_t lo32(uint64_t x) { return static_cast<uint32_t>(x); }
+
 // ------------------------------------------------------------ compress
 
 __global__ void zc_clear_kernel(uint64_t* __restrict__ p, uint32_t words)
@@ -161,227 +186,349 @@ __global__ void zc_clear_kernel(uint64_t* __restrict__ p, uint32_t words)
         p[i] = 0;
 }
 
-__global__ __launch_bounds__(kLanes)
-void zc_compress_kernel(const uint16_t* __restrict__ in, uint8_t* __restrict__ out,
-                        int64_t* __restrict__ comp_sizes,
-                        uint64_t* __restrict__ status, uint32_t* __restrict__ ticket,
-                        ChunkTable tab)
+// Encoder table entry for d = 0..255: code bits 0..21 (an escape carries
+// its code followed by 8 zero bits for the exponent), length in bits 24..28,
+// bit 31 set for escapes.
+__device__ inline uint32_t enc_entry(uint32_t d)
 {
-    __shared__ uint32_t s_bits[kTileWords + 1];
-    __shared__ uint32_t s_enc[256];   // d -> code | len << 24 (d >= 16: ESC)
-
-    const uint32_t lane = threadIdx.x;
-    for (uint32_t d = lane; d < 256; d += kLanes) {
-        const int s = d < kEsc ? static_cast<int>(d) : kEsc;
-        uint32_t code = c_code[s], len = c_len[s];
-        if (s == kEsc) {
-            code <<= 8;               // payload: the exponent, 8 bits
-            len += 8;
-        }
-        s_enc[d] = code | (len << 24);
+    const uint32_t s = d < static_cast<uint32_t>(kEsc) ? d : static_cast<uint32_t>(kEsc);
+    uint32_t code = c_code[s], len = c_len[s];
+    if (s == static_cast<uint32_t>(kEsc)) {
+        code <<= 8;
+        len += 8;
     }
+    return code | (len << 24) | (s == static_cast<uint32_t>(kEsc) ? 0x80000000u : 0u);
+}
 
-    uint32_t item = 0;
-    if (lane == 0)
-        item = atomicAdd(ticket, 1u);
-    item = __builtin_amdgcn_readfirstlane(item);
+struct TileCtx {
+    const uint16_t* src;
+    uint8_t* dst;
+    Geom G;
+    uint32_t n, t, base, rem, item, first, lane;
+    int c;
+};
 
-    const int c = find_chunk(tab, item);
-    const uint32_t n = tab.n[c];
-    const uint32_t t = item - tab.item_begin[c];
-    const uint16_t* src = in + tab.voff[c];
-    uint8_t* dst = out + tab.boff[c];
-    const Geom G = geometry(n);
-
-    if (n == 0) {
-        if (lane < 8)
-            reinterpret_cast<uint32_t*>(dst)[lane] = header_word(lane, 0, 32);
-        if (lane == 0)
-            comp_sizes[c] = 32;
-        return;
-    }
-
-    const uint32_t base = t * kTile;
-    const uint32_t rem = min(n - base, static_cast<uint32_t>(kTile));
-    const bool vec = rem == kTile && ((reinterpret_cast<uintptr_t>(src) & 15) == 0);
-    const uint32_t ng = group_members(rem, lane);
-
-    // 1. load, split, raw bytes out, exponents kept packed 4 per word
-    uint32_t ex[kSteps][2];
+// Phase 1 of a tile: loads, raw bytes out, exponents packed 4 per word,
+// group maximum.  FULL = 8192 values at a 16-byte aligned address.
+template <bool FULL>
+__device__ inline uint32_t load_split(const TileCtx& x, uint32_t (&ex)[kSteps][2])
+{
+    // wave-uniform bases, 32-bit lane offsets
+    const char* sbase = reinterpret_cast<const char*>(x.src + x.base);
+    char* rbase = reinterpret_cast<char*>(x.dst + x.G.R + x.base);
+    const uint32_t lo16 = x.lane * 16, lo8 = x.lane * 8;
+    constexpr int kBatch = FULL ? 8 : 2;
     uint32_t mx = 0;
 #pragma unroll
-    for (int k = 0; k < kSteps; ++k) {
-        const uint32_t i0 = base + k * 512 + lane * 8;
-        uint4 v;
-        if (vec) {
-            v = *reinterpret_cast<const uint4*>(src + i0);
-        } else {
-            uint32_t w[8];
+    for (int h = 0; h < kSteps / kBatch; ++h) {
+        uint4 v[kBatch];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                w[j] = (i0 + j < n) ? src[i0 + j] : 0u;
-            v.x = w[0] | (w[1] << 16);
-            v.y = w[2] | (w[3] << 16);
-            v.z = w[4] | (w[5] << 16);
-            v.w = w[6] | (w[7] << 16);
+        for (int kk = 0; kk < kBatch; ++kk) {
+            const int k = h * kBatch + kk;
+            if (FULL) {
+                v[kk] = *reinterpret_cast<const uint4*>(sbase + lo16 + k * 1024);
+            } else {
+                const uint32_t i0 = x.base + k * 512 + x.lane * 8;
+                uint32_t w[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    w[j] = (i0 + j < x.n) ? x.src[i0 + j] : 0u;
+                v[kk].x = w[0] | (w[1] << 16);
+                v[kk].y = w[2] | (w[3] << 16);
+                v[kk].z = w[4] | (w[5] << 16);
+                v[kk].w = w[6] | (w[7] << 16);
+            }
         }
-        const uint32_t lo_a = __builtin_amdgcn_perm(v.y, v.x, 0x06040200u);
-        const uint32_t hi_a = __builtin_amdgcn_perm(v.y, v.x, 0x07050301u);
-        const uint32_t lo_b = __builtin_amdgcn_perm(v.w, v.z, 0x06040200u);
-        const uint32_t hi_b = __builtin_amdgcn_perm(v.w, v.z, 0x07050301u);
-        const uint32_t raw_a = (hi_a & 0x80808080u) | (lo_a & 0x7F7F7F7Fu);
-        const uint32_t raw_b = (hi_b & 0x80808080u) | (lo_b & 0x7F7F7F7Fu);
-        ex[k][0] = ((hi_a << 1) & 0xFEFEFEFEu) | ((lo_a >> 7) & 0x01010101u);
-        ex[k][1] = ((hi_b << 1) & 0xFEFEFEFEu) | ((lo_b >> 7) & 0x01010101u);
-        mx = max(mx, max(max(v.x & 0x7F80u, (v.x >> 16) & 0x7F80u),
-                         max(v.y & 0x7F80u, (v.y >> 16) & 0x7F80u)));
-        mx = max(mx, max(max(v.z & 0x7F80u, (v.z >> 16) & 0x7F80u),
-                         max(v.w & 0x7F80u, (v.w >> 16) & 0x7F80u)));
-        uint8_t* rdst = dst + G.R + i0;
-        if (vec) {
-            *reinterpret_cast<uint2*>(rdst) = make_uint2(raw_a, raw_b);
-        } else {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (i0 + j < n)
-                    rdst[j] = static_cast<uint8_t>(((j < 4 ? raw_a : raw_b) >> (8 * (j & 3))) & 0xFF);
+        for (int kk = 0; kk < kBatch; ++kk) {
+            const int k = h * kBatch + kk;
+            const uint4 q = v[kk];
+            const uint32_t lo_a = __builtin_amdgcn_perm(q.y, q.x, 0x06040200u);
+            const uint32_t hi_a = __builtin_amdgcn_perm(q.y, q.x, 0x07050301u);
+            const uint32_t lo_b = __builtin_amdgcn_perm(q.w, q.z, 0x06040200u);
+            const uint32_t hi_b = __builtin_amdgcn_perm(q.w, q.z, 0x07050301u);
+            const uint32_t raw_a = (hi_a & 0x80808080u) | (lo_a & 0x7F7F7F7Fu);
+            const uint32_t raw_b = (hi_b & 0x80808080u) | (lo_b & 0x7F7F7F7Fu);
+            ex[k][0] = ((hi_a << 1) & 0xFEFEFEFEu) | ((lo_a >> 7) & 0x01010101u);
+            ex[k][1] = ((hi_b << 1) & 0xFEFEFEFEu) | ((lo_b >> 7) & 0x01010101u);
+            mx = max(mx, max(max(q.x & 0x7F80u, (q.x >> 16) & 0x7F80u),
+                             max(q.y & 0x7F80u, (q.y >> 16) & 0x7F80u)));
+            mx = max(mx, max(max(q.z & 0x7F80u, (q.z >> 16) & 0x7F80u),
+                             max(q.w & 0x7F80u, (q.w >> 16) & 0x7F80u)));
+            if (FULL) {
+                *reinterpret_cast<uint2*>(rbase + lo8 + k * 512) = make_uint2(raw_a, raw_b);
+            } else {
+                const uint32_t i0 = x.base + k * 512 + x.lane * 8;
+                uint8_t* rdst = x.dst + x.G.R + i0;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (i0 + j < x.n)
+                        rdst[j] = static_cast<uint8_t>(((j < 4 ? raw_a : raw_b) >> (8 * (j & 3))) & 0xFF);
+            }
         }
     }
-    const uint32_t emax = mx >> 7;   // missing members were loaded as 0
+    return mx >> 7;   // missing members were loaded as 0
+}
 
-    __syncthreads();                 // s_enc ready
+// Decoupled look-back: exclusive byte offset of tile `item` in its chunk.
+__device__ inline uint32_t look_back(uint64_t* __restrict__ status, uint32_t item, uint32_t t,
+                                     uint32_t first, uint32_t tile_bytes, uint32_t lane)
+{
+    if (t == 0) {
+        if (lane == 0)
+            __hip_atomic_store(&status[item], kFlagInc | tile_bytes, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        return 0;
+    }
+    if (lane == 0)
+        __hip_atomic_store(&status[item], kFlagAgg | tile_bytes, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    int64_t top = static_cast<int64_t>(item) - 1;
+    uint32_t acc = 0;
+    while (true) {
+        const int64_t idx = top - static_cast<int64_t>(lane);
+        const bool in_range = idx >= static_cast<int64_t>(first);
+        uint64_t s = 0;
+        if (in_range)
+            s = __hip_atomic_load(&status[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t flag = static_cast<uint32_t>(s >> 62);
+        const uint64_t inc_mask = __ballot(in_range && flag == 2);
+        const uint64_t zero_mask = __ballot(in_range && flag == 0);
+        if (inc_mask) {
+            const int p = __ffsll(static_cast<unsigned long long>(inc_mask)) - 1;
+            const uint64_t below = (p == 0) ? 0ull : ((1ull << p) - 1);
+            if (zero_mask & below) {
+                __builtin_amdgcn_s_sleep(1);
+                continue;
+            }
+            acc += wave_sum(lane <= static_cast<uint32_t>(p) ? static_cast<uint32_t>(s) : 0u);
+            break;
+        }
+        if (zero_mask) {
+            __builtin_amdgcn_s_sleep(1);
+            continue;
+        }
+        acc += wave_sum(static_cast<uint32_t>(s));
+        top -= kLanes;
+    }
+    if (lane == 0)
+        __hip_atomic_store(&status[item], kFlagInc | (acc + tile_bytes), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    return acc;
+}
 
-    // 2. coded length of the group, raw decision
+// Raw groups of a full tile whose 64 groups are all raw: the exponents
+// themselves, 8 bits each, first value most significant.  Every lane holds
+// 1024 bits, so lane offsets are word aligned.
+__device__ inline void emit_all_raw(uint32_t* __restrict__ s_stream,
+                                    const uint32_t (&dd)[kSteps][2], uint32_t emax, uint32_t off)
+{
+    const uint32_t em4 = emax * 0x01010101u;
+    uint32_t* w = s_stream + (off >> 5);
+#pragma unroll
+    for (int k = 0; k < kSteps; ++k) {
+        const uint32_t e0 = em4 - dd[k][0], e1 = em4 - dd[k][1];
+        w[2 * k] = __builtin_amdgcn_perm(e0, e0, 0x00010203u);
+        w[2 * k + 1] = __builtin_amdgcn_perm(e1, e1, 0x00010203u);
+    }
+}
+
+// Appends the group's code words (or, for a raw group, its exponents as
+// 8-bit code words) to the LDS tile stream from bit offset `off`.
+template <bool FULL, bool MIXED>
+__device__ inline void emit_group(uint32_t* __restrict__ s_stream, const uint32_t* __restrict__ s_enc,
+                                  const uint32_t (&dd)[kSteps][2], uint32_t emax, uint32_t ng,
+                                  bool raw_mode, uint32_t off)
+{
+    uint64_t acc = 0;
+    uint32_t nacc = off & 31;
+    uint32_t wi = off >> 5;
+#pragma unroll 1
+    for (int k = 0; k < kSteps; ++k) {
+        const uint32_t d4[2] = {dd[k][0], dd[k][1]};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t d = (d4[j >> 2] >> (8 * (j & 3))) & 0xFF;
+            uint32_t ent = s_enc[d];
+            if (MIXED && raw_mode)
+                ent = ((emax - d) & 0xFF) | (8u << 24);
+            if (!FULL && static_cast<uint32_t>(k * 8 + j) >= ng)
+                ent = 0;
+            const uint32_t L = (ent >> 24) & 31;
+            const uint32_t esc = static_cast<uint32_t>(static_cast<int32_t>(ent) >> 31);
+            acc <<= L;
+            acc |= (ent & 0x3FFFFFu) | ((emax - d) & esc & 0xFFu);
+            nacc += L;
+            // the word that just filled up, if any (alignbit uses nacc mod 32)
+            const uint32_t w = __builtin_amdgcn_alignbit(hi32(acc), lo32(acc), nacc);
+            const uint32_t f = nacc >> 5;
+            atomicOr(&s_stream[wi], f ? w : 0u);
+            wi += f;
+            nacc &= 31;
+        }
+    }
+    if (nacc)
+        atomicOr(&s_stream[wi], lo32(acc) << (32 - nacc));
+}
+
+template <bool FULL>
+__device__ void compress_tile(const TileCtx& x, int64_t* __restrict__ comp_sizes,
+                              uint64_t* __restrict__ status, uint32_t* __restrict__ s_stream,
+                              const uint32_t* __restrict__ s_enc, const uint8_t* __restrict__ s_len)
+{
+    const uint32_t lane = x.lane;
+    const uint32_t ng = FULL ? 128u : group_members(x.rem, lane);
+
+    uint32_t dd[kSteps][2];
+    const uint32_t emax = load_split<FULL>(x, dd);
+
+    // 2. distances d = E_max - e (bytes never borrow: e <= E_max) and the
+    //    coded length of the group
+    const uint32_t em4 = emax * 0x01010101u;
+#pragma unroll
+    for (int k = 0; k < kSteps; ++k) {
+        dd[k][0] = em4 - dd[k][0];
+        dd[k][1] = em4 - dd[k][1];
+    }
     uint32_t bits = 0;
 #pragma unroll 1
     for (int k = 0; k < kSteps; ++k) {
-        const uint32_t e4[2] = {ex[k][0], ex[k][1]};
+        const uint32_t d4[2] = {dd[k][0], dd[k][1]};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const uint32_t e = (e4[j >> 2] >> (8 * (j & 3))) & 0xFF;
-            const uint32_t L = s_enc[emax - e] >> 24;
-            bits += (static_cast<uint32_t>(k * 8 + j) < ng) ? L : 0u;
+            const uint32_t d = (d4[j >> 2] >> (8 * (j & 3))) & 0xFF;
+            const uint32_t L = s_len[d];
+            bits += (FULL || static_cast<uint32_t>(k * 8 + j) < ng) ? L : 0u;
         }
     }
     const bool raw_mode = ng > 0 && bits >= 8 * ng;
     const uint32_t glen = raw_mode ? 8 * ng : bits;
 
-    // 3. lane offsets inside the tile stream, tile size
+    // 3. lane offsets, tile size, offset of the tile in the chunk
     uint32_t tile_bits;
     const uint32_t off = wave_excl_scan(glen, lane, &tile_bits);
     const uint32_t tile_words = (tile_bits + 31) >> 5;
     const uint32_t tile_bytes = tile_words * 4;
+    const uint32_t toff = look_back(status, x.item, x.t, x.first, tile_bytes, lane);
 
-    // 4. decoupled look-back over the tiles of this chunk
-    uint32_t toff = 0;
-    const uint32_t first = tab.item_begin[c];
-    if (t == 0) {
-        if (lane == 0)
-            __hip_atomic_store(&status[item], kFlagInc | tile_bytes, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-        if (lane == 0)
-            __hip_atomic_store(&status[item], kFlagAgg | tile_bytes, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        int64_t top = static_cast<int64_t>(item) - 1;
-        uint32_t acc = 0;
-        while (true) {
-            const int64_t idx = top - static_cast<int64_t>(lane);
-            const bool in_range = idx >= static_cast<int64_t>(first);
-            uint64_t s = 0;
-            if (in_range)
-                s = __hip_atomic_load(&status[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const uint32_t flag = static_cast<uint32_t>(s >> 62);
-            const uint64_t inc_mask = __ballot(in_range && flag == 2);
-            const uint64_t zero_mask = __ballot(in_range && flag == 0);
-            if (inc_mask) {
-                const int p = __ffsll(static_cast<unsigned long long>(inc_mask)) - 1;
-                const uint64_t below = (p == 0) ? 0ull : ((1ull << p) - 1);
-                if (zero_mask & below) {
-                    __builtin_amdgcn_s_sleep(1);
-                    continue;
-                }
-                acc += wave_sum(lane <= static_cast<uint32_t>(p) ? static_cast<uint32_t>(s) : 0u);
-                break;
-            }
-            if (zero_mask) {
-                __builtin_amdgcn_s_sleep(1);
-                continue;
-            }
-            acc += wave_sum(static_cast<uint32_t>(s));
-            top -= kLanes;
-        }
-        toff = acc;
-        if (lane == 0)
-            __hip_atomic_store(&status[item], kFlagInc | (toff + tile_bytes), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    }
-
-    // 5. index arrays
+    // 4. index arrays
     if (lane == 0)
-        *reinterpret_cast<uint32_t*>(dst + 32 + 4ull * t) = toff;
-    dst[32 + 4ull * G.T + 64ull * t + lane] = static_cast<uint8_t>(emax);
-    *reinterpret_cast<uint16_t*>(dst + 32 + 68ull * G.T + 2ull * (64ull * t + lane)) =
+        *reinterpret_cast<uint32_t*>(x.dst + 32 + 4ull * x.t) = toff;
+    x.dst[32 + 4ull * x.G.T + 64ull * x.t + lane] = static_cast<uint8_t>(emax);
+    *reinterpret_cast<uint16_t*>(x.dst + 32 + 68ull * x.G.T + 2ull * (64ull * x.t + lane)) =
         static_cast<uint16_t>(glen);
 
-    // 6. pack the lane streams into the LDS tile stream, MSB first
-    for (uint32_t w = lane; w < tile_words; w += kLanes)
-        s_bits[w] = 0;
-    __syncthreads();
-    {
-        uint64_t acc = 0;
-        uint32_t nacc = off & 31;
-        uint32_t wi = off >> 5;
-#pragma unroll 1
-        for (int k = 0; k < kSteps; ++k) {
-            const uint32_t e4[2] = {ex[k][0], ex[k][1]};
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (static_cast<uint32_t>(k * 8 + j) < ng) {
-                    const uint32_t e = (e4[j >> 2] >> (8 * (j & 3))) & 0xFF;
-                    uint32_t code, L;
-                    if (raw_mode) {
-                        code = e;
-                        L = 8;
-                    } else {
-                        const uint32_t d = emax - e;
-                        const uint32_t ent = s_enc[d];
-                        L = ent >> 24;
-                        code = (ent & 0xFFFFFFu) | (d >= static_cast<uint32_t>(kEsc) ? e : 0u);
-                    }
-                    acc = (acc << L) | code;
-                    nacc += L;
-                    if (nacc >= 32) {
-                        nacc -= 32;
-                        atomicOr(&s_bits[wi], static_cast<uint32_t>(acc >> nacc));
-                        ++wi;
-                    }
-                }
-            }
-        }
-        if (nacc)
-            atomicOr(&s_bits[wi], static_cast<uint32_t>(acc << (32 - nacc)));
+    // 5. pack the lane streams into the LDS tile stream, most significant bit first
+    const uint64_t raw_lanes = __ballot(raw_mode);
+    if (FULL && raw_lanes == ~0ull) {
+        emit_all_raw(s_stream, dd, emax, off);      // every word written once
+    } else {
+        for (uint32_t w = lane * 4; w <= tile_words; w += kLanes * 4)
+            *reinterpret_cast<uint4*>(&s_stream[w]) = make_uint4(0, 0, 0, 0);
+        wave_lds_sync();
+        if (raw_lanes == 0)
+            emit_group<FULL, false>(s_stream, s_enc, dd, emax, ng, raw_mode, off);
+        else
+            emit_group<FULL, true>(s_stream, s_enc, dd, emax, ng, raw_mode, off);
     }
-    __syncthreads();
+    wave_lds_sync();
 
-    // 7. coalesced store of the tile stream
-    uint32_t* sdst = reinterpret_cast<uint32_t*>(dst + G.X + toff);
+    // 6. coalesced store of the tile stream
+    uint32_t* sdst = reinterpret_cast<uint32_t*>(x.dst + x.G.X + toff);
     for (uint32_t w = lane; w < tile_words; w += kLanes)
-        sdst[w] = s_bits[w];
+        sdst[w] = s_stream[w];
 
-    // 8. the last tile finishes the chunk: header, gaps, size
-    if (t == G.T - 1) {
-        const uint64_t comp = G.X + toff + tile_bytes;
+    // 7. the last tile finishes the chunk: header, gaps, size
+    if (x.t == x.G.T - 1) {
+        const uint64_t comp = x.G.X + toff + tile_bytes;
         if (lane < 8)
-            reinterpret_cast<uint32_t*>(dst)[lane] = header_word(lane, n, comp);
-        const uint64_t g1 = 32 + 196ull * G.T;
-        if (g1 + lane < G.R)
-            dst[g1 + lane] = 0;
-        if (G.R + n + lane < G.X)
-            dst[G.R + n + lane] = 0;
+            reinterpret_cast<uint32_t*>(x.dst)[lane] = header_word(lane, x.n, comp);
+        const uint64_t g1 = 32 + 196ull * x.G.T;
+        if (g1 + lane < x.G.R)
+            x.dst[g1 + lane] = 0;
+        if (x.G.R + x.n + lane < x.G.X)
+            x.dst[x.G.R + x.n + lane] = 0;
         if (lane == 0)
-            comp_sizes[c] = static_cast<int64_t>(comp);
+            comp_sizes[x.c] = static_cast<int64_t>(comp);
     }
+}
+
+// Tiles that are partial (a chunk's last tile) or unaligned: kept out of
+// line so that their register needs do not constrain the full-tile path.
+__device__ __attribute__((noinline)) void compress_tile_partial(
+    const uint16_t* src, uint8_t* dst, uint32_t n, uint32_t t, uint32_t item, uint32_t first,
+    uint32_t lane, int c, int64_t* __restrict__ comp_sizes, uint64_t* __restrict__ status,
+    uint32_t* __restrict__ s_stream, const uint32_t* __restrict__ s_enc,
+    const uint8_t* __restrict__ s_len)
+{
+    TileCtx x;
+    x.src = src;
+    x.dst = dst;
+    x.n = n;
+    x.t = t;
+    x.item = item;
+    x.first = first;
+    x.lane = lane;
+    x.c = c;
+    x.G = geometry(n);
+    x.base = t * kTile;
+    x.rem = min(n - x.base, static_cast<uint32_t>(kTile));
+    compress_tile<false>(x, comp_sizes, status, s_stream, s_enc, s_len);
+}
+
+__global__ __launch_bounds__(kBlock, 4)
+void zc_compress_kernel(const uint16_t* __restrict__ in, uint8_t* __restrict__ out,
+                        int64_t* __restrict__ comp_sizes,
+                        uint64_t* __restrict__ status, uint32_t* __restrict__ ticket,
+                        ChunkTable tab)
+{
+    __shared__ __align__(16) uint32_t s_stream[kWaves][kStreamWords];
+    __shared__ uint32_t s_enc[256];
+    __shared__ uint8_t s_len[256];
+
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & (kLanes - 1);
+    const uint32_t wave = tid / kLanes;
+    {
+        const uint32_t e = enc_entry(tid);
+        s_enc[tid] = e;
+        s_len[tid] = static_cast<uint8_t>((e >> 24) & 31);
+    }
+    __syncthreads();
+
+    uint32_t item = 0;
+    if (lane == 0)
+        item = atomicAdd(ticket, 1u);
+    item = __builtin_amdgcn_readfirstlane(item);
+    if (item >= tab.nitems)
+        return;
+
+    TileCtx x;
+    x.c = find_chunk(tab, item);
+    x.n = tab.n[x.c];
+    x.t = item - tab.item_begin[x.c];
+    x.first = tab.item_begin[x.c];
+    x.item = item;
+    x.lane = lane;
+    x.src = in + tab.voff[x.c];
+    x.dst = out + tab.boff[x.c];
+    x.G = geometry(x.n);
+
+    if (x.n == 0) {
+        if (lane < 8)
+            reinterpret_cast<uint32_t*>(x.dst)[lane] = header_word(lane, 0, 32);
+        if (lane == 0)
+            comp_sizes[x.c] = 32;
+        return;
+    }
+    x.base = x.t * kTile;
+    x.rem = min(x.n - x.base, static_cast<uint32_t>(kTile));
+    const bool full = x.rem == kTile && ((reinterpret_cast<uintptr_t>(x.src) & 15) == 0);
+    if (full)
+        compress_tile<true>(x, comp_sizes, status, s_stream[wave], s_enc, s_len);
+    else
+        compress_tile_partial(x.src, x.dst, x.n, x.t, x.item, x.first, lane, x.c, comp_sizes,
+                              status, s_stream[wave], s_enc, s_len);
 }
 
 // ------------------------------------------------------------ decompress
@@ -391,21 +538,256 @@ __device__ inline void report(int32_t* status, int reason, int c)
     atomicCAS(status, 0, (reason << 24) | (c & 0xFFFFFF));
 }
 
-__global__ __launch_bounds__(kLanes)
+// 64 stream bits starting at bit `pos` of the LDS tile stream (word index
+// clamped to `cap`, past which the stream holds zero guard words).
+__device__ inline uint64_t window64(const uint32_t* __restrict__ s, uint32_t pos, uint32_t cap)
+{
+    const uint32_t wi = min(pos >> 5, cap);
+    const uint32_t w0 = s[wi], w1 = s[wi + 1], w2 = s[wi + 2];
+    const uint32_t sh = pos & 31;
+    const uint32_t hi = hi32(((static_cast<uint64_t>(w0) << 32) | w1) << sh);
+    const uint32_t lo = hi32(((static_cast<uint64_t>(w1) << 32) | w2) << sh);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Table entry of the symbol at the top of window W: length in bits 0..7,
+// symbol in bits 8.. (signed).  An escape is returned as (d << 8) | 22 with
+// d = E_max - e, so that E_max minus the symbol field is e in every case.
+// Raw groups look their 8 bits up in entries that hold 255 - e.
+__device__ inline uint32_t decode_entry(const uint16_t* __restrict__ s_lut, uint32_t top,
+                                        uint32_t lut_sh, uint32_t lut_base, uint32_t emax)
+{
+    uint32_t ent = s_lut[(top >> lut_sh) + lut_base];
+    if (ent == 0) {
+        // longer than the first lookup level: second level on the next bits
+        ent = s_lut[kLutTail + ((top >> (32 - kLutBits - kTailBits)) & ((1u << kTailBits) - 1))];
+        if ((ent >> 8) == static_cast<uint32_t>(kEsc)) {
+            const uint32_t e = (top >> (32 - kEscLen - 8)) & 0xFF;
+            ent = ((emax - e) << 8) | (kEscLen + 8);
+        }
+    }
+    return ent;
+}
+
+template <bool FULL>
+__device__ void decompress_tile(const uint8_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                int32_t* __restrict__ status, int c, uint32_t n, uint32_t t,
+                                const Geom& G, uint32_t lane, uint32_t* __restrict__ s_stream,
+                                const uint16_t* __restrict__ s_lut,
+                                const uint8_t* __restrict__ s_len, uint64_t comp)
+{
+    const uint32_t base = t * kTile;
+    const uint32_t rem = min(n - base, static_cast<uint32_t>(kTile));
+    const uint32_t ng = FULL ? 128u : group_members(rem, lane);
+
+    // tile extent
+    const uint32_t* toffs = reinterpret_cast<const uint32_t*>(src + 32);
+    const uint32_t toff = toffs[t];
+    const uint64_t next = (t + 1 < G.T) ? toffs[t + 1] : comp - G.X;
+    if ((t == 0 && toff != 0) || toff > next || next > comp - G.X) {
+        if (lane == 0)
+            report(status, ZC_REASON_TILE, c);
+        return;
+    }
+    const uint32_t tile_bytes = static_cast<uint32_t>(next - toff);
+
+    // raw bytes, prefetched three steps ahead
+    const uint2* rsrc2 = reinterpret_cast<const uint2*>(src + G.R + base) + lane;
+    uint2 r0 = make_uint2(0, 0), r1 = r0, r2 = r0;
+    if (FULL) {
+        r0 = rsrc2[0];
+        r1 = rsrc2[64];
+        r2 = rsrc2[128];
+    }
+
+    // group metadata
+    const uint32_t emax = src[32 + 4ull * G.T + 64ull * t + lane];
+    const uint32_t glen =
+        *reinterpret_cast<const uint16_t*>(src + 32 + 68ull * G.T + 2ull * (64ull * t + lane));
+    if (__ballot(glen > 8 * ng || (ng == 0 && emax != 0))) {
+        if (lane == 0)
+            report(status, ZC_REASON_GROUP, c);
+        return;
+    }
+    uint32_t tile_bits;
+    const uint32_t off = wave_excl_scan(glen, lane, &tile_bits);
+    const uint32_t tile_words = (tile_bits + 31) >> 5;
+    if (tile_bytes != 4 * tile_words) {
+        if (lane == 0)
+            report(status, ZC_REASON_TILE, c);
+        return;
+    }
+
+    // stage the tile stream in LDS, with zero guard words after it
+    const uint32_t* ssrc = reinterpret_cast<const uint32_t*>(src + G.X + toff);
+    for (uint32_t w = lane; w < tile_words; w += kLanes)
+        s_stream[w] = ssrc[w];
+    if (lane < 4)
+        s_stream[tile_words + lane] = 0;
+    wave_lds_sync();
+
+    int err = 0;
+    if ((tile_bits & 31) && lane == 0) {
+        const uint32_t last = s_stream[tile_words - 1];
+        if (last & ((1u << (32 - (tile_bits & 31))) - 1))
+            err = ZC_REASON_PADDING;
+    }
+    if (t == 0) {
+        const uint64_t g1 = 32 + 196ull * G.T;
+        if (g1 + lane < G.R && src[g1 + lane] != 0)
+            err = ZC_REASON_GAP;
+    }
+    if (t == G.T - 1) {
+        if (G.R + n + lane < G.X && src[G.R + n + lane] != 0)
+            err = ZC_REASON_GAP;
+    }
+
+    const bool raw_mode = ng > 0 && glen == 8 * ng;
+    const bool any_raw = __ballot(raw_mode) != 0;
+    const uint32_t emax_eff = raw_mode ? 255u : emax;
+    const uint32_t lut_sh = raw_mode ? 24u : static_cast<uint32_t>(32 - kLutBits);
+    const uint32_t lut_base = raw_mode ? static_cast<uint32_t>(kLutRaw) : 0u;
+    const bool vec_out = FULL && ((reinterpret_cast<uintptr_t>(dst) & 15) == 0);
+    const uint32_t cap = tile_words;
+    uint32_t pos = off;
+    uint32_t seen_max = 0, raw_coded = 0;
+    int32_t esc_min = 255;    // smallest E_max - e over escapes (must be >= 16)
+
+#pragma unroll 1
+    for (int k = 0; k < kSteps; ++k) {
+        uint32_t e8[8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t pos0 = pos;
+            uint64_t W = window64(s_stream, pos, cap);
+            uint32_t used = 0;
+            int32_t esc_h = 255;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t ent = decode_entry(s_lut, hi32(W), lut_sh, lut_base, emax);
+                if (!FULL && static_cast<uint32_t>(k * 8 + h * 4 + j) >= ng)
+                    ent = 0;
+                const int32_t sym = static_cast<int32_t>(ent) >> 8;
+                e8[h * 4 + j] = emax_eff - static_cast<uint32_t>(sym);
+                if ((ent & 0xFF) == static_cast<uint32_t>(kEscLen + 8))
+                    esc_h = min(esc_h, sym);
+                W <<= (ent & 63);
+                used += ent & 0xFF;
+            }
+            if (__ballot(used > 64)) {
+                // a half-step longer than the window (several escapes): decode
+                // those lanes again symbol by symbol
+                if (used > 64) {
+                    uint32_t p = pos0;
+                    esc_h = 255;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        uint32_t ent = decode_entry(s_lut, hi32(window64(s_stream, p, cap)),
+                                                    lut_sh, lut_base, emax);
+                        if (!FULL && static_cast<uint32_t>(k * 8 + h * 4 + j) >= ng)
+                            ent = 0;
+                        const int32_t sym = static_cast<int32_t>(ent) >> 8;
+                        e8[h * 4 + j] = emax_eff - static_cast<uint32_t>(sym);
+                        if ((ent & 0xFF) == static_cast<uint32_t>(kEscLen + 8))
+                            esc_h = min(esc_h, sym);
+                        p += ent & 0xFF;
+                    }
+                    used = p - pos0;
+                }
+            }
+            esc_min = min(esc_min, esc_h);
+            pos = pos0 + used;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (FULL || static_cast<uint32_t>(k * 8 + j) < ng)
+                seen_max = max(seen_max, e8[j]);
+        }
+        if (any_raw) {
+            // a raw group must not have been codable in fewer bits
+            if (raw_mode) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (FULL || static_cast<uint32_t>(k * 8 + j) < ng)
+                        raw_coded += s_len[(emax - e8[j]) & 0xFF];
+            }
+        }
+        const uint2 r = r0;
+        if (FULL) {
+            r0 = r1;
+            r1 = r2;
+            if (k + 3 < kSteps)
+                r2 = rsrc2[(k + 3) * 64];
+        }
+        const uint32_t i0 = base + k * 512 + lane * 8;
+        if (vec_out) {
+            uint4 o;
+            o.x = (__builtin_amdgcn_perm(r.x, r.x, 0x01010000u) & 0x807F807Fu) | (e8[0] << 7) | (e8[1] << 23);
+            o.y = (__builtin_amdgcn_perm(r.x, r.x, 0x03030202u) & 0x807F807Fu) | (e8[2] << 7) | (e8[3] << 23);
+            o.z = (__builtin_amdgcn_perm(r.y, r.y, 0x01010000u) & 0x807F807Fu) | (e8[4] << 7) | (e8[5] << 23);
+            o.w = (__builtin_amdgcn_perm(r.y, r.y, 0x03030202u) & 0x807F807Fu) | (e8[6] << 7) | (e8[7] << 23);
+            *reinterpret_cast<uint4*>(dst + i0) = o;
+        } else {
+            const uint8_t* rsrc = src + G.R;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (i0 + j < n) {
+                    const uint32_t r = rsrc[i0 + j];
+                    dst[i0 + j] = static_cast<uint16_t>(((r & 0x80u) << 8) | ((e8[j] & 0xFF) << 7) | (r & 0x7Fu));
+                }
+            }
+        }
+    }
+    if (err == 0 && ng > 0) {
+        if (pos != off + glen)
+            err = ZC_REASON_LENGTH;
+        else if (seen_max != emax)
+            err = ZC_REASON_EMAX;
+        else if (!raw_mode && esc_min < kEsc)
+            err = ZC_REASON_ESCAPE;
+        else if (raw_mode && raw_coded < 8 * ng)
+            err = ZC_REASON_RAWMODE;
+    }
+    if (err)
+        report(status, err, c);
+}
+
+// A chunk's last, partial tile, kept out of line (see compress_tile_partial).
+__device__ __attribute__((noinline)) void decompress_tile_partial(
+    const uint8_t* __restrict__ src, uint16_t* __restrict__ dst, int32_t* __restrict__ status,
+    int c, uint32_t n, uint32_t t, uint32_t lane, uint32_t* __restrict__ s_stream,
+    const uint16_t* __restrict__ s_lut, const uint8_t* __restrict__ s_len, uint64_t comp)
+{
+    const Geom G = geometry(n);
+    decompress_tile<false>(src, dst, status, c, n, t, G, lane, s_stream, s_lut, s_len, comp);
+}
+
+__global__ __launch_bounds__(kBlock, 4)
 void zc_decompress_kernel(const uint8_t* __restrict__ in, uint16_t* __restrict__ out,
                           int32_t* __restrict__ status, ChunkTable tab)
 {
-    __shared__ uint32_t s_bits[kTileWords + 2];
-    __shared__ uint16_t s_lut[1 << kLutBits];
-    __shared__ uint8_t s_len[ZC_T1_NSYM];
+    __shared__ __align__(16) uint32_t s_stream[kWaves][kStreamWords];
+    __shared__ uint16_t s_lut[kLutSize];
+    __shared__ uint8_t s_len[256];
 
-    const uint32_t lane = threadIdx.x;
-    for (uint32_t i = lane; i < (1u << kLutBits); i += kLanes)
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & (kLanes - 1);
+    const uint32_t wave = tid / kLanes;
+    for (uint32_t i = tid; i < (1u << kLutBits); i += kBlock)
         s_lut[i] = c_lut[i];
-    if (lane < ZC_T1_NSYM)
-        s_len[lane] = c_len[lane];
+    if (tid < (1u << kTailBits))
+        s_lut[kLutTail + tid] = c_tail[tid];
+    // raw groups: 8 bits b decode to the entry (255 - b, 8 bits)
+    s_lut[kLutRaw + tid] = static_cast<uint16_t>(((255u - tid) << 8) | 8u);
+    {
+        const uint32_t s = tid < static_cast<uint32_t>(kEsc) ? tid : static_cast<uint32_t>(kEsc);
+        s_len[tid] = static_cast<uint8_t>(c_len[s] + (s == static_cast<uint32_t>(kEsc) ? 8 : 0));
+    }
+    __syncthreads();
 
-    const uint32_t item = blockIdx.x;
+    const uint32_t item = blockIdx.x * kWaves + wave;
+    if (item >= tab.nitems)
+        return;
     const int c = find_chunk(tab, item);
     const uint32_t n = tab.n[c];
     const uint32_t t = item - tab.item_begin[c];
@@ -431,162 +813,13 @@ void zc_decompress_kernel(const uint8_t* __restrict__ in, uint16_t* __restrict__
     }
     if (n == 0)
         return;
-
-    // tile extent
-    const uint32_t* toffs = reinterpret_cast<const uint32_t*>(src + 32);
-    const uint32_t toff = toffs[t];
-    const uint64_t next = (t + 1 < G.T) ? toffs[t + 1] : comp - G.X;
-    const uint32_t base = t * kTile;
-    const uint32_t rem = min(n - base, static_cast<uint32_t>(kTile));
-    if ((t == 0 && toff != 0) || toff > next || next > comp - G.X) {
-        if (lane == 0)
-            report(status, ZC_REASON_TILE, c);
-        return;
-    }
-    const uint32_t tile_bytes = static_cast<uint32_t>(next - toff);
-
-    // group metadata
-    const uint32_t ng = group_members(rem, lane);
-    const uint32_t emax = src[32 + 4ull * G.T + 64ull * t + lane];
-    const uint32_t glen =
-        *reinterpret_cast<const uint16_t*>(src + 32 + 68ull * G.T + 2ull * (64ull * t + lane));
-    if (__ballot(glen > 8 * ng || (ng == 0 && emax != 0))) {
-        if (lane == 0)
-            report(status, ZC_REASON_GROUP, c);
-        return;
-    }
-    uint32_t tile_bits;
-    const uint32_t off = wave_excl_scan(glen, lane, &tile_bits);
-    const uint32_t tile_words = (tile_bits + 31) >> 5;
-    if (tile_bytes != 4 * tile_words) {
-        if (lane == 0)
-            report(status, ZC_REASON_TILE, c);
-        return;
-    }
-
-    // stage the tile stream in LDS (plus two zero guard words)
-    const uint32_t* ssrc = reinterpret_cast<const uint32_t*>(src + G.X + toff);
-    for (uint32_t w = lane; w < tile_words; w += kLanes)
-        s_bits[w] = ssrc[w];
-    if (lane < 2)
-        s_bits[tile_words + lane] = 0;
-    __syncthreads();
-
-    int err = 0;
-    if ((tile_bits & 31) && lane == 0) {
-        const uint32_t last = s_bits[tile_words - 1];
-        if (last & ((1u << (32 - (tile_bits & 31))) - 1))
-            err = ZC_REASON_PADDING;
-    }
-    if (t == 0) {
-        const uint64_t g1 = 32 + 196ull * G.T;
-        if (g1 + lane < G.R && src[g1 + lane] != 0)
-            err = ZC_REASON_GAP;
-    }
-    if (t == G.T - 1) {
-        if (G.R + n + lane < G.X && src[G.R + n + lane] != 0)
-            err = ZC_REASON_GAP;
-    }
-
-    const bool raw_mode = ng > 0 && glen == 8 * ng;
-    const bool vec_out = rem == kTile && ((reinterpret_cast<uintptr_t>(dst) & 15) == 0);
-    const uint8_t* rsrc = src + G.R;
-    uint32_t pos = off;
-    const uint32_t end = off + glen;
-    uint32_t seen_max = 0, coded_len = 0;
-
-#pragma unroll 1
-    for (int k = 0; k < kSteps; ++k) {
-        uint32_t e8[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            uint32_t e = 0;
-            if (static_cast<uint32_t>(k * 8 + j) < ng && err == 0) {
-                if (pos >= end) {
-                    err = ZC_REASON_LENGTH;
-                } else {
-                    const uint32_t w0 = s_bits[pos >> 5], w1 = s_bits[(pos >> 5) + 1];
-                    const uint32_t sh = pos & 31;
-                    const uint32_t win = sh ? (w0 << sh) | (w1 >> (32 - sh)) : w0;
-                    if (raw_mode) {
-                        e = win >> 24;
-                        pos += 8;
-                        const uint32_t d = emax - e;   // may wrap: then >= 16
-                        coded_len += d < static_cast<uint32_t>(kEsc) ? s_len[d] : s_len[kEsc] + 8u;
-                    } else {
-                        uint32_t ent = s_lut[win >> (32 - kLutBits)];
-                        uint32_t sym, L;
-                        if (ent != 0) {
-                            sym = ent >> 8;
-                            L = ent & 0xFF;
-                        } else {
-                            sym = 0xFFFFFFFFu;
-                            L = 0;
-                            for (uint32_t l = kLutBits + 1; l <= ZC_T1_MAXLEN; ++l) {
-                                const uint32_t v = win >> (32 - l);
-                                if (v < c_limit[l]) {
-                                    const uint32_t rank = v - c_base[l];
-                                    sym = c_sorted[rank < ZC_T1_NSYM ? rank : ZC_T1_NSYM - 1];
-                                    L = l;
-                                    break;
-                                }
-                            }
-                        }
-                        if (sym == 0xFFFFFFFFu) {
-                            err = ZC_REASON_SYMBOL;
-                        } else if (sym == static_cast<uint32_t>(kEsc)) {
-                            e = (win >> (32 - L - 8)) & 0xFF;
-                            L += 8;
-                            if (e + kEsc > emax)
-                                err = ZC_REASON_ESCAPE;
-                        } else if (sym > emax) {
-                            err = ZC_REASON_SYMBOL;
-                        } else {
-                            e = emax - sym;
-                        }
-                        pos += L;
-                        if (pos > end && err == 0)
-                            err = ZC_REASON_SYMBOL;
-                    }
-                    seen_max = max(seen_max, e);
-                }
-            }
-            e8[j] = e;
-        }
-        const uint32_t i0 = base + k * 512 + lane * 8;
-        if (vec_out) {
-            const uint2 rw = *reinterpret_cast<const uint2*>(rsrc + i0);
-            uint4 o;
-            o.x = (__builtin_amdgcn_perm(rw.x, rw.x, 0x01010000u) & 0x807F807Fu) | (e8[0] << 7) | (e8[1] << 23);
-            o.y = (__builtin_amdgcn_perm(rw.x, rw.x, 0x03030202u) & 0x807F807Fu) | (e8[2] << 7) | (e8[3] << 23);
-            o.z = (__builtin_amdgcn_perm(rw.y, rw.y, 0x01010000u) & 0x807F807Fu) | (e8[4] << 7) | (e8[5] << 23);
-            o.w = (__builtin_amdgcn_perm(rw.y, rw.y, 0x03030202u) & 0x807F807Fu) | (e8[6] << 7) | (e8[7] << 23);
-            *reinterpret_cast<uint4*>(dst + i0) = o;
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (i0 + j < n) {
-                    const uint32_t r = rsrc[i0 + j];
-                    dst[i0 + j] = static_cast<uint16_t>(((r & 0x80u) << 8) | (e8[j] << 7) | (r & 0x7Fu));
-                }
-            }
-        }
-    }
-    if (err == 0 && ng > 0) {
-        if (raw_mode) {
-            if (seen_max != emax)
-                err = ZC_REASON_EMAX;
-            else if (coded_len < 8 * ng)
-                err = ZC_REASON_RAWMODE;
-        } else {
-            if (pos != end)
-                err = ZC_REASON_LENGTH;
-            else if (seen_max != emax)
-                err = ZC_REASON_EMAX;
-        }
-    }
-    if (err)
-        report(status, err, c);
+    const uint32_t rem = min(n - t * kTile, static_cast<uint32_t>(kTile));
+    if (rem == kTile)
+        decompress_tile<true>(src, dst, status, c, n, t, G, lane, s_stream[wave], s_lut, s_len,
+                              comp);
+    else
+        decompress_tile_partial(src, dst, status, c, n, t, lane, s_stream[wave], s_lut, s_len,
+                                comp);
 }
 
 // ------------------------------------------------------------ host side
@@ -616,6 +849,8 @@ Counts check_counts(const int64_t* counts, int32_t num_chunks)
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 constexpr size_t kWsHeader = 256;   // ticket counter(s)
+
+uint32_t blocks_for(uint32_t items) { return (items + kWaves - 1) / kWaves; }
 
 }  // namespace
 
@@ -706,8 +941,8 @@ int zc_compress(const uint16_t* d_in, const int64_t* counts, int32_t num_chunks,
         const uint32_t cblocks = (words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024;
         hipLaunchKernelGGL(zc_clear_kernel, dim3(cblocks), dim3(256), 0, s,
                            static_cast<uint64_t*>(d_ws), words);
-        hipLaunchKernelGGL(zc_compress_kernel, dim3(items), dim3(kLanes), 0, s, d_in, out,
-                           d_comp_sizes + c0, status, ticket, tab);
+        hipLaunchKernelGGL(zc_compress_kernel, dim3(blocks_for(items)), dim3(kBlock), 0, s, d_in,
+                           out, d_comp_sizes + c0, status, ticket, tab);
         if (hipGetLastError() != hipSuccess)
             return ZC_EHIP;
     }
@@ -755,8 +990,8 @@ int zc_decompress(const void* d_in, size_t in_bytes, const int64_t* in_offsets,
         tab.nchunks = m;
         tab.nitems = items;
         tab.item_begin[m] = items;
-        hipLaunchKernelGGL(zc_decompress_kernel, dim3(items), dim3(kLanes), 0, s, in, d_out,
-                           d_status, tab);
+        hipLaunchKernelGGL(zc_decompress_kernel, dim3(blocks_for(items)), dim3(kBlock), 0, s, in,
+                           d_out, d_status, tab);
         if (hipGetLastError() != hipSuccess)
             return ZC_EHIP;
     }
@@ -787,10 +1022,13 @@ int zc_code_table(int32_t table_id, int32_t* lengths, uint32_t* codes, double* p
         static const uint32_t built_len[] = ZC_T1_LEN_INIT;
         static const uint32_t built_code[] = ZC_T1_CODE_INIT;
         static const uint32_t built_lut[] = ZC_T1_LUT_INIT;
+        static const uint32_t built_tail[] = ZC_T1_TAIL_INIT;
         for (int s = 0; ok && s < ZC_T1_NSYM; ++s)
             ok = static_cast<uint32_t>(tab.len[s]) == built_len[s] && tab.code[s] == built_code[s];
         for (int i = 0; ok && i < (1 << kLutBits); ++i)
             ok = tab.lut[i] == built_lut[i];
+        for (int i = 0; ok && i < (1 << kTailBits); ++i)
+            ok = tab.tail[i] == built_tail[i] && tab.tail_ok;
     });
     if (!ok)
         return ZC_EINVAL;

@@ -125,6 +125,27 @@ bool build_table(Table* t)
         for (uint32_t i = 0; i < count; ++i)
             t->lut[first + i] = static_cast<uint16_t>((s << 8) | L);
     }
+    // Second level for the long code words (all must share the all-ones
+    // prefix of kLutBits bits and fit in kLutBits + kTailBits bits).
+    t->tail_ok = true;
+    std::memset(t->tail, 0, sizeof t->tail);
+    for (int s = 0; s < kSymbols; ++s) {
+        const int L = t->len[s];
+        if (L <= kLutBits)
+            continue;
+        if (L > kLutBits + kTailBits || (t->code[s] >> (L - kLutBits)) != (1u << kLutBits) - 1) {
+            t->tail_ok = false;
+            continue;
+        }
+        const int rest = L - kLutBits;                       // bits after the prefix
+        const uint32_t low = t->code[s] & ((1u << rest) - 1);
+        const uint32_t first = low << (kTailBits - rest);
+        for (uint32_t i = 0; i < (1u << (kTailBits - rest)); ++i)
+            t->tail[first + i] = static_cast<uint16_t>((s << 8) | L);
+    }
+    for (int i = 0; i < (1 << kTailBits); ++i)
+        if (t->tail[i] == 0)
+            t->tail_ok = false;
     // Per-length canonical ranges for the long code words: a window whose
     // first L bits are v (left-aligned in 32 bits) holds a code word of
     // length L if v < limit[L]; its symbol is sym[v - base[L]].

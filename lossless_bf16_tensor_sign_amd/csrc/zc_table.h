@@ -19,7 +19,14 @@ struct Table {
     uint32_t limit[kMaxCodeLen + 1];     // canonical decode, per length
     int32_t base[kMaxCodeLen + 1];
     uint8_t sorted_sym[kSymbols];        // symbols by (length, symbol)
+    // Second decoder level: every code word longer than kLutBits bits must
+    // start with kLutBits ones and be at most kLutBits + kTailBits long; the
+    // kTailBits bits after that prefix then select its entry.
+    bool tail_ok;
+    uint16_t tail[1 << 4];
 };
+
+constexpr int kTailBits = 4;
 
 // Phase-averaged law of d = E_max - e: w[0..15] = P(d), w[16] = P(d >= 16).
 void exponent_law(double* w);

@@ -45,5 +45,10 @@ int main()
     for (int r = 0; r < zc::kSymbols; ++r)
         buf[r] = t.sorted_sym[r];
     row("ZC_T1_SORTED_INIT", buf, zc::kSymbols);
+    std::printf("#define ZC_T1_TAIL_OK %d\n", t.tail_ok ? 1 : 0);
+    for (int i = 0; i < (1 << zc::kTailBits); ++i)
+        buf[i] = t.tail[i];
+    row("ZC_T1_TAIL_INIT", buf, 1 << zc::kTailBits);
+    std::printf("#define ZC_T1_ESC_LEN %d\n", t.len[zc::kEscape]);
     return 0;
 }
