@@ -45,8 +45,10 @@ constexpr int kWaves = 4;                          // waves per workgroup
 constexpr int kBlock = kLanes * kWaves;
 constexpr int kSteps = 16;
 constexpr int kTile = 8192;
-constexpr int kTileWords = kTile * 8 / 32;        // raw tile stream: 2048 words
-constexpr int kStreamWords = kTileWords + 8;      // + guard words
+constexpr int kStageWords = 1024;                 // LDS tile-stream buffer per wave (4 KiB)
+constexpr int kStageAlloc = kStageWords + 8;      // + guard and carry words
+constexpr int kMinWavesEnc = 4;                   // occupancy targets, waves per SIMD
+constexpr int kMinWavesDec = 8;
 constexpr int kMaxChunks = 64;                     // chunks per launch
 constexpr uint32_t kMagic = 0x3142435Au;
 constexpr uint32_t kVerTable = 0x00010001u;        // version 1, table_id 1
@@ -186,9 +188,9 @@ __global__ void zc_clear_kernel(uint64_t* __restrict__ p, uint32_t words)
         p[i] = 0;
 }
 
-// Encoder table entry for d = 0..255: code bits 0..21 (an escape carries
-// its code followed by 8 zero bits for the exponent), length in bits 24..28,
-// bit 31 set for escapes.
+// Encoder entry for d = 0..255 used when escapes occur: code bits 0..21 (an
+// escape carries its code followed by 8 zero bits for the exponent), length
+// in bits 24..28, bit 31 set for escapes.
 __device__ inline uint32_t enc_entry(uint32_t d)
 {
     const uint32_t s = d < static_cast<uint32_t>(kEsc) ? d : static_cast<uint32_t>(kEsc);
@@ -199,6 +201,12 @@ __device__ inline uint32_t enc_entry(uint32_t d)
     }
     return code | (len << 24) | (s == static_cast<uint32_t>(kEsc) ? 0x80000000u : 0u);
 }
+
+struct EncTables {
+    uint32_t esc[256];    // enc_entry(d)
+    uint16_t code[256];   // code word of d (the escape code for d >= 16)
+    uint8_t len[256];     // coded length of d, escape payload included
+};
 
 struct TileCtx {
     const uint16_t* src;
@@ -217,7 +225,7 @@ __device__ inline uint32_t load_split(const TileCtx& x, uint32_t (&ex)[kSteps][2
     const char* sbase = reinterpret_cast<const char*>(x.src + x.base);
     char* rbase = reinterpret_cast<char*>(x.dst + x.G.R + x.base);
     const uint32_t lo16 = x.lane * 16, lo8 = x.lane * 8;
-    constexpr int kBatch = FULL ? 8 : 2;
+    constexpr int kBatch = FULL ? 4 : 2;
     uint32_t mx = 0;
 #pragma unroll
     for (int h = 0; h < kSteps / kBatch; ++h) {
@@ -270,19 +278,24 @@ __device__ inline uint32_t load_split(const TileCtx& x, uint32_t (&ex)[kSteps][2
     return mx >> 7;   // missing members were loaded as 0
 }
 
-// Decoupled look-back: exclusive byte offset of tile `item` in its chunk.
-__device__ inline uint32_t look_back(uint64_t* __restrict__ status, uint32_t item, uint32_t t,
-                                     uint32_t first, uint32_t tile_bytes, uint32_t lane)
+// Decoupled look-back over per-tile status words (flag in bits 62-63:
+// 1 = the tile's own byte count is known, 2 = its inclusive prefix is).
+// Publishing comes first; the exclusive offset is resolved later, so the
+// caller can do other work while predecessors finish.
+__device__ inline void look_back_publish(uint64_t* __restrict__ status, uint32_t item, uint32_t t,
+                                         uint32_t tile_bytes, uint32_t lane)
 {
-    if (t == 0) {
-        if (lane == 0)
-            __hip_atomic_store(&status[item], kFlagInc | tile_bytes, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        return 0;
-    }
     if (lane == 0)
-        __hip_atomic_store(&status[item], kFlagAgg | tile_bytes, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&status[item], (t == 0 ? kFlagInc : kFlagAgg) | tile_bytes,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline uint32_t look_back_resolve(uint64_t* __restrict__ status, uint32_t item,
+                                             uint32_t t, uint32_t first, uint32_t tile_bytes,
+                                             uint32_t lane)
+{
+    if (t == 0)
+        return 0;
     int64_t top = static_cast<int64_t>(item) - 1;
     uint32_t acc = 0;
     while (true) {
@@ -317,64 +330,108 @@ __device__ inline uint32_t look_back(uint64_t* __restrict__ status, uint32_t ite
     return acc;
 }
 
-// Raw groups of a full tile whose 64 groups are all raw: the exponents
-// themselves, 8 bits each, first value most significant.  Every lane holds
-// 1024 bits, so lane offsets are word aligned.
-__device__ inline void emit_all_raw(uint32_t* __restrict__ s_stream,
-                                    const uint32_t (&dd)[kSteps][2], uint32_t emax, uint32_t off)
+// A raw group of a full tile: its 128 exponents, 8 bits each, first value
+// most significant, as 32 words starting at buffer word `w0`.
+__device__ inline void emit_raw_words(uint32_t* __restrict__ s, const uint32_t (&dd)[kSteps][2],
+                                      uint32_t emax, uint32_t w0)
 {
     const uint32_t em4 = emax * 0x01010101u;
-    uint32_t* w = s_stream + (off >> 5);
 #pragma unroll
     for (int k = 0; k < kSteps; ++k) {
         const uint32_t e0 = em4 - dd[k][0], e1 = em4 - dd[k][1];
-        w[2 * k] = __builtin_amdgcn_perm(e0, e0, 0x00010203u);
-        w[2 * k + 1] = __builtin_amdgcn_perm(e1, e1, 0x00010203u);
+        *reinterpret_cast<uint2*>(&s[w0 + 2 * k]) =
+            make_uint2(__builtin_amdgcn_perm(e0, e0, 0x00010203u),
+                       __builtin_amdgcn_perm(e1, e1, 0x00010203u));
     }
 }
 
-// Appends the group's code words (or, for a raw group, its exponents as
-// 8-bit code words) to the LDS tile stream from bit offset `off`.
+// Appends this lane's group to the LDS buffer from bit `off` (relative to
+// the buffer): one code word per value, or for a raw group (MIXED waves
+// only) its exponents as 8-bit words.  Inactive lanes write nothing.
+// A step whose coded values are all below the escape threshold appends its
+// code words two at a time (at most 28 bits per pair).
 template <bool FULL, bool MIXED>
-__device__ inline void emit_group(uint32_t* __restrict__ s_stream, const uint32_t* __restrict__ s_enc,
+__device__ inline void emit_group(uint32_t* __restrict__ s, const EncTables& tb,
                                   const uint32_t (&dd)[kSteps][2], uint32_t emax, uint32_t ng,
-                                  bool raw_mode, uint32_t off)
+                                  bool raw_mode, uint32_t off, bool active)
 {
     uint64_t acc = 0;
-    uint32_t nacc = off & 31;
-    uint32_t wi = off >> 5;
+    uint32_t nacc = active ? (off & 31) : 0u;
+    uint32_t wi = active ? (off >> 5) : 0u;
+    const bool coded = active && !raw_mode;
 #pragma unroll 1
     for (int k = 0; k < kSteps; ++k) {
         const uint32_t d4[2] = {dd[k][0], dd[k][1]};
+        const bool esc_here = coded && (((d4[0] | d4[1]) & 0xF0F0F0F0u) != 0);
+        if (__ballot(esc_here) == 0) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t d = (d4[j >> 2] >> (8 * (j & 3))) & 0xFF;
-            uint32_t ent = s_enc[d];
-            if (MIXED && raw_mode)
-                ent = ((emax - d) & 0xFF) | (8u << 24);
-            if (!FULL && static_cast<uint32_t>(k * 8 + j) >= ng)
-                ent = 0;
-            const uint32_t L = (ent >> 24) & 31;
-            const uint32_t esc = static_cast<uint32_t>(static_cast<int32_t>(ent) >> 31);
-            acc <<= L;
-            acc |= (ent & 0x3FFFFFu) | ((emax - d) & esc & 0xFFu);
-            nacc += L;
-            // the word that just filled up, if any (alignbit uses nacc mod 32)
-            const uint32_t w = __builtin_amdgcn_alignbit(hi32(acc), lo32(acc), nacc);
-            const uint32_t f = nacc >> 5;
-            atomicOr(&s_stream[wi], f ? w : 0u);
-            wi += f;
-            nacc &= 31;
+            for (int j = 0; j < 8; j += 2) {
+                uint32_t c2[2], l2[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int jj = j + u;
+                    const uint32_t d = (d4[jj >> 2] >> (8 * (jj & 3))) & 0xFF;
+                    uint32_t c = tb.code[d], l = tb.len[d];
+                    if (MIXED) {
+                        c = raw_mode ? ((emax - d) & 0xFF) : c;
+                        l = raw_mode ? 8u : l;
+                    }
+                    const bool valid = active && (FULL || static_cast<uint32_t>(k * 8 + jj) < ng);
+                    c2[u] = valid ? c : 0u;
+                    l2[u] = valid ? l : 0u;
+                }
+                const uint32_t pl = l2[0] + l2[1];
+                acc = (acc << pl) | ((c2[0] << l2[1]) | c2[1]);
+                nacc += pl;
+                const uint32_t w = __builtin_amdgcn_alignbit(hi32(acc), lo32(acc), nacc);
+                const uint32_t f = nacc >> 5;
+                atomicOr(&s[wi], f ? w : 0u);
+                wi += f;
+                nacc &= 31;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t d = (d4[j >> 2] >> (8 * (j & 3))) & 0xFF;
+                uint32_t ent = tb.esc[d];
+                if (MIXED && raw_mode)
+                    ent = ((emax - d) & 0xFF) | (8u << 24);
+                const bool valid = active && (FULL || static_cast<uint32_t>(k * 8 + j) < ng);
+                ent = valid ? ent : 0u;
+                const uint32_t L = (ent >> 24) & 31;
+                const uint32_t esc = static_cast<uint32_t>(static_cast<int32_t>(ent) >> 31);
+                acc <<= L;
+                acc |= (ent & 0x3FFFFFu) | ((emax - d) & esc & 0xFFu);
+                nacc += L;
+                const uint32_t w = __builtin_amdgcn_alignbit(hi32(acc), lo32(acc), nacc);
+                const uint32_t f = nacc >> 5;
+                atomicOr(&s[wi], f ? w : 0u);
+                wi += f;
+                nacc &= 31;
+            }
         }
     }
     if (nacc)
-        atomicOr(&s_stream[wi], lo32(acc) << (32 - nacc));
+        atomicOr(&s[wi], lo32(acc) << (32 - nacc));
+}
+
+__device__ inline void zero_words(uint32_t* __restrict__ s, uint32_t count, uint32_t lane)
+{
+    for (uint32_t w = lane * 4; w < count; w += kLanes * 4)
+        *reinterpret_cast<uint4*>(&s[w]) = make_uint4(0, 0, 0, 0);
+}
+
+__device__ inline void store_words(uint32_t* __restrict__ g, const uint32_t* __restrict__ s,
+                                   uint32_t count, uint32_t lane)
+{
+    for (uint32_t w = lane; w < count; w += kLanes)
+        g[w] = s[w];
 }
 
 template <bool FULL>
 __device__ void compress_tile(const TileCtx& x, int64_t* __restrict__ comp_sizes,
-                              uint64_t* __restrict__ status, uint32_t* __restrict__ s_stream,
-                              const uint32_t* __restrict__ s_enc, const uint8_t* __restrict__ s_len)
+                              uint64_t* __restrict__ status, uint32_t* __restrict__ s,
+                              const EncTables& tb)
 {
     const uint32_t lane = x.lane;
     const uint32_t ng = FULL ? 128u : group_members(x.rem, lane);
@@ -397,48 +454,78 @@ __device__ void compress_tile(const TileCtx& x, int64_t* __restrict__ comp_sizes
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const uint32_t d = (d4[j >> 2] >> (8 * (j & 3))) & 0xFF;
-            const uint32_t L = s_len[d];
+            const uint32_t L = tb.len[d];
             bits += (FULL || static_cast<uint32_t>(k * 8 + j) < ng) ? L : 0u;
         }
     }
     const bool raw_mode = ng > 0 && bits >= 8 * ng;
     const uint32_t glen = raw_mode ? 8 * ng : bits;
 
-    // 3. lane offsets, tile size, offset of the tile in the chunk
+    // 3. lane offsets and tile size; the tile's size is published at once
     uint32_t tile_bits;
     const uint32_t off = wave_excl_scan(glen, lane, &tile_bits);
     const uint32_t tile_words = (tile_bits + 31) >> 5;
     const uint32_t tile_bytes = tile_words * 4;
-    const uint32_t toff = look_back(status, x.item, x.t, x.first, tile_bytes, lane);
+    look_back_publish(status, x.item, x.t, tile_bytes, lane);
 
-    // 4. index arrays
+    // 4. the tile stream, assembled in LDS (most significant bit first) while
+    //    the predecessors finish; then the tile's offset, the index arrays
+    //    and a coalesced store.  A stream longer than the buffer (many raw
+    //    groups) is assembled and stored in two passes, lanes 0-31 then 32-63.
+    const uint64_t raw_lanes = __ballot(raw_mode);
+    uint32_t toff;
+    if (tile_words <= static_cast<uint32_t>(kStageWords)) {
+        zero_words(s, tile_words + 1, lane);
+        wave_lds_sync();
+        if (raw_lanes == 0)
+            emit_group<FULL, false>(s, tb, dd, emax, ng, raw_mode, off, true);
+        else
+            emit_group<FULL, true>(s, tb, dd, emax, ng, raw_mode, off, true);
+        wave_lds_sync();
+        toff = look_back_resolve(status, x.item, x.t, x.first, tile_bytes, lane);
+        uint32_t* gstream = reinterpret_cast<uint32_t*>(x.dst + x.G.X + toff);
+        store_words(gstream, s, tile_words, lane);
+    } else {
+        toff = look_back_resolve(status, x.item, x.t, x.first, tile_bytes, lane);
+        uint32_t* gstream = reinterpret_cast<uint32_t*>(x.dst + x.G.X + toff);
+        const bool all_raw = FULL && raw_lanes == ~0ull;
+        const uint32_t m = __shfl(off, 32) >> 5;   // first word lanes 32-63 touch
+#pragma unroll 1
+        for (int h = 0; h < 2; ++h) {
+            const bool active = (lane >> 5) == static_cast<uint32_t>(h);
+            const uint32_t bw = h ? m : 0u;        // buffer word 0 = stream word bw
+            const uint32_t count = h ? tile_words - m : m + 1;
+            if (h) {
+                const uint32_t carry = s[m];       // lanes 0-31's bits in word m
+                wave_lds_sync();
+                zero_words(s, count + 1, lane);
+                wave_lds_sync();
+                if (lane == 0)
+                    s[0] = carry;
+            } else {
+                zero_words(s, count + 1, lane);
+            }
+            wave_lds_sync();
+            if (all_raw) {
+                if (active)
+                    emit_raw_words(s, dd, emax, (off >> 5) - bw);
+            } else {
+                emit_group<FULL, true>(s, tb, dd, emax, ng, raw_mode, off - 32 * bw, active);
+            }
+            wave_lds_sync();
+            store_words(gstream + bw, s, h ? count : m, lane);
+            wave_lds_sync();
+        }
+    }
+
+    // 5. index arrays
     if (lane == 0)
         *reinterpret_cast<uint32_t*>(x.dst + 32 + 4ull * x.t) = toff;
     x.dst[32 + 4ull * x.G.T + 64ull * x.t + lane] = static_cast<uint8_t>(emax);
     *reinterpret_cast<uint16_t*>(x.dst + 32 + 68ull * x.G.T + 2ull * (64ull * x.t + lane)) =
         static_cast<uint16_t>(glen);
 
-    // 5. pack the lane streams into the LDS tile stream, most significant bit first
-    const uint64_t raw_lanes = __ballot(raw_mode);
-    if (FULL && raw_lanes == ~0ull) {
-        emit_all_raw(s_stream, dd, emax, off);      // every word written once
-    } else {
-        for (uint32_t w = lane * 4; w <= tile_words; w += kLanes * 4)
-            *reinterpret_cast<uint4*>(&s_stream[w]) = make_uint4(0, 0, 0, 0);
-        wave_lds_sync();
-        if (raw_lanes == 0)
-            emit_group<FULL, false>(s_stream, s_enc, dd, emax, ng, raw_mode, off);
-        else
-            emit_group<FULL, true>(s_stream, s_enc, dd, emax, ng, raw_mode, off);
-    }
-    wave_lds_sync();
-
-    // 6. coalesced store of the tile stream
-    uint32_t* sdst = reinterpret_cast<uint32_t*>(x.dst + x.G.X + toff);
-    for (uint32_t w = lane; w < tile_words; w += kLanes)
-        sdst[w] = s_stream[w];
-
-    // 7. the last tile finishes the chunk: header, gaps, size
+    // 6. the last tile finishes the chunk: header, gaps, size
     if (x.t == x.G.T - 1) {
         const uint64_t comp = x.G.X + toff + tile_bytes;
         if (lane < 8)
@@ -458,8 +545,7 @@ __device__ void compress_tile(const TileCtx& x, int64_t* __restrict__ comp_sizes
 __device__ __attribute__((noinline)) void compress_tile_partial(
     const uint16_t* src, uint8_t* dst, uint32_t n, uint32_t t, uint32_t item, uint32_t first,
     uint32_t lane, int c, int64_t* __restrict__ comp_sizes, uint64_t* __restrict__ status,
-    uint32_t* __restrict__ s_stream, const uint32_t* __restrict__ s_enc,
-    const uint8_t* __restrict__ s_len)
+    uint32_t* __restrict__ s, const EncTables& tb)
 {
     TileCtx x;
     x.src = src;
@@ -473,26 +559,27 @@ __device__ __attribute__((noinline)) void compress_tile_partial(
     x.G = geometry(n);
     x.base = t * kTile;
     x.rem = min(n - x.base, static_cast<uint32_t>(kTile));
-    compress_tile<false>(x, comp_sizes, status, s_stream, s_enc, s_len);
+    compress_tile<false>(x, comp_sizes, status, s, tb);
 }
 
-__global__ __launch_bounds__(kBlock, 4)
+__global__ __launch_bounds__(kBlock, kMinWavesEnc)
 void zc_compress_kernel(const uint16_t* __restrict__ in, uint8_t* __restrict__ out,
                         int64_t* __restrict__ comp_sizes,
                         uint64_t* __restrict__ status, uint32_t* __restrict__ ticket,
                         ChunkTable tab)
 {
-    __shared__ __align__(16) uint32_t s_stream[kWaves][kStreamWords];
-    __shared__ uint32_t s_enc[256];
-    __shared__ uint8_t s_len[256];
+    __shared__ __align__(16) uint32_t s_stage[kWaves][kStageAlloc];
+    __shared__ EncTables tb;
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & (kLanes - 1);
     const uint32_t wave = tid / kLanes;
     {
         const uint32_t e = enc_entry(tid);
-        s_enc[tid] = e;
-        s_len[tid] = static_cast<uint8_t>((e >> 24) & 31);
+        tb.esc[tid] = e;
+        tb.len[tid] = static_cast<uint8_t>((e >> 24) & 31);
+        const uint32_t s = tid < static_cast<uint32_t>(kEsc) ? tid : static_cast<uint32_t>(kEsc);
+        tb.code[tid] = static_cast<uint16_t>(c_code[s]);
     }
     __syncthreads();
 
@@ -525,10 +612,10 @@ void zc_compress_kernel(const uint16_t* __restrict__ in, uint8_t* __restrict__ o
     x.rem = min(x.n - x.base, static_cast<uint32_t>(kTile));
     const bool full = x.rem == kTile && ((reinterpret_cast<uintptr_t>(x.src) & 15) == 0);
     if (full)
-        compress_tile<true>(x, comp_sizes, status, s_stream[wave], s_enc, s_len);
+        compress_tile<true>(x, comp_sizes, status, s_stage[wave], tb);
     else
         compress_tile_partial(x.src, x.dst, x.n, x.t, x.item, x.first, lane, x.c, comp_sizes,
-                              status, s_stream[wave], s_enc, s_len);
+                              status, s_stage[wave], tb);
 }
 
 // ------------------------------------------------------------ decompress
@@ -538,24 +625,48 @@ __device__ inline void report(int32_t* status, int reason, int c)
     atomicCAS(status, 0, (reason << 24) | (c & 0xFFFFFF));
 }
 
-// 64 stream bits starting at bit `pos` of the LDS tile stream (word index
-// clamped to `cap`, past which the stream holds zero guard words).
-__device__ inline uint64_t window64(const uint32_t* __restrict__ s, uint32_t pos, uint32_t cap)
-{
-    const uint32_t wi = min(pos >> 5, cap);
-    const uint32_t w0 = s[wi], w1 = s[wi + 1], w2 = s[wi + 2];
-    const uint32_t sh = pos & 31;
-    const uint32_t hi = hi32(((static_cast<uint64_t>(w0) << 32) | w1) << sh);
-    const uint32_t lo = hi32(((static_cast<uint64_t>(w1) << 32) | w2) << sh);
-    return (static_cast<uint64_t>(hi) << 32) | lo;
-}
+// 64 stream bits from bit `pos` of a tile stream staged in LDS (word index
+// clamped to `cap`, where the buffer holds zero guard words).
+struct LdsWindow {
+    const uint32_t* s;
+    uint32_t cap;
+    __device__ inline uint64_t operator()(uint32_t pos) const
+    {
+        const uint32_t wi = min(pos >> 5, cap);
+        const uint32_t w0 = s[wi], w1 = s[wi + 1], w2 = s[wi + 2];
+        const uint32_t sh = pos & 31;
+        const uint32_t hi = hi32(((static_cast<uint64_t>(w0) << 32) | w1) << sh);
+        const uint32_t lo = hi32(((static_cast<uint64_t>(w1) << 32) | w2) << sh);
+        return (static_cast<uint64_t>(hi) << 32) | lo;
+    }
+};
 
-// Table entry of the symbol at the top of window W: length in bits 0..7,
+// The same from the tile stream in global memory (words past `nwords` read
+// as zero); used for tile streams longer than the LDS buffer.
+struct GlobalWindow {
+    const uint32_t* g;
+    uint32_t nwords;
+    __device__ inline uint64_t operator()(uint32_t pos) const
+    {
+        const uint32_t wi = pos >> 5;
+        const uint32_t w0 = wi < nwords ? g[wi] : 0u;
+        const uint32_t w1 = wi + 1 < nwords ? g[wi + 1] : 0u;
+        const uint32_t w2 = wi + 2 < nwords ? g[wi + 2] : 0u;
+        const uint32_t sh = pos & 31;
+        const uint32_t hi = hi32(((static_cast<uint64_t>(w0) << 32) | w1) << sh);
+        const uint32_t lo = hi32(((static_cast<uint64_t>(w1) << 32) | w2) << sh);
+        return (static_cast<uint64_t>(hi) << 32) | lo;
+    }
+};
+
+// Table entry of the symbol at the top of a window: length in bits 0..7,
 // symbol in bits 8.. (signed).  An escape is returned as (d << 8) | 22 with
-// d = E_max - e, so that E_max minus the symbol field is e in every case.
-// Raw groups look their 8 bits up in entries that hold 255 - e.
+// d = E_max - e, so that E_max minus the symbol field is e in every case;
+// its d also lowers esc_min (a valid escape has d >= 16).  Raw groups look
+// their 8 bits up in entries that hold 255 - e.
 __device__ inline uint32_t decode_entry(const uint16_t* __restrict__ s_lut, uint32_t top,
-                                        uint32_t lut_sh, uint32_t lut_base, uint32_t emax)
+                                        uint32_t lut_sh, uint32_t lut_base, uint32_t emax,
+                                        bool valid, int32_t& esc_min)
 {
     uint32_t ent = s_lut[(top >> lut_sh) + lut_base];
     if (ent == 0) {
@@ -563,47 +674,221 @@ __device__ inline uint32_t decode_entry(const uint16_t* __restrict__ s_lut, uint
         ent = s_lut[kLutTail + ((top >> (32 - kLutBits - kTailBits)) & ((1u << kTailBits) - 1))];
         if ((ent >> 8) == static_cast<uint32_t>(kEsc)) {
             const uint32_t e = (top >> (32 - kEscLen - 8)) & 0xFF;
-            ent = ((emax - e) << 8) | (kEscLen + 8);
+            const int32_t d = static_cast<int32_t>(emax) - static_cast<int32_t>(e);
+            if (valid)
+                esc_min = min(esc_min, d);
+            ent = (static_cast<uint32_t>(d) << 8) | (kEscLen + 8);
         }
     }
     return ent;
 }
 
+// Joins 8 exponents with their sign+mantissa bytes and stores them.
 template <bool FULL>
-__device__ void decompress_tile(const uint8_t* __restrict__ src, uint16_t* __restrict__ dst,
-                                int32_t* __restrict__ status, int c, uint32_t n, uint32_t t,
-                                const Geom& G, uint32_t lane, uint32_t* __restrict__ s_stream,
-                                const uint16_t* __restrict__ s_lut,
-                                const uint8_t* __restrict__ s_len, uint64_t comp)
+__device__ inline void put_values(uint16_t* __restrict__ dst, const uint8_t* __restrict__ rsrc,
+                                  uint32_t n, uint32_t i0, uint2 r, const uint32_t (&e8)[8],
+                                  bool vec_out)
 {
-    const uint32_t base = t * kTile;
-    const uint32_t rem = min(n - base, static_cast<uint32_t>(kTile));
-    const uint32_t ng = FULL ? 128u : group_members(rem, lane);
-
-    // tile extent
-    const uint32_t* toffs = reinterpret_cast<const uint32_t*>(src + 32);
-    const uint32_t toff = toffs[t];
-    const uint64_t next = (t + 1 < G.T) ? toffs[t + 1] : comp - G.X;
-    if ((t == 0 && toff != 0) || toff > next || next > comp - G.X) {
-        if (lane == 0)
-            report(status, ZC_REASON_TILE, c);
-        return;
+    if (FULL && vec_out) {
+        uint4 o;
+        o.x = (__builtin_amdgcn_perm(r.x, r.x, 0x01010000u) & 0x807F807Fu) | (e8[0] << 7) | (e8[1] << 23);
+        o.y = (__builtin_amdgcn_perm(r.x, r.x, 0x03030202u) & 0x807F807Fu) | (e8[2] << 7) | (e8[3] << 23);
+        o.z = (__builtin_amdgcn_perm(r.y, r.y, 0x01010000u) & 0x807F807Fu) | (e8[4] << 7) | (e8[5] << 23);
+        o.w = (__builtin_amdgcn_perm(r.y, r.y, 0x03030202u) & 0x807F807Fu) | (e8[6] << 7) | (e8[7] << 23);
+        *reinterpret_cast<uint4*>(dst + i0) = o;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (i0 + j < n) {
+                const uint32_t b = rsrc[i0 + j];
+                dst[i0 + j] = static_cast<uint16_t>(((b & 0x80u) << 8) | ((e8[j] & 0xFF) << 7) | (b & 0x7Fu));
+            }
+        }
     }
-    const uint32_t tile_bytes = static_cast<uint32_t>(next - toff);
+}
 
-    // raw bytes, prefetched three steps ahead
-    const uint2* rsrc2 = reinterpret_cast<const uint2*>(src + G.R + base) + lane;
+struct DecState {
+    uint32_t pos;        // bit position in the tile stream
+    uint32_t seen_max;   // largest decoded exponent
+    uint32_t raw_coded;  // raw groups: coded length their values would take
+    int32_t esc_min;     // smallest E_max - e over escapes
+};
+
+// Decodes the 128 members of this lane's group from a window source and
+// writes the values.  Raw groups take 8-bit entries from the same table.
+template <bool FULL, class Win>
+__device__ inline void decode_group(const Win& win, const uint16_t* __restrict__ s_lut,
+                                    const uint8_t* __restrict__ s_len, const uint8_t* __restrict__ rsrc,
+                                    uint16_t* __restrict__ dst, uint32_t n, uint32_t base,
+                                    uint32_t lane, uint32_t ng, uint32_t emax, bool raw_mode,
+                                    bool any_raw, bool vec_out, DecState& st)
+{
+    const uint32_t emax_eff = raw_mode ? 255u : emax;
+    const uint32_t lut_sh = raw_mode ? 24u : static_cast<uint32_t>(32 - kLutBits);
+    const uint32_t lut_base = raw_mode ? static_cast<uint32_t>(kLutRaw) : 0u;
+
+    // sign+mantissa bytes, prefetched three steps ahead
+    const uint2* rsrc2 = reinterpret_cast<const uint2*>(rsrc + base) + lane;
     uint2 r0 = make_uint2(0, 0), r1 = r0, r2 = r0;
     if (FULL) {
         r0 = rsrc2[0];
         r1 = rsrc2[64];
         r2 = rsrc2[128];
     }
+#pragma unroll 1
+    for (int k = 0; k < kSteps; ++k) {
+        uint32_t e8[8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t pos0 = st.pos;
+            uint64_t W = win(pos0);
+            uint32_t used = 0;
+            int32_t esc_h = 255;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool valid = FULL || static_cast<uint32_t>(k * 8 + h * 4 + j) < ng;
+                uint32_t ent = decode_entry(s_lut, hi32(W), lut_sh, lut_base, emax, valid, esc_h);
+                if (!FULL && !valid)
+                    ent = 0;
+                e8[h * 4 + j] = emax_eff - static_cast<uint32_t>(static_cast<int32_t>(ent) >> 8);
+                W <<= (ent & 63);
+                used += ent & 0xFF;
+            }
+            if (__ballot(used > 64)) {
+                // a half-step longer than the window (several escapes): decode
+                // those lanes again symbol by symbol
+                if (used > 64) {
+                    uint32_t p = pos0;
+                    esc_h = 255;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const bool valid = FULL || static_cast<uint32_t>(k * 8 + h * 4 + j) < ng;
+                        uint32_t ent = decode_entry(s_lut, hi32(win(p)), lut_sh, lut_base, emax,
+                                                    valid, esc_h);
+                        if (!FULL && !valid)
+                            ent = 0;
+                        e8[h * 4 + j] = emax_eff - static_cast<uint32_t>(static_cast<int32_t>(ent) >> 8);
+                        p += ent & 0xFF;
+                    }
+                    used = p - pos0;
+                }
+            }
+            st.esc_min = min(st.esc_min, esc_h);
+            st.pos = pos0 + used;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (FULL || static_cast<uint32_t>(k * 8 + j) < ng)
+                st.seen_max = max(st.seen_max, e8[j]);
+        }
+        if (any_raw) {
+            // a raw group must not have been codable in fewer bits
+            if (raw_mode) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (FULL || static_cast<uint32_t>(k * 8 + j) < ng)
+                        st.raw_coded += s_len[(emax - e8[j]) & 0xFF];
+            }
+        }
+        const uint2 r = r0;
+        if (FULL) {
+            r0 = r1;
+            r1 = r2;
+            if (k + 3 < kSteps)
+                r2 = rsrc2[(k + 3) * 64];
+        }
+        put_values<FULL>(dst, rsrc, n, base + k * 512 + lane * 8, r, e8, vec_out);
+    }
+}
 
-    // group metadata
+// A full tile whose 64 groups are all raw: every group stream is 1024 bits
+// of plain exponents at bit 1024 * lane.  The 8 KiB tile stream is staged in
+// two halves, each decoded by the 32 lanes that own it.
+__device__ inline void decode_all_raw(const uint32_t* __restrict__ gstream,
+                                      uint32_t* __restrict__ s, const uint8_t* __restrict__ s_len,
+                                      const uint8_t* __restrict__ rsrc, uint16_t* __restrict__ dst,
+                                      uint32_t n, uint32_t base, uint32_t lane, uint32_t emax,
+                                      bool vec_out, DecState& st)
+{
+    const uint2* rsrc2 = reinterpret_cast<const uint2*>(rsrc + base) + lane;
+#pragma unroll 1
+    for (int h = 0; h < 2; ++h) {
+        wave_lds_sync();
+        for (uint32_t w = lane; w < static_cast<uint32_t>(kStageWords); w += kLanes)
+            s[w] = gstream[h * kStageWords + w];
+        wave_lds_sync();
+        if ((lane >> 5) == static_cast<uint32_t>(h)) {
+            const uint32_t* mine = s + (lane & 31) * 32;
+#pragma unroll 2
+            for (int k = 0; k < kSteps; ++k) {
+                const uint2 ew = *reinterpret_cast<const uint2*>(mine + 2 * k);
+                const uint32_t e4a = __builtin_amdgcn_perm(ew.x, ew.x, 0x00010203u);
+                const uint32_t e4b = __builtin_amdgcn_perm(ew.y, ew.y, 0x00010203u);
+                uint32_t e8[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    e8[j] = (e4a >> (8 * j)) & 0xFF;
+                    e8[4 + j] = (e4b >> (8 * j)) & 0xFF;
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    st.seen_max = max(st.seen_max, e8[j]);
+                    st.raw_coded += s_len[(emax - e8[j]) & 0xFF];
+                }
+                put_values<true>(dst, rsrc, n, base + k * 512 + lane * 8, rsrc2[k * 64], e8, vec_out);
+            }
+            st.pos += 1024;
+        }
+    }
+}
+
+template <bool FULL>
+__device__ void decompress_tile(const uint8_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                int32_t* __restrict__ status, int c, uint32_t n, uint32_t t,
+                                uint64_t bavail, uint32_t lane, uint32_t* __restrict__ s,
+                                const uint16_t* __restrict__ s_lut,
+                                const uint8_t* __restrict__ s_len)
+{
+    const Geom G = geometry(n);
+    const uint32_t base = t * kTile;
+    const uint32_t rem = min(n - base, static_cast<uint32_t>(kTile));
+    const uint32_t ng = FULL ? 128u : group_members(rem, lane);
+    if (G.X > bavail) {          // the index arrays and raw bytes cannot fit
+        if (lane == 0)
+            report(status, ZC_REASON_SIZE, c);
+        return;
+    }
+
+    // header, tile offsets and group metadata, all loaded at once
+    const uint32_t hw = lane < 8 ? reinterpret_cast<const uint32_t*>(src)[lane] : 0u;
+    const uint32_t* toffs = reinterpret_cast<const uint32_t*>(src + 32);
+    const uint32_t toff = toffs[t];
+    const uint32_t tnext = (t + 1 < G.T) ? toffs[t + 1] : 0u;
     const uint32_t emax = src[32 + 4ull * G.T + 64ull * t + lane];
     const uint32_t glen =
         *reinterpret_cast<const uint16_t*>(src + 32 + 68ull * G.T + 2ull * (64ull * t + lane));
+
+    const uint32_t h0 = __shfl(hw, 0), h1 = __shfl(hw, 1), h2 = __shfl(hw, 2),
+                   h3 = __shfl(hw, 3), h4 = __shfl(hw, 4), h5 = __shfl(hw, 5),
+                   h6 = __shfl(hw, 6), h7 = __shfl(hw, 7);
+    if (h0 != kMagic || h1 != kVerTable || h2 != 0 || h3 != 0 || h4 != n || h5 != 0) {
+        if (lane == 0)
+            report(status, ZC_REASON_HEADER, c);
+        return;
+    }
+    const uint64_t comp = h6 | (static_cast<uint64_t>(h7) << 32);
+    if (comp < G.X || comp > bavail || comp > chunk_bound(n)) {
+        if (lane == 0)
+            report(status, ZC_REASON_SIZE, c);
+        return;
+    }
+    const uint64_t next = (t + 1 < G.T) ? tnext : comp - G.X;
+    if ((t == 0 && toff != 0) || toff > next || next > comp - G.X) {
+        if (lane == 0)
+            report(status, ZC_REASON_TILE, c);
+        return;
+    }
+    const uint32_t tile_bytes = static_cast<uint32_t>(next - toff);
     if (__ballot(glen > 8 * ng || (ng == 0 && emax != 0))) {
         if (lane == 0)
             report(status, ZC_REASON_GROUP, c);
@@ -618,20 +903,8 @@ __device__ void decompress_tile(const uint8_t* __restrict__ src, uint16_t* __res
         return;
     }
 
-    // stage the tile stream in LDS, with zero guard words after it
-    const uint32_t* ssrc = reinterpret_cast<const uint32_t*>(src + G.X + toff);
-    for (uint32_t w = lane; w < tile_words; w += kLanes)
-        s_stream[w] = ssrc[w];
-    if (lane < 4)
-        s_stream[tile_words + lane] = 0;
-    wave_lds_sync();
-
+    const uint32_t* gstream = reinterpret_cast<const uint32_t*>(src + G.X + toff);
     int err = 0;
-    if ((tile_bits & 31) && lane == 0) {
-        const uint32_t last = s_stream[tile_words - 1];
-        if (last & ((1u << (32 - (tile_bits & 31))) - 1))
-            err = ZC_REASON_PADDING;
-    }
     if (t == 0) {
         const uint64_t g1 = 32 + 196ull * G.T;
         if (g1 + lane < G.R && src[g1 + lane] != 0)
@@ -641,111 +914,43 @@ __device__ void decompress_tile(const uint8_t* __restrict__ src, uint16_t* __res
         if (G.R + n + lane < G.X && src[G.R + n + lane] != 0)
             err = ZC_REASON_GAP;
     }
+    if ((tile_bits & 31) && lane == 0) {
+        const uint32_t last = gstream[tile_words - 1];
+        if (last & ((1u << (32 - (tile_bits & 31))) - 1))
+            err = ZC_REASON_PADDING;
+    }
 
     const bool raw_mode = ng > 0 && glen == 8 * ng;
-    const bool any_raw = __ballot(raw_mode) != 0;
-    const uint32_t emax_eff = raw_mode ? 255u : emax;
-    const uint32_t lut_sh = raw_mode ? 24u : static_cast<uint32_t>(32 - kLutBits);
-    const uint32_t lut_base = raw_mode ? static_cast<uint32_t>(kLutRaw) : 0u;
+    const uint64_t raw_lanes = __ballot(raw_mode);
     const bool vec_out = FULL && ((reinterpret_cast<uintptr_t>(dst) & 15) == 0);
-    const uint32_t cap = tile_words;
-    uint32_t pos = off;
-    uint32_t seen_max = 0, raw_coded = 0;
-    int32_t esc_min = 255;    // smallest E_max - e over escapes (must be >= 16)
-
-#pragma unroll 1
-    for (int k = 0; k < kSteps; ++k) {
-        uint32_t e8[8];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint32_t pos0 = pos;
-            uint64_t W = window64(s_stream, pos, cap);
-            uint32_t used = 0;
-            int32_t esc_h = 255;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint32_t ent = decode_entry(s_lut, hi32(W), lut_sh, lut_base, emax);
-                if (!FULL && static_cast<uint32_t>(k * 8 + h * 4 + j) >= ng)
-                    ent = 0;
-                const int32_t sym = static_cast<int32_t>(ent) >> 8;
-                e8[h * 4 + j] = emax_eff - static_cast<uint32_t>(sym);
-                if ((ent & 0xFF) == static_cast<uint32_t>(kEscLen + 8))
-                    esc_h = min(esc_h, sym);
-                W <<= (ent & 63);
-                used += ent & 0xFF;
-            }
-            if (__ballot(used > 64)) {
-                // a half-step longer than the window (several escapes): decode
-                // those lanes again symbol by symbol
-                if (used > 64) {
-                    uint32_t p = pos0;
-                    esc_h = 255;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        uint32_t ent = decode_entry(s_lut, hi32(window64(s_stream, p, cap)),
-                                                    lut_sh, lut_base, emax);
-                        if (!FULL && static_cast<uint32_t>(k * 8 + h * 4 + j) >= ng)
-                            ent = 0;
-                        const int32_t sym = static_cast<int32_t>(ent) >> 8;
-                        e8[h * 4 + j] = emax_eff - static_cast<uint32_t>(sym);
-                        if ((ent & 0xFF) == static_cast<uint32_t>(kEscLen + 8))
-                            esc_h = min(esc_h, sym);
-                        p += ent & 0xFF;
-                    }
-                    used = p - pos0;
-                }
-            }
-            esc_min = min(esc_min, esc_h);
-            pos = pos0 + used;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (FULL || static_cast<uint32_t>(k * 8 + j) < ng)
-                seen_max = max(seen_max, e8[j]);
-        }
-        if (any_raw) {
-            // a raw group must not have been codable in fewer bits
-            if (raw_mode) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if (FULL || static_cast<uint32_t>(k * 8 + j) < ng)
-                        raw_coded += s_len[(emax - e8[j]) & 0xFF];
-            }
-        }
-        const uint2 r = r0;
-        if (FULL) {
-            r0 = r1;
-            r1 = r2;
-            if (k + 3 < kSteps)
-                r2 = rsrc2[(k + 3) * 64];
-        }
-        const uint32_t i0 = base + k * 512 + lane * 8;
-        if (vec_out) {
-            uint4 o;
-            o.x = (__builtin_amdgcn_perm(r.x, r.x, 0x01010000u) & 0x807F807Fu) | (e8[0] << 7) | (e8[1] << 23);
-            o.y = (__builtin_amdgcn_perm(r.x, r.x, 0x03030202u) & 0x807F807Fu) | (e8[2] << 7) | (e8[3] << 23);
-            o.z = (__builtin_amdgcn_perm(r.y, r.y, 0x01010000u) & 0x807F807Fu) | (e8[4] << 7) | (e8[5] << 23);
-            o.w = (__builtin_amdgcn_perm(r.y, r.y, 0x03030202u) & 0x807F807Fu) | (e8[6] << 7) | (e8[7] << 23);
-            *reinterpret_cast<uint4*>(dst + i0) = o;
-        } else {
-            const uint8_t* rsrc = src + G.R;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (i0 + j < n) {
-                    const uint32_t r = rsrc[i0 + j];
-                    dst[i0 + j] = static_cast<uint16_t>(((r & 0x80u) << 8) | ((e8[j] & 0xFF) << 7) | (r & 0x7Fu));
-                }
-            }
-        }
+    const uint8_t* rsrc = src + G.R;
+    DecState st;
+    st.pos = off;
+    st.seen_max = 0;
+    st.raw_coded = 0;
+    st.esc_min = 255;
+    if (FULL && raw_lanes == ~0ull) {
+        decode_all_raw(gstream, s, s_len, rsrc, dst, n, base, lane, emax, vec_out, st);
+    } else if (tile_words <= static_cast<uint32_t>(kStageWords)) {
+        for (uint32_t w = lane; w < tile_words; w += kLanes)
+            s[w] = gstream[w];
+        if (lane < 4)
+            s[tile_words + lane] = 0;
+        wave_lds_sync();
+        decode_group<FULL>(LdsWindow{s, tile_words}, s_lut, s_len, rsrc, dst, n, base, lane, ng,
+                           emax, raw_mode, raw_lanes != 0, vec_out, st);
+    } else {
+        decode_group<FULL>(GlobalWindow{gstream, tile_words}, s_lut, s_len, rsrc, dst, n, base,
+                           lane, ng, emax, raw_mode, raw_lanes != 0, vec_out, st);
     }
     if (err == 0 && ng > 0) {
-        if (pos != off + glen)
+        if (st.pos != off + glen)
             err = ZC_REASON_LENGTH;
-        else if (seen_max != emax)
+        else if (st.seen_max != emax)
             err = ZC_REASON_EMAX;
-        else if (!raw_mode && esc_min < kEsc)
+        else if (!raw_mode && st.esc_min < kEsc)
             err = ZC_REASON_ESCAPE;
-        else if (raw_mode && raw_coded < 8 * ng)
+        else if (raw_mode && st.raw_coded < 8 * ng)
             err = ZC_REASON_RAWMODE;
     }
     if (err)
@@ -755,18 +960,17 @@ __device__ void decompress_tile(const uint8_t* __restrict__ src, uint16_t* __res
 // A chunk's last, partial tile, kept out of line (see compress_tile_partial).
 __device__ __attribute__((noinline)) void decompress_tile_partial(
     const uint8_t* __restrict__ src, uint16_t* __restrict__ dst, int32_t* __restrict__ status,
-    int c, uint32_t n, uint32_t t, uint32_t lane, uint32_t* __restrict__ s_stream,
-    const uint16_t* __restrict__ s_lut, const uint8_t* __restrict__ s_len, uint64_t comp)
+    int c, uint32_t n, uint32_t t, uint64_t bavail, uint32_t lane, uint32_t* __restrict__ s,
+    const uint16_t* __restrict__ s_lut, const uint8_t* __restrict__ s_len)
 {
-    const Geom G = geometry(n);
-    decompress_tile<false>(src, dst, status, c, n, t, G, lane, s_stream, s_lut, s_len, comp);
+    decompress_tile<false>(src, dst, status, c, n, t, bavail, lane, s, s_lut, s_len);
 }
 
-__global__ __launch_bounds__(kBlock, 4)
+__global__ __launch_bounds__(kBlock, kMinWavesDec)
 void zc_decompress_kernel(const uint8_t* __restrict__ in, uint16_t* __restrict__ out,
                           int32_t* __restrict__ status, ChunkTable tab)
 {
-    __shared__ __align__(16) uint32_t s_stream[kWaves][kStreamWords];
+    __shared__ __align__(16) uint32_t s_stage[kWaves][kStageAlloc];
     __shared__ uint16_t s_lut[kLutSize];
     __shared__ uint8_t s_len[256];
 
@@ -790,36 +994,24 @@ void zc_decompress_kernel(const uint8_t* __restrict__ in, uint16_t* __restrict__
         return;
     const int c = find_chunk(tab, item);
     const uint32_t n = tab.n[c];
-    const uint32_t t = item - tab.item_begin[c];
-    const uint8_t* src = in + tab.boff[c];
-    uint16_t* dst = out + tab.voff[c];
-    const Geom G = geometry(n);
-
-    // header (the host has checked that 32 bytes are readable)
-    const uint32_t hw = lane < 8 ? reinterpret_cast<const uint32_t*>(src)[lane] : 0u;
-    const uint32_t h0 = __shfl(hw, 0), h1 = __shfl(hw, 1), h2 = __shfl(hw, 2),
-                   h3 = __shfl(hw, 3), h4 = __shfl(hw, 4), h5 = __shfl(hw, 5),
-                   h6 = __shfl(hw, 6), h7 = __shfl(hw, 7);
-    if (h0 != kMagic || h1 != kVerTable || h2 != 0 || h3 != 0 || h4 != n || h5 != 0) {
-        if (lane == 0)
+    if (n == 0) {
+        // a header-only stream
+        const uint8_t* src = in + tab.boff[c];
+        const uint32_t hw = lane < 8 ? reinterpret_cast<const uint32_t*>(src)[lane] : 0u;
+        if (__ballot(lane < 8 && hw != header_word(lane, 0, 32)) && lane == 0)
             report(status, ZC_REASON_HEADER, c);
         return;
     }
-    const uint64_t comp = h6 | (static_cast<uint64_t>(h7) << 32);
-    if (comp < G.X || comp > tab.bavail[c] || comp > chunk_bound(n)) {
-        if (lane == 0)
-            report(status, ZC_REASON_SIZE, c);
-        return;
-    }
-    if (n == 0)
-        return;
+    const uint32_t t = item - tab.item_begin[c];
+    const uint8_t* src = in + tab.boff[c];
+    uint16_t* dst = out + tab.voff[c];
     const uint32_t rem = min(n - t * kTile, static_cast<uint32_t>(kTile));
     if (rem == kTile)
-        decompress_tile<true>(src, dst, status, c, n, t, G, lane, s_stream[wave], s_lut, s_len,
-                              comp);
+        decompress_tile<true>(src, dst, status, c, n, t, tab.bavail[c], lane, s_stage[wave], s_lut,
+                              s_len);
     else
-        decompress_tile_partial(src, dst, status, c, n, t, lane, s_stream[wave], s_lut, s_len,
-                                comp);
+        decompress_tile_partial(src, dst, status, c, n, t, tab.bavail[c], lane, s_stage[wave],
+                                s_lut, s_len);
 }
 
 // ------------------------------------------------------------ host side

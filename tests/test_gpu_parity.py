@@ -252,3 +252,57 @@ def test_corrupt_streams_match_oracle_verdict(oracle):
         assert zc.zc_decompress(d, [n], out, status) == zc.ZC_OK
         torch.cuda.synchronize()
         assert int(status.item()) >> 24 == 2     # SIZE
+
+
+# ----------------------------------------------------- stress layouts ---
+
+def _stress_tiles(kind, tiles, seed):
+    """Crafted tiles that drive the kernels' less common paths."""
+    rng = np.random.default_rng(seed)
+    w = synth.gaussian_bits(tiles * TILE, 0.02, seed=seed)
+    grid = w.reshape(tiles, 16, 64, 8)           # tile, step, lane, value
+    if kind == "raw_heavy":
+        # lanes below `cut` get one huge value, which forces raw mode; the
+        # tile stream then exceeds 4 KiB without every group being raw
+        for t in range(tiles):
+            cut = int(rng.integers(34, 60))
+            grid[t, 0, :cut, 3] = 0x7F00          # e = 254
+    elif kind == "escape_runs":
+        # runs of three zeros inside one half-step (members 4h..4h+2): three
+        # escapes (66 bits) overflow the 64-bit decode window; the group stays
+        # coded (a few escapes are far below 8 bits per value)
+        for t in range(tiles):
+            for lane in range(64):
+                for h in rng.choice(32, size=3, replace=False):
+                    k, j0 = divmod(4 * int(h), 8)
+                    grid[t, k, lane, j0:j0 + 3] = 0
+    elif kind == "long_codes":
+        # values 12-15 binades below the group maximum: long code words
+        for t in range(tiles):
+            for lane in range(64):
+                pos = rng.integers(0, 128, size=6)
+                e = 110 + rng.integers(0, 4, size=6)
+                grid[t, pos // 8, lane, pos % 8] = (e << 7).astype(np.uint16)
+            grid[t, 0, :, 0] = 125 << 7
+    return grid.reshape(-1)
+
+
+@pytest.mark.parametrize("kind", ["raw_heavy", "escape_runs", "long_codes"])
+def test_stress_layouts(oracle, kind):
+    seed = {"raw_heavy": 11, "escape_runs": 12, "long_codes": 13}[kind]
+    w = _stress_tiles(kind, 5, seed=seed)
+    n = w.size
+    # full tiles, then the same data with a ragged tail and an unaligned start
+    check_against_oracle(oracle, w, [n], label=kind)
+    cnt = np.array([3, n - 3 - 1000, 1000], np.int64)
+    check_against_oracle(oracle, w, cnt, label=kind + " ragged")
+
+
+def test_stress_paths_are_taken(oracle):
+    # the crafted layouts really produce the intended stream shapes
+    s = oracle.compress_chunk(_stress_tiles("raw_heavy", 2, seed=1))
+    T, NG, R, X = oracle.geometry(2 * TILE)
+    toffs = s[32:32 + 4 * T].view(np.uint32)
+    assert toffs[1] - toffs[0] > 4096            # tile stream beyond the LDS buffer
+    glen = s[32 + 68 * T:32 + 68 * T + 2 * NG].view(np.uint16)
+    assert 0 < int((glen == 1024).sum()) < NG     # raw and coded groups mixed
