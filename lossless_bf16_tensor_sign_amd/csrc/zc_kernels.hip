@@ -38,6 +38,20 @@
 #include "zc_table.h"
 #include "zc_table_v1.inc"
 
+// Tuning knobs (compile-time; the defaults are the measured best).
+#ifndef ZC_ENC_BATCH
+#define ZC_ENC_BATCH 16          // 16-byte loads in flight per lane (full tiles)
+#endif
+#ifndef ZC_ENC_WAVES
+#define ZC_ENC_WAVES 4           // compress occupancy target, waves per SIMD
+#endif
+#ifndef ZC_ENC_INTERLEAVE
+#define ZC_ENC_INTERLEAVE 1      // equal-size chunks: hand out tiles round-robin
+#endif
+#ifndef ZC_DEC_WAVES
+#define ZC_DEC_WAVES 7           // decompress occupancy target, waves per SIMD
+#endif
+
 namespace {
 
 constexpr int kLanes = 64;
@@ -47,18 +61,17 @@ constexpr int kSteps = 16;
 constexpr int kTile = 8192;
 constexpr int kStageWords = 1024;                 // LDS tile-stream buffer per wave (4 KiB)
 constexpr int kStageAlloc = kStageWords + 8;      // + guard and carry words
-constexpr int kMinWavesEnc = 4;                   // occupancy targets, waves per SIMD
-constexpr int kMinWavesDec = 8;
+constexpr int kMinWavesEnc = ZC_ENC_WAVES;        // occupancy targets, waves per SIMD
+constexpr int kMinWavesDec = ZC_DEC_WAVES;
 constexpr int kMaxChunks = 64;                     // chunks per launch
 constexpr uint32_t kMagic = 0x3142435Au;
 constexpr uint32_t kVerTable = 0x00010001u;        // version 1, table_id 1
 constexpr int kEsc = ZC_T1_NSYM - 1;
 constexpr int kEscLen = ZC_T1_ESC_LEN;
-constexpr int kLutBits = 10;
-constexpr int kTailBits = 4;
-constexpr int kLutTail = 1 << kLutBits;            // LDS index of the second level
-constexpr int kLutRaw = kLutTail + (1 << kTailBits);   // raw-mode byte entries
-constexpr int kLutSize = kLutRaw + 256;
+constexpr int kLutBits = ZC_T1_LUT_BITS;          // first decode level (byte entries)
+constexpr int kTailBits = ZC_T1_TAIL_BITS;        // second level
+constexpr int kLutRaw = 1 << kLutBits;            // raw-mode byte entries follow
+constexpr uint32_t kTicketStride = 32;             // one 128-byte line per chunk counter
 constexpr uint64_t kFlagAgg = 1ull << 62;
 constexpr uint64_t kFlagInc = 2ull << 62;
 
@@ -66,9 +79,9 @@ static_assert(ZC_T1_NSYM == 17, "table_id 1 has 17 symbols");
 static_assert(ZC_T1_TAIL_OK == 1, "long code words must share the all-ones prefix");
 static_assert(ZC_T1_MAXLEN <= kLutBits + kTailBits, "code words must fit two lookup levels");
 static_assert(kEscLen + 8 <= 32, "escape payload must fit the window");
-static_assert(kEscLen + 8 > ZC_T1_MAXLEN, "an escape entry is told apart by its length");
+static_assert(kLutBits == 8, "raw groups index the byte table with 8 stream bits");
 
-__constant__ uint16_t c_lut[1 << kLutBits] = ZC_T1_LUT_INIT;
+__constant__ uint8_t c_lut[1 << kLutBits] = ZC_T1_LUT_INIT;
 __constant__ uint16_t c_tail[1 << kTailBits] = ZC_T1_TAIL_INIT;
 __constant__ uint8_t c_len[ZC_T1_NSYM] = ZC_T1_LEN_INIT;
 __constant__ uint32_t c_code[ZC_T1_NSYM] = ZC_T1_CODE_INIT;
@@ -78,6 +91,7 @@ __constant__ uint32_t c_code[ZC_T1_NSYM] = ZC_T1_CODE_INIT;
 struct ChunkTable {
     int32_t nchunks;
     uint32_t nitems;
+    uint32_t uniform_tiles;        // > 0: every chunk has this many tiles
     uint32_t item_begin[kMaxChunks + 1];
     uint32_t n[kMaxChunks];
     uint64_t voff[kMaxChunks];     // value offset of the chunk (bf16 side)
@@ -225,7 +239,7 @@ __device__ inline uint32_t load_split(const TileCtx& x, uint32_t (&ex)[kSteps][2
     const char* sbase = reinterpret_cast<const char*>(x.src + x.base);
     char* rbase = reinterpret_cast<char*>(x.dst + x.G.R + x.base);
     const uint32_t lo16 = x.lane * 16, lo8 = x.lane * 8;
-    constexpr int kBatch = FULL ? 4 : 2;
+    constexpr int kBatch = FULL ? ZC_ENC_BATCH : 2;
     uint32_t mx = 0;
 #pragma unroll
     for (int h = 0; h < kSteps / kBatch; ++h) {
@@ -562,6 +576,55 @@ __device__ __attribute__((noinline)) void compress_tile_partial(
     compress_tile<false>(x, comp_sizes, status, s, tb);
 }
 
+__device__ inline void compress_item(const ChunkTable& tab, uint32_t item, uint32_t lane,
+                                     uint32_t* __restrict__ tickets,
+                                     const uint16_t* __restrict__ in, uint8_t* __restrict__ out,
+                                     int64_t* __restrict__ comp_sizes,
+                                     uint64_t* __restrict__ status, uint32_t* __restrict__ s,
+                                     const EncTables& tb)
+{
+    // The wave's chunk comes from its position in the grid: round-robin over
+    // the chunks when they are all the same size, so that few tiles of one
+    // chunk are in flight at once; chunk by chunk otherwise.  Its tile within
+    // the chunk comes from that chunk's own ticket counter, so a tile only
+    // ever waits for lower tickets of its chunk, held by waves that are
+    // already running.  Status words stay in chunk order.
+    TileCtx x;
+    if (ZC_ENC_INTERLEAVE && tab.uniform_tiles)
+        x.c = static_cast<int>(item % static_cast<uint32_t>(tab.nchunks));
+    else
+        x.c = find_chunk(tab, item);
+    {
+        uint32_t tk = 0;
+        if (lane == 0)
+            tk = atomicAdd(&tickets[x.c * kTicketStride], 1u);
+        x.t = __builtin_amdgcn_readfirstlane(tk);
+    }
+    x.n = tab.n[x.c];
+    x.first = tab.item_begin[x.c];
+    x.item = x.first + x.t;
+    x.lane = lane;
+    x.src = in + tab.voff[x.c];
+    x.dst = out + tab.boff[x.c];
+    x.G = geometry(x.n);
+
+    if (x.n == 0) {
+        if (lane < 8)
+            reinterpret_cast<uint32_t*>(x.dst)[lane] = header_word(lane, 0, 32);
+        if (lane == 0)
+            comp_sizes[x.c] = 32;
+        return;
+    }
+    x.base = x.t * kTile;
+    x.rem = min(x.n - x.base, static_cast<uint32_t>(kTile));
+    const bool full = x.rem == kTile && ((reinterpret_cast<uintptr_t>(x.src) & 15) == 0);
+    if (full)
+        compress_tile<true>(x, comp_sizes, status, s, tb);
+    else
+        compress_tile_partial(x.src, x.dst, x.n, x.t, x.item, x.first, lane, x.c, comp_sizes,
+                              status, s, tb);
+}
+
 __global__ __launch_bounds__(kBlock, kMinWavesEnc)
 void zc_compress_kernel(const uint16_t* __restrict__ in, uint8_t* __restrict__ out,
                         int64_t* __restrict__ comp_sizes,
@@ -583,46 +646,20 @@ void zc_compress_kernel(const uint16_t* __restrict__ in, uint8_t* __restrict__ o
     }
     __syncthreads();
 
-    uint32_t item = 0;
-    if (lane == 0)
-        item = atomicAdd(ticket, 1u);
-    item = __builtin_amdgcn_readfirstlane(item);
-    if (item >= tab.nitems)
-        return;
-
-    TileCtx x;
-    x.c = find_chunk(tab, item);
-    x.n = tab.n[x.c];
-    x.t = item - tab.item_begin[x.c];
-    x.first = tab.item_begin[x.c];
-    x.item = item;
-    x.lane = lane;
-    x.src = in + tab.voff[x.c];
-    x.dst = out + tab.boff[x.c];
-    x.G = geometry(x.n);
-
-    if (x.n == 0) {
-        if (lane < 8)
-            reinterpret_cast<uint32_t*>(x.dst)[lane] = header_word(lane, 0, 32);
-        if (lane == 0)
-            comp_sizes[x.c] = 32;
-        return;
-    }
-    x.base = x.t * kTile;
-    x.rem = min(x.n - x.base, static_cast<uint32_t>(kTile));
-    const bool full = x.rem == kTile && ((reinterpret_cast<uintptr_t>(x.src) & 15) == 0);
-    if (full)
-        compress_tile<true>(x, comp_sizes, status, s_stage[wave], tb);
-    else
-        compress_tile_partial(x.src, x.dst, x.n, x.t, x.item, x.first, lane, x.c, comp_sizes,
-                              status, s_stage[wave], tb);
+    const uint32_t item = blockIdx.x * kWaves + wave;
+    if (item < tab.nitems)
+        compress_item(tab, item, lane, ticket, in, out, comp_sizes, status, s_stage[wave], tb);
 }
 
 // ------------------------------------------------------------ decompress
 
+// Records one failed check (the first to arrive wins).  Callers pass a
+// wave-uniform reason; only one lane touches the status word, and not at all
+// once a failure is recorded, so a wholly corrupt buffer cannot flood it.
 __device__ inline void report(int32_t* status, int reason, int c)
 {
-    atomicCAS(status, 0, (reason << 24) | (c & 0xFFFFFF));
+    if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0)
+        atomicCAS(status, 0, (reason << 24) | (c & 0xFFFFFF));
 }
 
 // 64 stream bits from bit `pos` of a tile stream staged in LDS (word index
@@ -659,28 +696,43 @@ struct GlobalWindow {
     }
 };
 
-// Table entry of the symbol at the top of a window: length in bits 0..7,
-// symbol in bits 8.. (signed).  An escape is returned as (d << 8) | 22 with
-// d = E_max - e, so that E_max minus the symbol field is e in every case;
-// its d also lowers esc_min (a valid escape has d >= 16).  Raw groups look
-// their 8 bits up in entries that hold 255 - e.
-__device__ inline uint32_t decode_entry(const uint16_t* __restrict__ s_lut, uint32_t top,
-                                        uint32_t lut_sh, uint32_t lut_base, uint32_t emax,
-                                        bool valid, int32_t& esc_min)
+// Per-lane decoding parameters.  Coded groups look the first 8 stream bits
+// up in (symbol << 4 | length) byte entries; raw groups look their 8 bits up
+// in entries that hold 255 - e and always advance by 8.
+struct LaneCode {
+    uint32_t base;       // LDS byte index of the lane's table
+    uint32_t sym_sh;     // entry >> sym_sh = symbol
+    uint32_t smask;      // (entry & smask) | sor = bits consumed
+    uint32_t sor;
+    uint32_t lmark;      // entry value that means "longer code word"
+    uint32_t emax_eff;   // e = emax_eff - symbol
+};
+
+// Symbol and length of the code word at the top of a window.  Code words
+// longer than the first level take the second: an escape then yields
+// d = E_max - e as its symbol (so that E_max - symbol is e) and lowers
+// esc_min, since a valid escape has d >= 16.
+__device__ inline void decode_sym(const uint8_t* __restrict__ s_lut8,
+                                  const uint16_t* __restrict__ s_tail, uint32_t top,
+                                  const LaneCode& q, uint32_t emax, bool valid,
+                                  int32_t& esc_min, uint32_t& sym, uint32_t& sh)
 {
-    uint32_t ent = s_lut[(top >> lut_sh) + lut_base];
-    if (ent == 0) {
-        // longer than the first lookup level: second level on the next bits
-        ent = s_lut[kLutTail + ((top >> (32 - kLutBits - kTailBits)) & ((1u << kTailBits) - 1))];
-        if ((ent >> 8) == static_cast<uint32_t>(kEsc)) {
+    const uint32_t ent = s_lut8[(top >> (32 - kLutBits)) + q.base];
+    sym = ent >> q.sym_sh;
+    sh = (ent & q.smask) | q.sor;
+    if (ent == q.lmark) {
+        const uint32_t t2 = s_tail[(top >> (32 - kLutBits - kTailBits)) & ((1u << kTailBits) - 1)];
+        sym = t2 >> 8;
+        sh = t2 & 0xFF;
+        if (sym == static_cast<uint32_t>(kEsc)) {
             const uint32_t e = (top >> (32 - kEscLen - 8)) & 0xFF;
             const int32_t d = static_cast<int32_t>(emax) - static_cast<int32_t>(e);
             if (valid)
                 esc_min = min(esc_min, d);
-            ent = (static_cast<uint32_t>(d) << 8) | (kEscLen + 8);
+            sym = static_cast<uint32_t>(d);
+            sh = kEscLen + 8;
         }
     }
-    return ent;
 }
 
 // Joins 8 exponents with their sign+mantissa bytes and stores them.
@@ -715,17 +767,22 @@ struct DecState {
 };
 
 // Decodes the 128 members of this lane's group from a window source and
-// writes the values.  Raw groups take 8-bit entries from the same table.
+// writes the values.
 template <bool FULL, class Win>
-__device__ inline void decode_group(const Win& win, const uint16_t* __restrict__ s_lut,
+__device__ inline void decode_group(const Win& win, const uint8_t* __restrict__ s_lut8,
+                                    const uint16_t* __restrict__ s_tail,
                                     const uint8_t* __restrict__ s_len, const uint8_t* __restrict__ rsrc,
                                     uint16_t* __restrict__ dst, uint32_t n, uint32_t base,
                                     uint32_t lane, uint32_t ng, uint32_t emax, bool raw_mode,
                                     bool any_raw, bool vec_out, DecState& st)
 {
-    const uint32_t emax_eff = raw_mode ? 255u : emax;
-    const uint32_t lut_sh = raw_mode ? 24u : static_cast<uint32_t>(32 - kLutBits);
-    const uint32_t lut_base = raw_mode ? static_cast<uint32_t>(kLutRaw) : 0u;
+    LaneCode q;
+    q.base = raw_mode ? static_cast<uint32_t>(kLutRaw) : 0u;
+    q.sym_sh = raw_mode ? 0u : 4u;
+    q.smask = raw_mode ? 0u : 15u;
+    q.sor = raw_mode ? 8u : 0u;
+    q.lmark = raw_mode ? 256u : 0u;
+    q.emax_eff = raw_mode ? 255u : emax;
 
     // sign+mantissa bytes, prefetched three steps ahead
     const uint2* rsrc2 = reinterpret_cast<const uint2*>(rsrc + base) + lane;
@@ -747,12 +804,13 @@ __device__ inline void decode_group(const Win& win, const uint16_t* __restrict__
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const bool valid = FULL || static_cast<uint32_t>(k * 8 + h * 4 + j) < ng;
-                uint32_t ent = decode_entry(s_lut, hi32(W), lut_sh, lut_base, emax, valid, esc_h);
+                uint32_t sym, sh;
+                decode_sym(s_lut8, s_tail, hi32(W), q, emax, valid, esc_h, sym, sh);
                 if (!FULL && !valid)
-                    ent = 0;
-                e8[h * 4 + j] = emax_eff - static_cast<uint32_t>(static_cast<int32_t>(ent) >> 8);
-                W <<= (ent & 63);
-                used += ent & 0xFF;
+                    sh = 0;
+                e8[h * 4 + j] = q.emax_eff - sym;
+                W <<= sh;
+                used += sh;
             }
             if (__ballot(used > 64)) {
                 // a half-step longer than the window (several escapes): decode
@@ -763,12 +821,12 @@ __device__ inline void decode_group(const Win& win, const uint16_t* __restrict__
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const bool valid = FULL || static_cast<uint32_t>(k * 8 + h * 4 + j) < ng;
-                        uint32_t ent = decode_entry(s_lut, hi32(win(p)), lut_sh, lut_base, emax,
-                                                    valid, esc_h);
+                        uint32_t sym, sh;
+                        decode_sym(s_lut8, s_tail, hi32(win(p)), q, emax, valid, esc_h, sym, sh);
                         if (!FULL && !valid)
-                            ent = 0;
-                        e8[h * 4 + j] = emax_eff - static_cast<uint32_t>(static_cast<int32_t>(ent) >> 8);
-                        p += ent & 0xFF;
+                            sh = 0;
+                        e8[h * 4 + j] = q.emax_eff - sym;
+                        p += sh;
                     }
                     used = p - pos0;
                 }
@@ -846,7 +904,8 @@ template <bool FULL>
 __device__ void decompress_tile(const uint8_t* __restrict__ src, uint16_t* __restrict__ dst,
                                 int32_t* __restrict__ status, int c, uint32_t n, uint32_t t,
                                 uint64_t bavail, uint32_t lane, uint32_t* __restrict__ s,
-                                const uint16_t* __restrict__ s_lut,
+                                const uint8_t* __restrict__ s_lut8,
+                                const uint16_t* __restrict__ s_tail,
                                 const uint8_t* __restrict__ s_len)
 {
     const Geom G = geometry(n);
@@ -937,11 +996,11 @@ __device__ void decompress_tile(const uint8_t* __restrict__ src, uint16_t* __res
         if (lane < 4)
             s[tile_words + lane] = 0;
         wave_lds_sync();
-        decode_group<FULL>(LdsWindow{s, tile_words}, s_lut, s_len, rsrc, dst, n, base, lane, ng,
-                           emax, raw_mode, raw_lanes != 0, vec_out, st);
-    } else {
-        decode_group<FULL>(GlobalWindow{gstream, tile_words}, s_lut, s_len, rsrc, dst, n, base,
+        decode_group<FULL>(LdsWindow{s, tile_words}, s_lut8, s_tail, s_len, rsrc, dst, n, base,
                            lane, ng, emax, raw_mode, raw_lanes != 0, vec_out, st);
+    } else {
+        decode_group<FULL>(GlobalWindow{gstream, tile_words}, s_lut8, s_tail, s_len, rsrc, dst, n,
+                           base, lane, ng, emax, raw_mode, raw_lanes != 0, vec_out, st);
     }
     if (err == 0 && ng > 0) {
         if (st.pos != off + glen)
@@ -953,17 +1012,24 @@ __device__ void decompress_tile(const uint8_t* __restrict__ src, uint16_t* __res
         else if (raw_mode && st.raw_coded < 8 * ng)
             err = ZC_REASON_RAWMODE;
     }
-    if (err)
-        report(status, err, c);
+    // one report per wave: the lowest failing lane's reason
+    const uint64_t bad = __ballot(err != 0);
+    if (bad) {
+        const int first = __ffsll(static_cast<unsigned long long>(bad)) - 1;
+        const int reason = __shfl(err, first);
+        if (lane == 0)
+            report(status, reason, c);
+    }
 }
 
 // A chunk's last, partial tile, kept out of line (see compress_tile_partial).
 __device__ __attribute__((noinline)) void decompress_tile_partial(
     const uint8_t* __restrict__ src, uint16_t* __restrict__ dst, int32_t* __restrict__ status,
     int c, uint32_t n, uint32_t t, uint64_t bavail, uint32_t lane, uint32_t* __restrict__ s,
-    const uint16_t* __restrict__ s_lut, const uint8_t* __restrict__ s_len)
+    const uint8_t* __restrict__ s_lut8, const uint16_t* __restrict__ s_tail,
+    const uint8_t* __restrict__ s_len)
 {
-    decompress_tile<false>(src, dst, status, c, n, t, bavail, lane, s, s_lut, s_len);
+    decompress_tile<false>(src, dst, status, c, n, t, bavail, lane, s, s_lut8, s_tail, s_len);
 }
 
 __global__ __launch_bounds__(kBlock, kMinWavesDec)
@@ -971,18 +1037,18 @@ void zc_decompress_kernel(const uint8_t* __restrict__ in, uint16_t* __restrict__
                           int32_t* __restrict__ status, ChunkTable tab)
 {
     __shared__ __align__(16) uint32_t s_stage[kWaves][kStageAlloc];
-    __shared__ uint16_t s_lut[kLutSize];
+    __shared__ uint8_t s_lut8[kLutRaw + 256];
+    __shared__ uint16_t s_tail[1 << kTailBits];
     __shared__ uint8_t s_len[256];
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & (kLanes - 1);
     const uint32_t wave = tid / kLanes;
-    for (uint32_t i = tid; i < (1u << kLutBits); i += kBlock)
-        s_lut[i] = c_lut[i];
+    s_lut8[tid] = c_lut[tid];
+    // raw groups: 8 bits b decode to 255 - b
+    s_lut8[kLutRaw + tid] = static_cast<uint8_t>(255u - tid);
     if (tid < (1u << kTailBits))
-        s_lut[kLutTail + tid] = c_tail[tid];
-    // raw groups: 8 bits b decode to the entry (255 - b, 8 bits)
-    s_lut[kLutRaw + tid] = static_cast<uint16_t>(((255u - tid) << 8) | 8u);
+        s_tail[tid] = c_tail[tid];
     {
         const uint32_t s = tid < static_cast<uint32_t>(kEsc) ? tid : static_cast<uint32_t>(kEsc);
         s_len[tid] = static_cast<uint8_t>(c_len[s] + (s == static_cast<uint32_t>(kEsc) ? 8 : 0));
@@ -1007,11 +1073,11 @@ void zc_decompress_kernel(const uint8_t* __restrict__ in, uint16_t* __restrict__
     uint16_t* dst = out + tab.voff[c];
     const uint32_t rem = min(n - t * kTile, static_cast<uint32_t>(kTile));
     if (rem == kTile)
-        decompress_tile<true>(src, dst, status, c, n, t, tab.bavail[c], lane, s_stage[wave], s_lut,
-                              s_len);
+        decompress_tile<true>(src, dst, status, c, n, t, tab.bavail[c], lane, s_stage[wave],
+                              s_lut8, s_tail, s_len);
     else
         decompress_tile_partial(src, dst, status, c, n, t, tab.bavail[c], lane, s_stage[wave],
-                                s_lut, s_len);
+                                s_lut8, s_tail, s_len);
 }
 
 // ------------------------------------------------------------ host side
@@ -1040,7 +1106,7 @@ Counts check_counts(const int64_t* counts, int32_t num_chunks)
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
-constexpr size_t kWsHeader = 256;   // ticket counter(s)
+constexpr size_t kWsHeader = kMaxChunks * kTicketStride * 4;   // per-chunk ticket counters
 
 uint32_t blocks_for(uint32_t items) { return (items + kWaves - 1) / kWaves; }
 
@@ -1127,6 +1193,10 @@ int zc_compress(const uint16_t* d_in, const int64_t* counts, int32_t num_chunks,
         tab.nchunks = m;
         tab.nitems = items;
         tab.item_begin[m] = items;
+        tab.uniform_tiles = tab.n[0] ? (items / static_cast<uint32_t>(m)) : 0u;
+        for (int32_t i = 0; i < m && tab.uniform_tiles; ++i)
+            if (tab.item_begin[i + 1] - tab.item_begin[i] != tab.uniform_tiles || tab.n[i] == 0)
+                tab.uniform_tiles = 0;
 
         // the ticket word and the look-back status words start at zero
         const uint32_t words = items + static_cast<uint32_t>(kWsHeader / 8);
@@ -1215,6 +1285,7 @@ int zc_code_table(int32_t table_id, int32_t* lengths, uint32_t* codes, double* p
         static const uint32_t built_code[] = ZC_T1_CODE_INIT;
         static const uint32_t built_lut[] = ZC_T1_LUT_INIT;
         static const uint32_t built_tail[] = ZC_T1_TAIL_INIT;
+        static_assert(sizeof(built_lut) / sizeof(built_lut[0]) == (1 << kLutBits), "lookup size");
         for (int s = 0; ok && s < ZC_T1_NSYM; ++s)
             ok = static_cast<uint32_t>(tab.len[s]) == built_len[s] && tab.code[s] == built_code[s];
         for (int i = 0; ok && i < (1 << kLutBits); ++i)

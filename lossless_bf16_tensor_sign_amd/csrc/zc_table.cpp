@@ -113,17 +113,20 @@ bool build_table(Table* t)
             return false;
     }
     // Decoder lookup on the first kLutBits bits of the stream: symbol and
-    // length of every code word no longer than kLutBits; 0 for prefixes of
-    // longer code words, which take the per-length path.
+    // length of every code word no longer than kLutBits (both must fit a
+    // nibble); 0 for prefixes of longer code words, which take the second
+    // level.
     std::memset(t->lut, 0, sizeof t->lut);
     for (int s = 0; s < kSymbols; ++s) {
         const int L = t->len[s];
         if (L > kLutBits)
             continue;
+        if (s > 15 || L > 15)
+            return false;
         const uint32_t first = t->code[s] << (kLutBits - L);
         const uint32_t count = 1u << (kLutBits - L);
         for (uint32_t i = 0; i < count; ++i)
-            t->lut[first + i] = static_cast<uint16_t>((s << 8) | L);
+            t->lut[first + i] = static_cast<uint8_t>((s << 4) | L);
     }
     // Second level for the long code words (all must share the all-ones
     // prefix of kLutBits bits and fit in kLutBits + kTailBits bits).

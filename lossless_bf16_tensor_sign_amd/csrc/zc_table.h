@@ -9,13 +9,14 @@ constexpr int kEscapeFrom = 16;          // d >= 16 is escaped
 constexpr int kEscape = kEscapeFrom;     // symbol index of ESC
 constexpr int kSymbols = kEscapeFrom + 1;
 constexpr int kMaxCodeLen = 24;          // longest code word the kernels take
-constexpr int kLutBits = 10;             // decoder lookup width
+constexpr int kLutBits = 8;              // decoder first-level lookup width
+constexpr int kTailBits = 6;             // second level (codes up to 14 bits)
 
 struct Table {
     double prob[kSymbols];
     int len[kSymbols];
     uint32_t code[kSymbols];
-    uint16_t lut[1 << kLutBits];         // (symbol << 8) | length, 0 = long
+    uint8_t lut[1 << kLutBits];          // (symbol << 4) | length, 0 = long
     uint32_t limit[kMaxCodeLen + 1];     // canonical decode, per length
     int32_t base[kMaxCodeLen + 1];
     uint8_t sorted_sym[kSymbols];        // symbols by (length, symbol)
@@ -23,10 +24,8 @@ struct Table {
     // start with kLutBits ones and be at most kLutBits + kTailBits long; the
     // kTailBits bits after that prefix then select its entry.
     bool tail_ok;
-    uint16_t tail[1 << 4];
+    uint16_t tail[1 << kTailBits];       // (symbol << 8) | length
 };
-
-constexpr int kTailBits = 4;
 
 // Phase-averaged law of d = E_max - e: w[0..15] = P(d), w[16] = P(d >= 16).
 void exponent_law(double* w);

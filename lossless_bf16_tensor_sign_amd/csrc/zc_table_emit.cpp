@@ -35,6 +35,8 @@ int main()
     row("ZC_T1_CODE_INIT", buf, zc::kSymbols);
     for (int i = 0; i < (1 << zc::kLutBits); ++i)
         buf[i] = t.lut[i];
+    std::printf("#define ZC_T1_LUT_BITS %d\n", zc::kLutBits);
+    std::printf("#define ZC_T1_TAIL_BITS %d\n", zc::kTailBits);
     row("ZC_T1_LUT_INIT", buf, 1 << zc::kLutBits);
     for (int L = 0; L <= zc::kMaxCodeLen; ++L)
         buf[L] = t.limit[L];
