@@ -6,16 +6,26 @@ workload is the FSDP parameter all-gather shard (64 chunks x 4 Mi bf16,
 sigma log-uniform in [0.005, 0.05]); --workload picks another (1..5).
 
 Throughput is GB/s of uncompressed input (2 bytes per value).  Each call is
-timed with HIP events on the stream the library launches on; a 1 GiB write
-evicts the 256 MB Infinity Cache before each call, outside the timed
-intervals.  The oracle (plain C, test infrastructure) is timed on the host
-cores over the same workload for the cpu_baseline field.
+timed with HIP events recorded on the stream the library launches on; a 1 GiB
+write evicts the 256 MB Infinity Cache before each call, outside the timed
+intervals.  After the timed steps a plain device copy of the input (2n bytes
+read, 2n written) is timed the same way: it is the achievable streaming rate
+on this device, and the reference kernel that calibrates the HBM byte
+counters.
 
-Prints one JSON line.
+roofline.traffic is read from the committed counter summary of this workload
+(profiles/zc_kernels_<workload>_traffic.txt) when the kernel sources hash to
+the value recorded there; otherwise it is null.
+
+The oracle (plain C, test infrastructure) is timed on the host cores over the
+same workload for the cpu_baseline field.
+
+Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -28,37 +38,112 @@ if ROOT not in sys.path:
 METRIC = ("compress / decompress GB/s (uncompressed input) on 1 MI355X; "
           "% HBM peak; ratio")
 HBM_PEAK_GBPS = 8000.0
+KERNEL_NAMES = {"compress": "zc_compress_kernel",
+                "decompress": "zc_decompress_kernel"}
+# Every file the kernels are compiled from (and the flags they are built with).
+KERNEL_SOURCES = [
+    "lossless_bf16_tensor_sign_amd/csrc/zc_kernels.hip",
+    "lossless_bf16_tensor_sign_amd/csrc/zc_table.cpp",
+    "lossless_bf16_tensor_sign_amd/csrc/zc_table.h",
+    "lossless_bf16_tensor_sign_amd/csrc/zc_table_emit.cpp",
+    "lossless_bf16_tensor_sign_amd/build.py",
+    "include/zc.h",
+]
 
 
 def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, counts, threads):
-    """The oracle over every chunk, chunks spread over `threads` threads."""
+def kernel_sources_sha256():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            data = f.read()
+        h.update(rel.encode() + b"\0" + str(len(data)).encode() + b"\0" + data)
+    return h.hexdigest()
+
+
+def traffic_path(workload_name):
+    return os.path.join(ROOT, "profiles", "zc_kernels_%s_traffic.txt" % workload_name)
+
+
+def read_traffic(workload_name):
+    """Per-dispatch HBM bytes by kernel from the committed counter summary,
+    or None when it is absent or was taken from other kernel sources."""
+    path = traffic_path(workload_name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for ln in f:
+            ln = ln.strip()
+            if not ln or ln.startswith("#") or "=" not in ln:
+                continue
+            k, v = ln.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    out = {}
+    for name in KERNEL_NAMES.values():
+        key = name + ".traffic_bytes"
+        if key in kv:
+            out[name] = int(float(kv[key]))
+    return out
+
+
+def cpu_baseline(w, counts, threads, budget_s):
+    """The oracle on the host: one thread over the first chunk (per-core
+    rate), then the first k chunks spread over `threads` threads, k chosen so
+    that about budget_s seconds of CPU time are spent (the whole workload if
+    it fits).  Each chunk is compressed, decompressed and checked."""
     import numpy as np
     from concurrent.futures import ThreadPoolExecutor
     from oracle import oracle
     oracle.build(force=False)
     vo = np.concatenate([[0], np.cumsum(counts)])
+    order = [c for c in range(len(counts)) if counts[c] > 0]
 
-    def comp(c):
-        return oracle.compress_chunk(w[vo[c]:vo[c + 1]])
+    def run(c):
+        x = w[vo[c]:vo[c + 1]]
+        t0 = time.perf_counter()
+        s = oracle.compress_chunk(x)
+        t1 = time.perf_counter()
+        r, back = oracle.decompress_chunk(s, x.size)
+        t2 = time.perf_counter()
+        return t1 - t0, t2 - t1, s.size, r == 0 and np.array_equal(back, x)
 
+    tc1, td1, _, ok1 = run(order[0])
+    one = 2.0 * counts[order[0]]
+    per_chunk = (tc1 + td1) * float(np.mean(counts[order])) / counts[order[0]]
+    k = int(budget_s / max(per_chunk, 1e-9))
+    k = min(len(order), max(threads, (k // threads) * threads))
+    sample = order[:k]
     t0 = time.perf_counter()
     with ThreadPoolExecutor(threads) as ex:
-        streams = list(ex.map(comp, range(len(counts))))
-    t1 = time.perf_counter()
-
-    def dec(c):
-        r, back = oracle.decompress_chunk(streams[c], int(counts[c]))
-        return r == 0 and np.array_equal(back, w[vo[c]:vo[c + 1]])
-
-    with ThreadPoolExecutor(threads) as ex:
-        ok = all(ex.map(dec, range(len(counts))))
-    t2 = time.perf_counter()
-    comp_bytes = sum(s.size for s in streams)
-    return t1 - t0, t2 - t1, comp_bytes, ok
+        res = list(ex.map(run, sample))
+    wall = time.perf_counter() - t0
+    nbytes = 2.0 * float(sum(counts[c] for c in sample))
+    tc = sum(r[0] for r in res)
+    td = sum(r[1] for r in res)
+    ok = ok1 and all(r[3] for r in res)
+    return {
+        "value": round(nbytes / wall / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d of %d chunks (%.1f MB of input), each compressed then "
+                  "decompressed and checked, spread over %d threads; value = "
+                  "input bytes / wall time of both directions"
+                  % (len(sample), len(order), nbytes / 1e6, threads),
+        "compress_GBps_per_core": round(one / tc1 / 1e9, 4),
+        "decompress_GBps_per_core": round(one / td1 / 1e9, 4),
+        "thread_seconds_compress": round(tc, 3),
+        "thread_seconds_decompress": round(td, 3),
+        "wall_s": round(wall, 3),
+        "comp_bytes_sample": int(sum(r[2] for r in res)),
+        "roundtrip_ok": bool(ok),
+    }
 
 
 def main():
@@ -69,12 +154,16 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0,
+                    help="CPU seconds (summed over threads) of the oracle run")
+    ap.add_argument("--copies", type=int, default=3,
+                    help="timed plain device copies of the input after the steps")
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU "
-              "path (the codec is per-GPU; collectives are out of scope), so "
-              "--gpus %d is not supported." % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU only: this codec runs per GPU and no "
+              "multi-GPU path is built, so --gpus %d is not supported."
+              % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -83,7 +172,7 @@ def main():
 
     dev = torch.device("cuda:0")
     seed = synth.default_seed(args.workload)
-    log("generating workload %d" % args.workload)
+    log("generating workload %d (%s)" % (args.workload, synth.NAMES[args.workload]))
     w, counts = synth.make(args.workload, seed=seed, workers=8)
     n = int(counts.sum())
     in_bytes = 2 * n
@@ -97,12 +186,12 @@ def main():
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
     def step(times=None, i=0):
         flush.fill_(i & 0xFF)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e2 = torch.cuda.Event(enable_timing=True)
-        e3 = torch.cuda.Event(enable_timing=True)
+        e0, e1, e2, e3 = ev(), ev(), ev(), ev()
         e0.record(stream)
         r = zc.zc_compress(x, counts, buf, sizes, ws, stream=stream)
         e1.record(stream)
@@ -138,6 +227,20 @@ def main():
     if not ok:
         log("ROUND TRIP FAILED (status %#x)" % st)
         sys.exit(1)
+    log("steps done: round trip exact")
+
+    # plain device copy of the same bytes: streaming ceiling and the
+    # calibration kernel of the byte counters
+    tcopy = []
+    for i in range(args.copies):
+        flush.fill_((i + 7) & 0xFF)
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        y.copy_(x)
+        e1.record(stream)
+        tcopy.append((e0, e1))
+    torch.cuda.synchronize()
+    copy_s = float(np.mean([a.elapsed_time(b) for a, b in tcopy])) * 1e-3 if tcopy else None
 
     ratio = in_bytes / comp
     c_mean, d_mean = float(tc.mean()), float(td.mean())
@@ -145,10 +248,13 @@ def main():
     dec_gbps = in_bytes / d_mean / 1e9
     step_s = c_mean + d_mean
     value = in_bytes / step_s / 1e9
-    alg_c = (in_bytes + comp) / c_mean / 1e9      # algorithmic bytes / time
-    alg_d = (comp + in_bytes) / d_mean / 1e9
+    alg_bytes = in_bytes + comp              # read 2n + write C, or read C + write 2n
+    alg_c = alg_bytes / c_mean / 1e9
+    alg_d = alg_bytes / d_mean / 1e9
     dom = "decompress" if d_mean >= c_mean else "compress"
     achieved = alg_d if dom == "decompress" else alg_c
+    traffic = read_traffic(synth.NAMES[args.workload])
+    dom_traffic = traffic.get(KERNEL_NAMES[dom]) if traffic else None
 
     line = {
         "metric": METRIC,
@@ -169,14 +275,15 @@ def main():
             "chunks": int(len(counts)),
             "bytes_in": in_bytes,
             "seed": seed,
-            "step": "zc_compress + zc_decompress, MALL flushed before each",
+            "step": "zc_compress + zc_decompress of every chunk, "
+                    "1 GiB cache flush before each call (untimed)",
         },
         "compress_GBps": round(comp_gbps, 2),
         "decompress_GBps": round(dec_gbps, 2),
         "compress_ms": round(c_mean * 1e3, 4),
         "decompress_ms": round(d_mean * 1e3, 4),
-        "compress_ms_min": round(float(tc.min()) * 1e3, 4),
-        "decompress_ms_min": round(float(td.min()) * 1e3, 4),
+        "compress_ms_median": round(float(np.median(tc)) * 1e3, 4),
+        "decompress_ms_median": round(float(np.median(td)) * 1e3, 4),
         "ratio": round(ratio, 5),
         "saving": round(1.0 - comp / in_bytes, 5),
         "comp_bytes": comp,
@@ -184,34 +291,31 @@ def main():
             "compress": round(100 * alg_c / HBM_PEAK_GBPS, 2),
             "decompress": round(100 * alg_d / HBM_PEAK_GBPS, 2),
         },
+        "device_copy": None if copy_s is None else {
+            "bytes_moved": 2 * in_bytes,
+            "ms": round(copy_s * 1e3, 4),
+            "GBps_moved": round(2 * in_bytes / copy_s / 1e9, 2),
+            "frac_of_peak": round(2 * in_bytes / copy_s / 1e9 / HBM_PEAK_GBPS, 4),
+        },
         "roofline": {
-            "kernel": dom,
+            "kernel": KERNEL_NAMES[dom],
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": dom_traffic,
+            "algorithmic_bytes": alg_bytes,
+            "traffic_by_kernel": traffic,
         },
         "wall_s_timed_region": round(t_wall, 4),
+        "kernel_sources_sha256": kernel_sources_sha256(),
     }
 
     if not args.no_cpu_baseline:
-        threads = max(1, min(args.cpu_threads, os.cpu_count() or 1))
+        threads = max(1, min(args.cpu_threads, os.cpu_count() or 1, len(counts)))
         log("cpu baseline: oracle, %d threads" % threads)
-        t_c, t_d, cb, cok = cpu_baseline(w, counts, threads)
-        line["cpu_baseline"] = {
-            "value": round(in_bytes / (t_c + t_d) / 1e9, 4),
-            "unit": "GB/s",
-            "cores": threads,
-            "kind": "oracle",
-            "sample": "whole workload (%d chunks), compress then decompress, "
-                      "chunks spread over %d threads" % (len(counts), threads),
-            "compress_GBps": round(in_bytes / t_c / 1e9, 4),
-            "decompress_GBps": round(in_bytes / t_d / 1e9, 4),
-            "comp_bytes_equal_gpu": cb == comp,
-            "roundtrip_ok": bool(cok),
-        }
+        line["cpu_baseline"] = cpu_baseline(w, counts, threads, args.cpu_budget_s)
     print(json.dumps(line), flush=True)
 
 
