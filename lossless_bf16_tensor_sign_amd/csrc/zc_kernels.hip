@@ -193,6 +193,34 @@ __device__ inline int find_chunk(const ChunkTable& tab, uint32_t item)
 __device__ inline uint32_t hi32(uint64_t x) { return static_cast<uint32_t>(x >> 32); }
 __device__ inline uint32_t lo32(uint64_t x) { return static_cast<uint32_t>(x); }
 
+// Streaming accesses: every input byte is read once and every output byte
+// written once, so they are marked nontemporal (no reuse expected in the
+// caches).  On gfx950 this nearly doubles the rate of plain 16-byte loads
+// over a large buffer.
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+
+__device__ inline uint4 ld_nt4(const void* p)
+{
+    const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ inline uint2 ld_nt2(const void* p)
+{
+    const v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
+    return make_uint2(v.x, v.y);
+}
+__device__ inline uint32_t ld_nt1(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+__device__ inline void st_nt4(void* p, uint4 v)
+{
+    __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(p));
+}
+__device__ inline void st_nt2(void* p, uint2 v)
+{
+    __builtin_nontemporal_store(v2u{v.x, v.y}, reinterpret_cast<v2u*>(p));
+}
+__device__ inline void st_nt1(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+
 // ------------------------------------------------------------ compress
 
 __global__ void zc_clear_kernel(uint64_t* __restrict__ p, uint32_t words)
@@ -248,7 +276,7 @@ __device__ inline uint32_t load_split(const TileCtx& x, uint32_t (&ex)[kSteps][2
         for (int kk = 0; kk < kBatch; ++kk) {
             const int k = h * kBatch + kk;
             if (FULL) {
-                v[kk] = *reinterpret_cast<const uint4*>(sbase + lo16 + k * 1024);
+                v[kk] = ld_nt4(sbase + lo16 + k * 1024);
             } else {
                 const uint32_t i0 = x.base + k * 512 + x.lane * 8;
                 uint32_t w[8];
@@ -278,7 +306,7 @@ __device__ inline uint32_t load_split(const TileCtx& x, uint32_t (&ex)[kSteps][2
             mx = max(mx, max(max(q.z & 0x7F80u, (q.z >> 16) & 0x7F80u),
                              max(q.w & 0x7F80u, (q.w >> 16) & 0x7F80u)));
             if (FULL) {
-                *reinterpret_cast<uint2*>(rbase + lo8 + k * 512) = make_uint2(raw_a, raw_b);
+                st_nt2(rbase + lo8 + k * 512, make_uint2(raw_a, raw_b));
             } else {
                 const uint32_t i0 = x.base + k * 512 + x.lane * 8;
                 uint8_t* rdst = x.dst + x.G.R + i0;
@@ -439,7 +467,7 @@ __device__ inline void store_words(uint32_t* __restrict__ g, const uint32_t* __r
                                    uint32_t count, uint32_t lane)
 {
     for (uint32_t w = lane; w < count; w += kLanes)
-        g[w] = s[w];
+        st_nt1(g + w, s[w]);
 }
 
 template <bool FULL>
@@ -747,7 +775,7 @@ __device__ inline void put_values(uint16_t* __restrict__ dst, const uint8_t* __r
         o.y = (__builtin_amdgcn_perm(r.x, r.x, 0x03030202u) & 0x807F807Fu) | (e8[2] << 7) | (e8[3] << 23);
         o.z = (__builtin_amdgcn_perm(r.y, r.y, 0x01010000u) & 0x807F807Fu) | (e8[4] << 7) | (e8[5] << 23);
         o.w = (__builtin_amdgcn_perm(r.y, r.y, 0x03030202u) & 0x807F807Fu) | (e8[6] << 7) | (e8[7] << 23);
-        *reinterpret_cast<uint4*>(dst + i0) = o;
+        st_nt4(dst + i0, o);
     } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -788,9 +816,9 @@ __device__ inline void decode_group(const Win& win, const uint8_t* __restrict__ 
     const uint2* rsrc2 = reinterpret_cast<const uint2*>(rsrc + base) + lane;
     uint2 r0 = make_uint2(0, 0), r1 = r0, r2 = r0;
     if (FULL) {
-        r0 = rsrc2[0];
-        r1 = rsrc2[64];
-        r2 = rsrc2[128];
+        r0 = ld_nt2(rsrc2);
+        r1 = ld_nt2(rsrc2 + 64);
+        r2 = ld_nt2(rsrc2 + 128);
     }
 #pragma unroll 1
     for (int k = 0; k < kSteps; ++k) {
@@ -853,7 +881,7 @@ __device__ inline void decode_group(const Win& win, const uint8_t* __restrict__ 
             r0 = r1;
             r1 = r2;
             if (k + 3 < kSteps)
-                r2 = rsrc2[(k + 3) * 64];
+                r2 = ld_nt2(rsrc2 + (k + 3) * 64);
         }
         put_values<FULL>(dst, rsrc, n, base + k * 512 + lane * 8, r, e8, vec_out);
     }
@@ -873,7 +901,7 @@ __device__ inline void decode_all_raw(const uint32_t* __restrict__ gstream,
     for (int h = 0; h < 2; ++h) {
         wave_lds_sync();
         for (uint32_t w = lane; w < static_cast<uint32_t>(kStageWords); w += kLanes)
-            s[w] = gstream[h * kStageWords + w];
+            s[w] = ld_nt1(gstream + h * kStageWords + w);
         wave_lds_sync();
         if ((lane >> 5) == static_cast<uint32_t>(h)) {
             const uint32_t* mine = s + (lane & 31) * 32;
@@ -893,7 +921,7 @@ __device__ inline void decode_all_raw(const uint32_t* __restrict__ gstream,
                     st.seen_max = max(st.seen_max, e8[j]);
                     st.raw_coded += s_len[(emax - e8[j]) & 0xFF];
                 }
-                put_values<true>(dst, rsrc, n, base + k * 512 + lane * 8, rsrc2[k * 64], e8, vec_out);
+                put_values<true>(dst, rsrc, n, base + k * 512 + lane * 8, ld_nt2(rsrc2 + k * 64), e8, vec_out);
             }
             st.pos += 1024;
         }
@@ -992,7 +1020,7 @@ __device__ void decompress_tile(const uint8_t* __restrict__ src, uint16_t* __res
         decode_all_raw(gstream, s, s_len, rsrc, dst, n, base, lane, emax, vec_out, st);
     } else if (tile_words <= static_cast<uint32_t>(kStageWords)) {
         for (uint32_t w = lane; w < tile_words; w += kLanes)
-            s[w] = gstream[w];
+            s[w] = ld_nt1(gstream + w);
         if (lane < 4)
             s[tile_words + lane] = 0;
         wave_lds_sync();
