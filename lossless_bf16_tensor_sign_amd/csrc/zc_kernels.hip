@@ -48,6 +48,9 @@
 #ifndef ZC_ENC_INTERLEAVE
 #define ZC_ENC_INTERLEAVE 1      // equal-size chunks: hand out tiles round-robin
 #endif
+#ifndef ZC_STATUS_STRIDE
+#define ZC_STATUS_STRIDE 8       // 8-byte look-back status words, one per this many
+#endif
 #ifndef ZC_DEC_WAVES
 #define ZC_DEC_WAVES 7           // decompress occupancy target, waves per SIMD
 #endif
@@ -72,6 +75,10 @@ constexpr int kLutBits = ZC_T1_LUT_BITS;          // first decode level (byte en
 constexpr int kTailBits = ZC_T1_TAIL_BITS;        // second level
 constexpr int kLutRaw = 1 << kLutBits;            // raw-mode byte entries follow
 constexpr uint32_t kTicketStride = 32;             // one 128-byte line per chunk counter
+// Look-back status words sit one per 128-byte line: a tile's status is
+// written through to device-coherent memory, and tiles sharing a line would
+// serialize those writes.
+constexpr uint32_t kStatusStride = ZC_STATUS_STRIDE;
 constexpr uint64_t kFlagAgg = 1ull << 62;
 constexpr uint64_t kFlagInc = 2ull << 62;
 
@@ -223,11 +230,17 @@ __device__ inline void st_nt1(uint32_t* p, uint32_t v) { __builtin_nontemporal_s
 
 // ------------------------------------------------------------ compress
 
-__global__ void zc_clear_kernel(uint64_t* __restrict__ p, uint32_t words)
+// Zeroes the ticket counters and the first word of each status slot.
+__global__ void zc_clear_kernel(uint32_t* __restrict__ tickets, uint32_t ticket_words,
+                                uint64_t* __restrict__ status, uint32_t items)
 {
-    for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < words;
-         i += gridDim.x * blockDim.x)
-        p[i] = 0;
+    for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < ticket_words + items;
+         i += gridDim.x * blockDim.x) {
+        if (i < ticket_words)
+            tickets[i] = 0;
+        else
+            status[static_cast<size_t>(i - ticket_words) * kStatusStride] = 0;
+    }
 }
 
 // Encoder entry for d = 0..255 used when escapes occur: code bits 0..21 (an
@@ -328,7 +341,7 @@ __device__ inline void look_back_publish(uint64_t* __restrict__ status, uint32_t
                                          uint32_t tile_bytes, uint32_t lane)
 {
     if (lane == 0)
-        __hip_atomic_store(&status[item], (t == 0 ? kFlagInc : kFlagAgg) | tile_bytes,
+        __hip_atomic_store(&status[item * kStatusStride], (t == 0 ? kFlagInc : kFlagAgg) | tile_bytes,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -345,7 +358,7 @@ __device__ inline uint32_t look_back_resolve(uint64_t* __restrict__ status, uint
         const bool in_range = idx >= static_cast<int64_t>(first);
         uint64_t s = 0;
         if (in_range)
-            s = __hip_atomic_load(&status[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s = __hip_atomic_load(&status[idx * kStatusStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const uint32_t flag = static_cast<uint32_t>(s >> 62);
         const uint64_t inc_mask = __ballot(in_range && flag == 2);
         const uint64_t zero_mask = __ballot(in_range && flag == 0);
@@ -367,7 +380,7 @@ __device__ inline uint32_t look_back_resolve(uint64_t* __restrict__ status, uint
         top -= kLanes;
     }
     if (lane == 0)
-        __hip_atomic_store(&status[item], kFlagInc | (acc + tile_bytes), __ATOMIC_RELAXED,
+        __hip_atomic_store(&status[item * kStatusStride], kFlagInc | (acc + tile_bytes), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     return acc;
 }
@@ -1174,7 +1187,7 @@ size_t zc_workspace_bytes(const int64_t* counts, int32_t num_chunks)
         }
         most = items > most ? items : most;
     }
-    return static_cast<size_t>(kWsHeader + 8 * most);
+    return static_cast<size_t>(kWsHeader + 8ull * kStatusStride * most);
 }
 
 int zc_compress(const uint16_t* d_in, const int64_t* counts, int32_t num_chunks,
@@ -1227,10 +1240,11 @@ int zc_compress(const uint16_t* d_in, const int64_t* counts, int32_t num_chunks,
                 tab.uniform_tiles = 0;
 
         // the ticket word and the look-back status words start at zero
-        const uint32_t words = items + static_cast<uint32_t>(kWsHeader / 8);
+        const uint32_t twords = static_cast<uint32_t>(kWsHeader / 4);
+        const uint32_t words = items + twords;
         const uint32_t cblocks = (words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024;
-        hipLaunchKernelGGL(zc_clear_kernel, dim3(cblocks), dim3(256), 0, s,
-                           static_cast<uint64_t*>(d_ws), words);
+        hipLaunchKernelGGL(zc_clear_kernel, dim3(cblocks), dim3(256), 0, s, ticket, twords,
+                           status, items);
         hipLaunchKernelGGL(zc_compress_kernel, dim3(blocks_for(items)), dim3(kBlock), 0, s, d_in,
                            out, d_comp_sizes + c0, status, ticket, tab);
         if (hipGetLastError() != hipSuccess)

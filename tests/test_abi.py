@@ -48,13 +48,17 @@ def test_bounds_match_oracle(oracle):
 
 
 def test_workspace_bytes():
-    # a fixed header (per-chunk ticket counters), then 8 bytes per tile of
-    # the largest launch (at most 64 chunks per launch)
-    head = zc.zc_workspace_bytes([0]) - 8
+    # a fixed header (per-chunk ticket counters), then one status slot per
+    # tile of the largest launch (at most 64 chunks per launch)
+    one = zc.zc_workspace_bytes([0])          # header + 1 slot
+    three = zc.zc_workspace_bytes([8193, 1])  # header + 3 slots
+    slot = (three - one) // 2
+    assert three - one == 2 * slot and slot >= 8 and slot % 8 == 0
+    head = one - slot
     assert head >= 64 * 4
-    assert zc.zc_workspace_bytes([8193, 1]) == head + 8 * 3
     cnt = [8192] * 64 + [3 * 8192]
-    assert zc.zc_workspace_bytes(cnt) == head + 8 * 64
+    assert zc.zc_workspace_bytes(cnt) == head + slot * 64
+    assert zc.zc_workspace_bytes([8192 * 5] * 2) == head + slot * 10
 
 
 def test_code_table_matches_oracle(oracle):
