@@ -39,17 +39,23 @@
 #include "zc_table_v1.inc"
 
 // Tuning knobs (compile-time; the defaults are the measured best).
-#ifndef ZC_ENC_BATCH
-#define ZC_ENC_BATCH 16          // 16-byte loads in flight per lane (full tiles)
-#endif
 #ifndef ZC_ENC_WAVES
-#define ZC_ENC_WAVES 4           // compress occupancy target, waves per SIMD
+#define ZC_ENC_WAVES 8           // compress occupancy target, waves per SIMD
 #endif
 #ifndef ZC_ENC_INTERLEAVE
 #define ZC_ENC_INTERLEAVE 1      // equal-size chunks: hand out tiles round-robin
 #endif
 #ifndef ZC_STATUS_STRIDE
 #define ZC_STATUS_STRIDE 8       // 8-byte look-back status words, one per this many
+#endif
+#ifndef ZC_EARLY_POLL
+#define ZC_EARLY_POLL 0          // first look-back poll issued before emission
+#endif
+#ifndef ZC_STORE_X4
+#define ZC_STORE_X4 0            // tile streams stored with 16-byte stores
+#endif
+#ifndef ZC_MIXED_PAIR
+#define ZC_MIXED_PAIR 1          // waves with raw groups may also emit pairs
 #endif
 #ifndef ZC_DEC_WAVES
 #define ZC_DEC_WAVES 7           // decompress occupancy target, waves per SIMD
@@ -263,71 +269,84 @@ struct EncTables {
     uint8_t len[256];     // coded length of d, escape payload included
 };
 
+// A tile is compressed by one workgroup of four waves.  Lane l of every wave
+// works on group l; wave w takes steps 4w..4w+3 of it, which are members
+// 32w..32w+31 in the group's order.  The four partial maxima and partial code
+// lengths of a group meet in LDS, so each thread knows where its quarter of
+// the group's stream starts; the four waves then write their code words into
+// one LDS copy of the tile stream, and wave 0 places it in the chunk.
+constexpr int kQSteps = kSteps / kWaves;           // steps per wave
+constexpr int kQMembers = kQSteps * 8;             // members per wave and group
+constexpr int kTileWordsMax = kTile / 4;           // an all-raw tile stream
+constexpr int kEncStage = kTileWordsMax + 8;       // + guard words
+
+struct EncShared {
+    uint32_t stage[kEncStage];
+    uint32_t part_max[kWaves][kLanes];
+    uint32_t part_bits[kWaves][kLanes];
+    EncTables tb;
+    uint32_t tile;
+};
+
 struct TileCtx {
     const uint16_t* src;
     uint8_t* dst;
     Geom G;
-    uint32_t n, t, base, rem, item, first, lane;
+    uint32_t n, t, base, rem, item, first, lane, wave;
     int c;
 };
 
-// Phase 1 of a tile: loads, raw bytes out, exponents packed 4 per word,
-// group maximum.  FULL = 8192 values at a 16-byte aligned address.
+// Loads and splits this wave's four steps of the tile: raw bytes are stored
+// at once, exponents stay packed 4 per word, the maximum is returned.
+// FULL = 8192 values at a 16-byte aligned address.
 template <bool FULL>
-__device__ inline uint32_t load_split(const TileCtx& x, uint32_t (&ex)[kSteps][2])
+__device__ inline uint32_t load_split(const TileCtx& x, uint32_t (&ex)[kQSteps][2])
 {
-    // wave-uniform bases, 32-bit lane offsets
-    const char* sbase = reinterpret_cast<const char*>(x.src + x.base);
-    char* rbase = reinterpret_cast<char*>(x.dst + x.G.R + x.base);
-    const uint32_t lo16 = x.lane * 16, lo8 = x.lane * 8;
-    constexpr int kBatch = FULL ? ZC_ENC_BATCH : 2;
+    const uint32_t k0 = x.wave * kQSteps;
+    const char* sbase = reinterpret_cast<const char*>(x.src + x.base) + k0 * 1024 + x.lane * 16;
+    char* rbase = reinterpret_cast<char*>(x.dst + x.G.R + x.base) + k0 * 512 + x.lane * 8;
+    uint4 v[kQSteps];
+#pragma unroll
+    for (int k = 0; k < kQSteps; ++k) {
+        if (FULL) {
+            v[k] = ld_nt4(sbase + k * 1024);
+        } else {
+            const uint32_t i0 = x.base + (k0 + k) * 512 + x.lane * 8;
+            uint32_t w[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                w[j] = (i0 + j < x.n) ? x.src[i0 + j] : 0u;
+            v[k].x = w[0] | (w[1] << 16);
+            v[k].y = w[2] | (w[3] << 16);
+            v[k].z = w[4] | (w[5] << 16);
+            v[k].w = w[6] | (w[7] << 16);
+        }
+    }
     uint32_t mx = 0;
 #pragma unroll
-    for (int h = 0; h < kSteps / kBatch; ++h) {
-        uint4 v[kBatch];
+    for (int k = 0; k < kQSteps; ++k) {
+        const uint4 q = v[k];
+        const uint32_t lo_a = __builtin_amdgcn_perm(q.y, q.x, 0x06040200u);
+        const uint32_t hi_a = __builtin_amdgcn_perm(q.y, q.x, 0x07050301u);
+        const uint32_t lo_b = __builtin_amdgcn_perm(q.w, q.z, 0x06040200u);
+        const uint32_t hi_b = __builtin_amdgcn_perm(q.w, q.z, 0x07050301u);
+        const uint32_t raw_a = (hi_a & 0x80808080u) | (lo_a & 0x7F7F7F7Fu);
+        const uint32_t raw_b = (hi_b & 0x80808080u) | (lo_b & 0x7F7F7F7Fu);
+        ex[k][0] = ((hi_a << 1) & 0xFEFEFEFEu) | ((lo_a >> 7) & 0x01010101u);
+        ex[k][1] = ((hi_b << 1) & 0xFEFEFEFEu) | ((lo_b >> 7) & 0x01010101u);
+        mx = max(mx, max(max(q.x & 0x7F80u, (q.x >> 16) & 0x7F80u),
+                         max(q.y & 0x7F80u, (q.y >> 16) & 0x7F80u)));
+        mx = max(mx, max(max(q.z & 0x7F80u, (q.z >> 16) & 0x7F80u),
+                         max(q.w & 0x7F80u, (q.w >> 16) & 0x7F80u)));
+        if (FULL) {
+            st_nt2(rbase + k * 512, make_uint2(raw_a, raw_b));
+        } else {
+            const uint32_t i0 = x.base + (k0 + k) * 512 + x.lane * 8;
+            uint8_t* rdst = x.dst + x.G.R + i0;
 #pragma unroll
-        for (int kk = 0; kk < kBatch; ++kk) {
-            const int k = h * kBatch + kk;
-            if (FULL) {
-                v[kk] = ld_nt4(sbase + lo16 + k * 1024);
-            } else {
-                const uint32_t i0 = x.base + k * 512 + x.lane * 8;
-                uint32_t w[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    w[j] = (i0 + j < x.n) ? x.src[i0 + j] : 0u;
-                v[kk].x = w[0] | (w[1] << 16);
-                v[kk].y = w[2] | (w[3] << 16);
-                v[kk].z = w[4] | (w[5] << 16);
-                v[kk].w = w[6] | (w[7] << 16);
-            }
-        }
-#pragma unroll
-        for (int kk = 0; kk < kBatch; ++kk) {
-            const int k = h * kBatch + kk;
-            const uint4 q = v[kk];
-            const uint32_t lo_a = __builtin_amdgcn_perm(q.y, q.x, 0x06040200u);
-            const uint32_t hi_a = __builtin_amdgcn_perm(q.y, q.x, 0x07050301u);
-            const uint32_t lo_b = __builtin_amdgcn_perm(q.w, q.z, 0x06040200u);
-            const uint32_t hi_b = __builtin_amdgcn_perm(q.w, q.z, 0x07050301u);
-            const uint32_t raw_a = (hi_a & 0x80808080u) | (lo_a & 0x7F7F7F7Fu);
-            const uint32_t raw_b = (hi_b & 0x80808080u) | (lo_b & 0x7F7F7F7Fu);
-            ex[k][0] = ((hi_a << 1) & 0xFEFEFEFEu) | ((lo_a >> 7) & 0x01010101u);
-            ex[k][1] = ((hi_b << 1) & 0xFEFEFEFEu) | ((lo_b >> 7) & 0x01010101u);
-            mx = max(mx, max(max(q.x & 0x7F80u, (q.x >> 16) & 0x7F80u),
-                             max(q.y & 0x7F80u, (q.y >> 16) & 0x7F80u)));
-            mx = max(mx, max(max(q.z & 0x7F80u, (q.z >> 16) & 0x7F80u),
-                             max(q.w & 0x7F80u, (q.w >> 16) & 0x7F80u)));
-            if (FULL) {
-                st_nt2(rbase + lo8 + k * 512, make_uint2(raw_a, raw_b));
-            } else {
-                const uint32_t i0 = x.base + k * 512 + x.lane * 8;
-                uint8_t* rdst = x.dst + x.G.R + i0;
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if (i0 + j < x.n)
-                        rdst[j] = static_cast<uint8_t>(((j < 4 ? raw_a : raw_b) >> (8 * (j & 3))) & 0xFF);
-            }
+            for (int j = 0; j < 8; ++j)
+                if (i0 + j < x.n)
+                    rdst[j] = static_cast<uint8_t>(((j < 4 ? raw_a : raw_b) >> (8 * (j & 3))) & 0xFF);
         }
     }
     return mx >> 7;   // missing members were loaded as 0
@@ -345,80 +364,80 @@ __device__ inline void look_back_publish(uint64_t* __restrict__ status, uint32_t
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// One poll of the look-back window: the status words of the 64 tiles below
+// `top` (lane l reads tile top - l), zero where they belong to no
+// predecessor.
+__device__ inline uint64_t look_back_poll(const uint64_t* __restrict__ status, int64_t top,
+                                          uint32_t first, uint32_t lane)
+{
+    const int64_t idx = top - static_cast<int64_t>(lane);
+    uint64_t s = 0;
+    if (idx >= static_cast<int64_t>(first))
+        s = __hip_atomic_load(&status[idx * kStatusStride], __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+    return s;
+}
+
+// The exclusive byte offset of tile `t`: sums predecessors' sizes down to
+// the nearest one whose inclusive prefix is known, then publishes this
+// tile's inclusive prefix.  `s` is the first poll (of the window below the
+// tile), issued earlier by the caller so that its latency overlaps work.
 __device__ inline uint32_t look_back_resolve(uint64_t* __restrict__ status, uint32_t item,
                                              uint32_t t, uint32_t first, uint32_t tile_bytes,
-                                             uint32_t lane)
+                                             uint32_t lane, uint64_t s)
 {
     if (t == 0)
         return 0;
     int64_t top = static_cast<int64_t>(item) - 1;
     uint32_t acc = 0;
     while (true) {
-        const int64_t idx = top - static_cast<int64_t>(lane);
-        const bool in_range = idx >= static_cast<int64_t>(first);
-        uint64_t s = 0;
-        if (in_range)
-            s = __hip_atomic_load(&status[idx * kStatusStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool in_range = top - static_cast<int64_t>(lane) >= static_cast<int64_t>(first);
         const uint32_t flag = static_cast<uint32_t>(s >> 62);
         const uint64_t inc_mask = __ballot(in_range && flag == 2);
         const uint64_t zero_mask = __ballot(in_range && flag == 0);
         if (inc_mask) {
             const int p = __ffsll(static_cast<unsigned long long>(inc_mask)) - 1;
             const uint64_t below = (p == 0) ? 0ull : ((1ull << p) - 1);
-            if (zero_mask & below) {
-                __builtin_amdgcn_s_sleep(1);
-                continue;
+            if ((zero_mask & below) == 0) {
+                acc += wave_sum(lane <= static_cast<uint32_t>(p) ? static_cast<uint32_t>(s) : 0u);
+                break;
             }
-            acc += wave_sum(lane <= static_cast<uint32_t>(p) ? static_cast<uint32_t>(s) : 0u);
-            break;
-        }
-        if (zero_mask) {
-            __builtin_amdgcn_s_sleep(1);
+        } else if (zero_mask == 0) {
+            acc += wave_sum(static_cast<uint32_t>(s));
+            top -= kLanes;
+            s = look_back_poll(status, top, first, lane);
             continue;
         }
-        acc += wave_sum(static_cast<uint32_t>(s));
-        top -= kLanes;
+        // a predecessor has not published yet: poll the same window again
+        __builtin_amdgcn_s_sleep(1);
+        s = look_back_poll(status, top, first, lane);
     }
     if (lane == 0)
-        __hip_atomic_store(&status[item * kStatusStride], kFlagInc | (acc + tile_bytes), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&status[item * kStatusStride], kFlagInc | (acc + tile_bytes),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return acc;
 }
 
-// A raw group of a full tile: its 128 exponents, 8 bits each, first value
-// most significant, as 32 words starting at buffer word `w0`.
-__device__ inline void emit_raw_words(uint32_t* __restrict__ s, const uint32_t (&dd)[kSteps][2],
-                                      uint32_t emax, uint32_t w0)
-{
-    const uint32_t em4 = emax * 0x01010101u;
-#pragma unroll
-    for (int k = 0; k < kSteps; ++k) {
-        const uint32_t e0 = em4 - dd[k][0], e1 = em4 - dd[k][1];
-        *reinterpret_cast<uint2*>(&s[w0 + 2 * k]) =
-            make_uint2(__builtin_amdgcn_perm(e0, e0, 0x00010203u),
-                       __builtin_amdgcn_perm(e1, e1, 0x00010203u));
-    }
-}
-
-// Appends this lane's group to the LDS buffer from bit `off` (relative to
-// the buffer): one code word per value, or for a raw group (MIXED waves
-// only) its exponents as 8-bit words.  Inactive lanes write nothing.
-// A step whose coded values are all below the escape threshold appends its
-// code words two at a time (at most 28 bits per pair).
+// Appends this thread's members of its group to the LDS tile stream from bit
+// `off`: one code word per value, or for a raw group (MIXED waves only) the
+// exponents as 8-bit words.  `first` is the group member index of the
+// thread's first value; members at or past `ng` are not written.  A step in
+// which no lane of the wave has an escape appends its code words two at a
+// time (at most 28 bits per pair).
 template <bool FULL, bool MIXED>
-__device__ inline void emit_group(uint32_t* __restrict__ s, const EncTables& tb,
-                                  const uint32_t (&dd)[kSteps][2], uint32_t emax, uint32_t ng,
-                                  bool raw_mode, uint32_t off, bool active)
+__device__ inline void emit_quarter(uint32_t* __restrict__ s, const EncTables& tb,
+                                    const uint32_t (&dd)[kQSteps][2], uint32_t emax,
+                                    uint32_t ng, uint32_t first, bool raw_mode, uint32_t off)
 {
     uint64_t acc = 0;
-    uint32_t nacc = active ? (off & 31) : 0u;
-    uint32_t wi = active ? (off >> 5) : 0u;
-    const bool coded = active && !raw_mode;
-#pragma unroll 1
-    for (int k = 0; k < kSteps; ++k) {
+    uint32_t nacc = off & 31;
+    uint32_t wi = off >> 5;
+    const bool coded = !raw_mode;
+#pragma unroll
+    for (int k = 0; k < kQSteps; ++k) {
         const uint32_t d4[2] = {dd[k][0], dd[k][1]};
         const bool esc_here = coded && (((d4[0] | d4[1]) & 0xF0F0F0F0u) != 0);
-        if (__ballot(esc_here) == 0) {
+        if ((!MIXED || ZC_MIXED_PAIR) && __ballot(esc_here) == 0) {
 #pragma unroll
             for (int j = 0; j < 8; j += 2) {
                 uint32_t c2[2], l2[2];
@@ -431,7 +450,7 @@ __device__ inline void emit_group(uint32_t* __restrict__ s, const EncTables& tb,
                         c = raw_mode ? ((emax - d) & 0xFF) : c;
                         l = raw_mode ? 8u : l;
                     }
-                    const bool valid = active && (FULL || static_cast<uint32_t>(k * 8 + jj) < ng);
+                    const bool valid = FULL || first + static_cast<uint32_t>(k * 8 + jj) < ng;
                     c2[u] = valid ? c : 0u;
                     l2[u] = valid ? l : 0u;
                 }
@@ -451,7 +470,7 @@ __device__ inline void emit_group(uint32_t* __restrict__ s, const EncTables& tb,
                 uint32_t ent = tb.esc[d];
                 if (MIXED && raw_mode)
                     ent = ((emax - d) & 0xFF) | (8u << 24);
-                const bool valid = active && (FULL || static_cast<uint32_t>(k * 8 + j) < ng);
+                const bool valid = FULL || first + static_cast<uint32_t>(k * 8 + j) < ng;
                 ent = valid ? ent : 0u;
                 const uint32_t L = (ent >> 24) & 31;
                 const uint32_t esc = static_cast<uint32_t>(static_cast<int32_t>(ent) >> 31);
@@ -470,110 +489,115 @@ __device__ inline void emit_group(uint32_t* __restrict__ s, const EncTables& tb,
         atomicOr(&s[wi], lo32(acc) << (32 - nacc));
 }
 
-__device__ inline void zero_words(uint32_t* __restrict__ s, uint32_t count, uint32_t lane)
+// Stores a tile stream from LDS to its 4-byte aligned place: single words
+// up to the first 16-byte boundary, 16-byte stores after it, single words
+// for the rest.
+__device__ inline void store_stream(uint8_t* gdst, const uint32_t* __restrict__ s,
+                                    uint32_t words, uint32_t lane)
 {
-    for (uint32_t w = lane * 4; w < count; w += kLanes * 4)
-        *reinterpret_cast<uint4*>(&s[w]) = make_uint4(0, 0, 0, 0);
+    uint32_t* g = reinterpret_cast<uint32_t*>(gdst);
+    const uint32_t head = min(words, (4u - ((reinterpret_cast<uintptr_t>(g) >> 2) & 3u)) & 3u);
+    if (lane < head)
+        st_nt1(g + lane, s[lane]);
+    const uint32_t quads = (words - head) >> 2;
+    for (uint32_t q = lane; q < quads; q += kLanes) {
+        const uint32_t w = head + 4 * q;
+        st_nt4(g + w, make_uint4(s[w], s[w + 1], s[w + 2], s[w + 3]));
+    }
+    const uint32_t done = head + 4 * quads;
+    if (done + lane < words)
+        st_nt1(g + done + lane, s[done + lane]);
 }
 
-__device__ inline void store_words(uint32_t* __restrict__ g, const uint32_t* __restrict__ s,
-                                   uint32_t count, uint32_t lane)
-{
-    for (uint32_t w = lane; w < count; w += kLanes)
-        st_nt1(g + w, s[w]);
-}
-
+// Everything after the loads: the partial maxima of the four waves are in
+// sh.part_max (written before the barrier that precedes this call).
 template <bool FULL>
-__device__ void compress_tile(const TileCtx& x, int64_t* __restrict__ comp_sizes,
-                              uint64_t* __restrict__ status, uint32_t* __restrict__ s,
-                              const EncTables& tb)
+__device__ void compress_tile_back(const TileCtx& x, uint32_t (&dd)[kQSteps][2],
+                                   int64_t* __restrict__ comp_sizes,
+                                   uint64_t* __restrict__ status, EncShared& sh)
 {
-    const uint32_t lane = x.lane;
+    const uint32_t lane = x.lane, wave = x.wave;
     const uint32_t ng = FULL ? 128u : group_members(x.rem, lane);
+    const uint32_t first = wave * kQMembers;     // group index of this thread's first member
 
-    uint32_t dd[kSteps][2];
-    const uint32_t emax = load_split<FULL>(x, dd);
+    // 1. the group maximum from four partial ones
+    const uint32_t emax = max(max(sh.part_max[0][lane], sh.part_max[1][lane]),
+                              max(sh.part_max[2][lane], sh.part_max[3][lane]));
 
     // 2. distances d = E_max - e (bytes never borrow: e <= E_max) and the
-    //    coded length of the group
+    //    coded length of this thread's members
     const uint32_t em4 = emax * 0x01010101u;
 #pragma unroll
-    for (int k = 0; k < kSteps; ++k) {
+    for (int k = 0; k < kQSteps; ++k) {
         dd[k][0] = em4 - dd[k][0];
         dd[k][1] = em4 - dd[k][1];
     }
     uint32_t bits = 0;
-#pragma unroll 1
-    for (int k = 0; k < kSteps; ++k) {
-        const uint32_t d4[2] = {dd[k][0], dd[k][1]};
+#pragma unroll
+    for (int k = 0; k < kQSteps; ++k) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const uint32_t d = (d4[j >> 2] >> (8 * (j & 3))) & 0xFF;
-            const uint32_t L = tb.len[d];
-            bits += (FULL || static_cast<uint32_t>(k * 8 + j) < ng) ? L : 0u;
+            const uint32_t d = (dd[k][j >> 2] >> (8 * (j & 3))) & 0xFF;
+            const uint32_t L = sh.tb.len[d];
+            bits += (FULL || first + static_cast<uint32_t>(k * 8 + j) < ng) ? L : 0u;
         }
     }
-    const bool raw_mode = ng > 0 && bits >= 8 * ng;
-    const uint32_t glen = raw_mode ? 8 * ng : bits;
+    sh.part_bits[wave][lane] = bits;
+    __syncthreads();
 
-    // 3. lane offsets and tile size; the tile's size is published at once
+    // 3. the group's length and mode, where this thread's part starts, and
+    //    the lane offsets of the tile stream
+    const uint32_t b0 = sh.part_bits[0][lane], b1 = sh.part_bits[1][lane],
+                   b2 = sh.part_bits[2][lane], b3 = sh.part_bits[3][lane];
+    const uint32_t gbits = b0 + b1 + b2 + b3;
+    const bool raw_mode = ng > 0 && gbits >= 8 * ng;
+    const uint32_t glen = raw_mode ? 8 * ng : gbits;
+    uint32_t pre = 0;
+    pre += wave > 0 ? b0 : 0u;
+    pre += wave > 1 ? b1 : 0u;
+    pre += wave > 2 ? b2 : 0u;
+    if (raw_mode)
+        pre = 8 * min(ng, first);
     uint32_t tile_bits;
     const uint32_t off = wave_excl_scan(glen, lane, &tile_bits);
     const uint32_t tile_words = (tile_bits + 31) >> 5;
     const uint32_t tile_bytes = tile_words * 4;
-    look_back_publish(status, x.item, x.t, tile_bytes, lane);
-
-    // 4. the tile stream, assembled in LDS (most significant bit first) while
-    //    the predecessors finish; then the tile's offset, the index arrays
-    //    and a coalesced store.  A stream longer than the buffer (many raw
-    //    groups) is assembled and stored in two passes, lanes 0-31 then 32-63.
-    const uint64_t raw_lanes = __ballot(raw_mode);
-    uint32_t toff;
-    if (tile_words <= static_cast<uint32_t>(kStageWords)) {
-        zero_words(s, tile_words + 1, lane);
-        wave_lds_sync();
-        if (raw_lanes == 0)
-            emit_group<FULL, false>(s, tb, dd, emax, ng, raw_mode, off, true);
-        else
-            emit_group<FULL, true>(s, tb, dd, emax, ng, raw_mode, off, true);
-        wave_lds_sync();
-        toff = look_back_resolve(status, x.item, x.t, x.first, tile_bytes, lane);
-        uint32_t* gstream = reinterpret_cast<uint32_t*>(x.dst + x.G.X + toff);
-        store_words(gstream, s, tile_words, lane);
-    } else {
-        toff = look_back_resolve(status, x.item, x.t, x.first, tile_bytes, lane);
-        uint32_t* gstream = reinterpret_cast<uint32_t*>(x.dst + x.G.X + toff);
-        const bool all_raw = FULL && raw_lanes == ~0ull;
-        const uint32_t m = __shfl(off, 32) >> 5;   // first word lanes 32-63 touch
-#pragma unroll 1
-        for (int h = 0; h < 2; ++h) {
-            const bool active = (lane >> 5) == static_cast<uint32_t>(h);
-            const uint32_t bw = h ? m : 0u;        // buffer word 0 = stream word bw
-            const uint32_t count = h ? tile_words - m : m + 1;
-            if (h) {
-                const uint32_t carry = s[m];       // lanes 0-31's bits in word m
-                wave_lds_sync();
-                zero_words(s, count + 1, lane);
-                wave_lds_sync();
-                if (lane == 0)
-                    s[0] = carry;
-            } else {
-                zero_words(s, count + 1, lane);
-            }
-            wave_lds_sync();
-            if (all_raw) {
-                if (active)
-                    emit_raw_words(s, dd, emax, (off >> 5) - bw);
-            } else {
-                emit_group<FULL, true>(s, tb, dd, emax, ng, raw_mode, off - 32 * bw, active);
-            }
-            wave_lds_sync();
-            store_words(gstream + bw, s, h ? count : m, lane);
-            wave_lds_sync();
-        }
+    uint64_t poll = 0;
+    if (wave == 0) {
+        look_back_publish(status, x.item, x.t, tile_bytes, lane);
+        if (ZC_EARLY_POLL && x.t != 0)
+            poll = look_back_poll(status, static_cast<int64_t>(x.item) - 1, x.first, lane);
     }
 
-    // 5. index arrays
+    // 4. code words into the LDS tile stream (zeroed at the kernel's start)
+    if (__ballot(raw_mode) == 0)
+        emit_quarter<FULL, false>(sh.stage, sh.tb, dd, emax, ng, first, raw_mode, off + pre);
+    else
+        emit_quarter<FULL, true>(sh.stage, sh.tb, dd, emax, ng, first, raw_mode, off + pre);
+    __syncthreads();
+    if (wave != 0)
+        return;
+
+    // 5. wave 0: the tile's offset, the stream, the index arrays
+    if (!ZC_EARLY_POLL && x.t != 0)
+        poll = look_back_poll(status, static_cast<int64_t>(x.item) - 1, x.first, lane);
+    const uint32_t toff = look_back_resolve(status, x.item, x.t, x.first, tile_bytes, lane, poll);
+    if (ZC_STORE_X4) {
+        store_stream(x.dst + x.G.X + toff, sh.stage, tile_words, lane);
+    } else {
+        // eight rows of LDS reads ahead of their stores
+        uint32_t* gstream = reinterpret_cast<uint32_t*>(x.dst + x.G.X + toff);
+        for (uint32_t r0 = 0; r0 < tile_words; r0 += 8 * kLanes) {
+            uint32_t v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = sh.stage[min(r0 + i * kLanes + lane, static_cast<uint32_t>(kEncStage - 1))];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (r0 + i * kLanes + lane < tile_words)
+                    st_nt1(gstream + r0 + i * kLanes + lane, v[i]);
+        }
+    }
     if (lane == 0)
         *reinterpret_cast<uint32_t*>(x.dst + 32 + 4ull * x.t) = toff;
     x.dst[32 + 4ull * x.G.T + 64ull * x.t + lane] = static_cast<uint8_t>(emax);
@@ -599,8 +623,8 @@ __device__ void compress_tile(const TileCtx& x, int64_t* __restrict__ comp_sizes
 // line so that their register needs do not constrain the full-tile path.
 __device__ __attribute__((noinline)) void compress_tile_partial(
     const uint16_t* src, uint8_t* dst, uint32_t n, uint32_t t, uint32_t item, uint32_t first,
-    uint32_t lane, int c, int64_t* __restrict__ comp_sizes, uint64_t* __restrict__ status,
-    uint32_t* __restrict__ s, const EncTables& tb)
+    uint32_t lane, uint32_t wave, int c, int64_t* __restrict__ comp_sizes,
+    uint64_t* __restrict__ status, EncShared* sh)
 {
     TileCtx x;
     x.src = src;
@@ -610,86 +634,82 @@ __device__ __attribute__((noinline)) void compress_tile_partial(
     x.item = item;
     x.first = first;
     x.lane = lane;
+    x.wave = wave;
     x.c = c;
     x.G = geometry(n);
     x.base = t * kTile;
     x.rem = min(n - x.base, static_cast<uint32_t>(kTile));
-    compress_tile<false>(x, comp_sizes, status, s, tb);
-}
-
-__device__ inline void compress_item(const ChunkTable& tab, uint32_t item, uint32_t lane,
-                                     uint32_t* __restrict__ tickets,
-                                     const uint16_t* __restrict__ in, uint8_t* __restrict__ out,
-                                     int64_t* __restrict__ comp_sizes,
-                                     uint64_t* __restrict__ status, uint32_t* __restrict__ s,
-                                     const EncTables& tb)
-{
-    // The wave's chunk comes from its position in the grid: round-robin over
-    // the chunks when they are all the same size, so that few tiles of one
-    // chunk are in flight at once; chunk by chunk otherwise.  Its tile within
-    // the chunk comes from that chunk's own ticket counter, so a tile only
-    // ever waits for lower tickets of its chunk, held by waves that are
-    // already running.  Status words stay in chunk order.
-    TileCtx x;
-    if (ZC_ENC_INTERLEAVE && tab.uniform_tiles)
-        x.c = static_cast<int>(item % static_cast<uint32_t>(tab.nchunks));
-    else
-        x.c = find_chunk(tab, item);
-    {
-        uint32_t tk = 0;
-        if (lane == 0)
-            tk = atomicAdd(&tickets[x.c * kTicketStride], 1u);
-        x.t = __builtin_amdgcn_readfirstlane(tk);
-    }
-    x.n = tab.n[x.c];
-    x.first = tab.item_begin[x.c];
-    x.item = x.first + x.t;
-    x.lane = lane;
-    x.src = in + tab.voff[x.c];
-    x.dst = out + tab.boff[x.c];
-    x.G = geometry(x.n);
-
-    if (x.n == 0) {
-        if (lane < 8)
-            reinterpret_cast<uint32_t*>(x.dst)[lane] = header_word(lane, 0, 32);
-        if (lane == 0)
-            comp_sizes[x.c] = 32;
-        return;
-    }
-    x.base = x.t * kTile;
-    x.rem = min(x.n - x.base, static_cast<uint32_t>(kTile));
-    const bool full = x.rem == kTile && ((reinterpret_cast<uintptr_t>(x.src) & 15) == 0);
-    if (full)
-        compress_tile<true>(x, comp_sizes, status, s, tb);
-    else
-        compress_tile_partial(x.src, x.dst, x.n, x.t, x.item, x.first, lane, x.c, comp_sizes,
-                              status, s, tb);
+    uint32_t dd[kQSteps][2];
+    sh->part_max[wave][lane] = load_split<false>(x, dd);
+    __syncthreads();
+    compress_tile_back<false>(x, dd, comp_sizes, status, *sh);
 }
 
 __global__ __launch_bounds__(kBlock, kMinWavesEnc)
 void zc_compress_kernel(const uint16_t* __restrict__ in, uint8_t* __restrict__ out,
                         int64_t* __restrict__ comp_sizes,
-                        uint64_t* __restrict__ status, uint32_t* __restrict__ ticket,
+                        uint64_t* __restrict__ status, uint32_t* __restrict__ tickets,
                         ChunkTable tab)
 {
-    __shared__ __align__(16) uint32_t s_stage[kWaves][kStageAlloc];
-    __shared__ EncTables tb;
+    __shared__ __align__(16) EncShared sh;
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & (kLanes - 1);
     const uint32_t wave = tid / kLanes;
     {
         const uint32_t e = enc_entry(tid);
-        tb.esc[tid] = e;
-        tb.len[tid] = static_cast<uint8_t>((e >> 24) & 31);
+        sh.tb.esc[tid] = e;
+        sh.tb.len[tid] = static_cast<uint8_t>((e >> 24) & 31);
         const uint32_t s = tid < static_cast<uint32_t>(kEsc) ? tid : static_cast<uint32_t>(kEsc);
-        tb.code[tid] = static_cast<uint16_t>(c_code[s]);
+        sh.tb.code[tid] = static_cast<uint16_t>(c_code[s]);
     }
-    __syncthreads();
+    for (uint32_t i = tid * 4; i < static_cast<uint32_t>(kEncStage); i += kBlock * 4)
+        *reinterpret_cast<uint4*>(&sh.stage[i]) = make_uint4(0, 0, 0, 0);
 
-    const uint32_t item = blockIdx.x * kWaves + wave;
-    if (item < tab.nitems)
-        compress_item(tab, item, lane, ticket, in, out, comp_sizes, status, s_stage[wave], tb);
+    // The workgroup's chunk comes from its position in the grid: round-robin
+    // over the chunks when they all have the same number of tiles, so that
+    // few tiles of one chunk are in flight at once; chunk by chunk otherwise.
+    // Its tile within the chunk comes from that chunk's ticket counter, so a
+    // tile only waits for lower tickets of its chunk, held by workgroups that
+    // are already running.
+    const uint32_t item = blockIdx.x;
+    TileCtx x;
+    if (ZC_ENC_INTERLEAVE && tab.uniform_tiles)
+        x.c = static_cast<int>(item % static_cast<uint32_t>(tab.nchunks));
+    else
+        x.c = find_chunk(tab, item);
+    if (tid == 0)
+        sh.tile = atomicAdd(&tickets[x.c * kTicketStride], 1u);
+    __syncthreads();
+    x.t = sh.tile;
+    x.n = tab.n[x.c];
+    x.first = tab.item_begin[x.c];
+    x.item = x.first + x.t;
+    x.lane = lane;
+    x.wave = wave;
+    x.src = in + tab.voff[x.c];
+    x.dst = out + tab.boff[x.c];
+    x.G = geometry(x.n);
+
+    if (x.n == 0) {
+        if (tid < 8)
+            reinterpret_cast<uint32_t*>(x.dst)[tid] = header_word(tid, 0, 32);
+        if (tid == 0)
+            comp_sizes[x.c] = 32;
+        return;
+    }
+    x.base = x.t * kTile;
+    x.rem = min(x.n - x.base, static_cast<uint32_t>(kTile));
+    const bool full = x.rem == kTile && ((reinterpret_cast<uintptr_t>(x.src) & 15) == 0);
+    if (full) {
+        uint32_t dd[kQSteps][2];
+        sh.part_max[wave][lane] = load_split<true>(x, dd);
+        __syncthreads();
+        compress_tile_back<true>(x, dd, comp_sizes, status, sh);
+    } else {
+        compress_tile_partial(x.src, x.dst, x.n, x.t, x.item, x.first, lane, wave, x.c,
+                              comp_sizes, status, &sh);
+    }
 }
 
 // ------------------------------------------------------------ decompress
@@ -900,6 +920,25 @@ __device__ inline void decode_group(const Win& win, const uint8_t* __restrict__ 
     }
 }
 
+// Copies `words` (1..1024) tile-stream words from global memory into LDS.
+// Every load of a lane is issued before the first is written, so the copy
+// costs one memory round trip; rows past the end are skipped as a whole and
+// the last row's addresses are clamped to the last word.
+__device__ inline void stage_words(uint32_t* __restrict__ s, const uint32_t* __restrict__ g,
+                                   uint32_t words, uint32_t lane)
+{
+    constexpr int kRows = kStageWords / kLanes;
+    uint32_t v[kRows];
+#pragma unroll
+    for (int i = 0; i < kRows; ++i)
+        if (static_cast<uint32_t>(i * kLanes) < words)
+            v[i] = ld_nt1(g + min(lane + i * kLanes, words - 1));
+#pragma unroll
+    for (int i = 0; i < kRows; ++i)
+        if (lane + i * kLanes < words)
+            s[lane + i * kLanes] = v[i];
+}
+
 // A full tile whose 64 groups are all raw: every group stream is 1024 bits
 // of plain exponents at bit 1024 * lane.  The 8 KiB tile stream is staged in
 // two halves, each decoded by the 32 lanes that own it.
@@ -913,8 +952,7 @@ __device__ inline void decode_all_raw(const uint32_t* __restrict__ gstream,
 #pragma unroll 1
     for (int h = 0; h < 2; ++h) {
         wave_lds_sync();
-        for (uint32_t w = lane; w < static_cast<uint32_t>(kStageWords); w += kLanes)
-            s[w] = ld_nt1(gstream + h * kStageWords + w);
+        stage_words(s, gstream + h * kStageWords, kStageWords, lane);
         wave_lds_sync();
         if ((lane >> 5) == static_cast<uint32_t>(h)) {
             const uint32_t* mine = s + (lane & 31) * 32;
@@ -1032,8 +1070,7 @@ __device__ void decompress_tile(const uint8_t* __restrict__ src, uint16_t* __res
     if (FULL && raw_lanes == ~0ull) {
         decode_all_raw(gstream, s, s_len, rsrc, dst, n, base, lane, emax, vec_out, st);
     } else if (tile_words <= static_cast<uint32_t>(kStageWords)) {
-        for (uint32_t w = lane; w < tile_words; w += kLanes)
-            s[w] = ld_nt1(gstream + w);
+        stage_words(s, gstream, tile_words, lane);
         if (lane < 4)
             s[tile_words + lane] = 0;
         wave_lds_sync();
@@ -1149,7 +1186,6 @@ uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 constexpr size_t kWsHeader = kMaxChunks * kTicketStride * 4;   // per-chunk ticket counters
 
-uint32_t blocks_for(uint32_t items) { return (items + kWaves - 1) / kWaves; }
 
 }  // namespace
 
@@ -1245,7 +1281,7 @@ int zc_compress(const uint16_t* d_in, const int64_t* counts, int32_t num_chunks,
         const uint32_t cblocks = (words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024;
         hipLaunchKernelGGL(zc_clear_kernel, dim3(cblocks), dim3(256), 0, s, ticket, twords,
                            status, items);
-        hipLaunchKernelGGL(zc_compress_kernel, dim3(blocks_for(items)), dim3(kBlock), 0, s, d_in,
+        hipLaunchKernelGGL(zc_compress_kernel, dim3(items), dim3(kBlock), 0, s, d_in,
                            out, d_comp_sizes + c0, status, ticket, tab);
         if (hipGetLastError() != hipSuccess)
             return ZC_EHIP;
@@ -1294,7 +1330,7 @@ int zc_decompress(const void* d_in, size_t in_bytes, const int64_t* in_offsets,
         tab.nchunks = m;
         tab.nitems = items;
         tab.item_begin[m] = items;
-        hipLaunchKernelGGL(zc_decompress_kernel, dim3(blocks_for(items)), dim3(kBlock), 0, s, in,
+        hipLaunchKernelGGL(zc_decompress_kernel, dim3((items + kWaves - 1) / kWaves), dim3(kBlock), 0, s, in,
                            d_out, d_status, tab);
         if (hipGetLastError() != hipSuccess)
             return ZC_EHIP;
