@@ -92,9 +92,10 @@ static_assert(ZC_T1_NSYM == 17, "table_id 1 has 17 symbols");
 static_assert(ZC_T1_TAIL_OK == 1, "long code words must share the all-ones prefix");
 static_assert(ZC_T1_MAXLEN <= kLutBits + kTailBits, "code words must fit two lookup levels");
 static_assert(kEscLen + 8 <= 32, "escape payload must fit the window");
-static_assert(kLutBits == 8, "raw groups index the byte table with 8 stream bits");
+static_assert(kLutBits >= 8 && (1 << kLutBits) % (16 * kBlock) == 0,
+              "the first level is loaded as one 16-byte word per thread");
 
-__constant__ uint8_t c_lut[1 << kLutBits] = ZC_T1_LUT_INIT;
+__constant__ __align__(16) uint8_t c_lut[1 << kLutBits] = ZC_T1_LUT_INIT;
 __constant__ uint16_t c_tail[1 << kTailBits] = ZC_T1_TAIL_INIT;
 __constant__ uint8_t c_len[ZC_T1_NSYM] = ZC_T1_LEN_INIT;
 __constant__ uint32_t c_code[ZC_T1_NSYM] = ZC_T1_CODE_INIT;
@@ -757,10 +758,12 @@ struct GlobalWindow {
     }
 };
 
-// Per-lane decoding parameters.  Coded groups look the first 8 stream bits
-// up in (symbol << 4 | length) byte entries; raw groups look their 8 bits up
-// in entries that hold 255 - e and always advance by 8.
+// Per-lane decoding parameters.  Coded groups look the first 12 stream bits
+// up in (symbol << 4 | length) byte entries (every code word but the three
+// longest fits); raw groups look their 8 bits up in entries that hold 255 - e
+// and always advance by 8.
 struct LaneCode {
+    uint32_t ish;        // the table index is the window's top 32 - ish bits
     uint32_t base;       // LDS byte index of the lane's table
     uint32_t sym_sh;     // entry >> sym_sh = symbol
     uint32_t smask;      // (entry & smask) | sor = bits consumed
@@ -778,7 +781,7 @@ __device__ inline void decode_sym(const uint8_t* __restrict__ s_lut8,
                                   const LaneCode& q, uint32_t emax, bool valid,
                                   int32_t& esc_min, uint32_t& sym, uint32_t& sh)
 {
-    const uint32_t ent = s_lut8[(top >> (32 - kLutBits)) + q.base];
+    const uint32_t ent = s_lut8[(top >> q.ish) + q.base];
     sym = ent >> q.sym_sh;
     sh = (ent & q.smask) | q.sor;
     if (ent == q.lmark) {
@@ -838,6 +841,7 @@ __device__ inline void decode_group(const Win& win, const uint8_t* __restrict__ 
                                     bool any_raw, bool vec_out, DecState& st)
 {
     LaneCode q;
+    q.ish = raw_mode ? 24u : static_cast<uint32_t>(32 - kLutBits);
     q.base = raw_mode ? static_cast<uint32_t>(kLutRaw) : 0u;
     q.sym_sh = raw_mode ? 0u : 4u;
     q.smask = raw_mode ? 0u : 15u;
@@ -1115,14 +1119,15 @@ void zc_decompress_kernel(const uint8_t* __restrict__ in, uint16_t* __restrict__
                           int32_t* __restrict__ status, ChunkTable tab)
 {
     __shared__ __align__(16) uint32_t s_stage[kWaves][kStageAlloc];
-    __shared__ uint8_t s_lut8[kLutRaw + 256];
+    __shared__ __align__(16) uint8_t s_lut8[kLutRaw + 256];
     __shared__ uint16_t s_tail[1 << kTailBits];
     __shared__ uint8_t s_len[256];
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & (kLanes - 1);
     const uint32_t wave = tid / kLanes;
-    s_lut8[tid] = c_lut[tid];
+    for (uint32_t i = tid; i < (1u << kLutBits) / 16; i += kBlock)
+        reinterpret_cast<uint4*>(s_lut8)[i] = reinterpret_cast<const uint4*>(c_lut)[i];
     // raw groups: 8 bits b decode to 255 - b
     s_lut8[kLutRaw + tid] = static_cast<uint8_t>(255u - tid);
     if (tid < (1u << kTailBits))

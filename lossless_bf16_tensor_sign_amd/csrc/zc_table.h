@@ -9,8 +9,8 @@ constexpr int kEscapeFrom = 16;          // d >= 16 is escaped
 constexpr int kEscape = kEscapeFrom;     // symbol index of ESC
 constexpr int kSymbols = kEscapeFrom + 1;
 constexpr int kMaxCodeLen = 24;          // longest code word the kernels take
-constexpr int kLutBits = 8;              // decoder first-level lookup width
-constexpr int kTailBits = 6;             // second level (codes up to 14 bits)
+constexpr int kLutBits = 12;             // decoder first-level lookup width
+constexpr int kTailBits = 2;             // second level (codes up to 14 bits)
 
 struct Table {
     double prob[kSymbols];
