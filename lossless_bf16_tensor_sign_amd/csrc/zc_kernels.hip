@@ -205,6 +205,7 @@ __device__ inline int find_chunk(const ChunkTable& tab, uint32_t item)
 }
 
 __device__ inline uint32_t hi32(uint64_t x) { return static_cast<uint32_t>(x >> 32); }
+__device__ inline uint32_t max3(uint32_t a, uint32_t b, uint32_t c) { return max(a, max(b, c)); }
 __device__ inline uint32_t lo32(uint64_t x) { return static_cast<uint32_t>(x); }
 
 // Streaming accesses: every input byte is read once and every output byte
@@ -832,7 +833,7 @@ struct DecState {
 
 // Decodes the 128 members of this lane's group from a window source and
 // writes the values.
-template <bool FULL, class Win>
+template <bool FULL, int kSym, class Win>
 __device__ inline void decode_group(const Win& win, const uint8_t* __restrict__ s_lut8,
                                     const uint16_t* __restrict__ s_tail,
                                     const uint8_t* __restrict__ s_len, const uint8_t* __restrict__ rsrc,
@@ -859,50 +860,60 @@ __device__ inline void decode_group(const Win& win, const uint8_t* __restrict__ 
     }
 #pragma unroll 1
     for (int k = 0; k < kSteps; ++k) {
+        // kSym symbols per 64-bit window; a lane whose code words overrun
+        // the window (several escapes) decodes them again one at a time
         uint32_t e8[8];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < 8 / kSym; ++h) {
             const uint32_t pos0 = st.pos;
             uint64_t W = win(pos0);
             uint32_t used = 0;
-            int32_t esc_h = 255;
+            int32_t esc_w = 255;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bool valid = FULL || static_cast<uint32_t>(k * 8 + h * 4 + j) < ng;
+            for (int jj = 0; jj < kSym; ++jj) {
+                const int j = h * kSym + jj;
+                const bool valid = FULL || static_cast<uint32_t>(k * 8 + j) < ng;
                 uint32_t sym, sh;
-                decode_sym(s_lut8, s_tail, hi32(W), q, emax, valid, esc_h, sym, sh);
+                decode_sym(s_lut8, s_tail, hi32(W), q, emax, valid, esc_w, sym, sh);
                 if (!FULL && !valid)
                     sh = 0;
-                e8[h * 4 + j] = q.emax_eff - sym;
+                e8[j] = q.emax_eff - sym;
                 W <<= sh;
                 used += sh;
             }
-            if (__ballot(used > 64)) {
-                // a half-step longer than the window (several escapes): decode
-                // those lanes again symbol by symbol
-                if (used > 64) {
+            const bool slow = used > 64;
+            if (!slow)
+                st.esc_min = min(st.esc_min, esc_w);
+            if (__ballot(slow)) {
+                if (slow) {
                     uint32_t p = pos0;
-                    esc_h = 255;
+                    int32_t esc_h = 255;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const bool valid = FULL || static_cast<uint32_t>(k * 8 + h * 4 + j) < ng;
+                    for (int jj = 0; jj < kSym; ++jj) {
+                        const int j = h * kSym + jj;
+                        const bool valid = FULL || static_cast<uint32_t>(k * 8 + j) < ng;
                         uint32_t sym, sh;
                         decode_sym(s_lut8, s_tail, hi32(win(p)), q, emax, valid, esc_h, sym, sh);
                         if (!FULL && !valid)
                             sh = 0;
-                        e8[h * 4 + j] = q.emax_eff - sym;
+                        e8[j] = q.emax_eff - sym;
                         p += sh;
                     }
                     used = p - pos0;
+                    st.esc_min = min(st.esc_min, esc_h);
                 }
             }
-            st.esc_min = min(st.esc_min, esc_h);
             st.pos = pos0 + used;
         }
+        if (FULL) {
+            st.seen_max = max(st.seen_max, max3(e8[0], e8[1], e8[2]));
+            st.seen_max = max(st.seen_max, max3(e8[3], e8[4], e8[5]));
+            st.seen_max = max(st.seen_max, max(e8[6], e8[7]));
+        } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (FULL || static_cast<uint32_t>(k * 8 + j) < ng)
-                st.seen_max = max(st.seen_max, e8[j]);
+            for (int j = 0; j < 8; ++j)
+                if (static_cast<uint32_t>(k * 8 + j) < ng)
+                    st.seen_max = max(st.seen_max, e8[j]);
         }
         if (any_raw) {
             // a raw group must not have been codable in fewer bits
@@ -1078,11 +1089,17 @@ __device__ void decompress_tile(const uint8_t* __restrict__ src, uint16_t* __res
         if (lane < 4)
             s[tile_words + lane] = 0;
         wave_lds_sync();
-        decode_group<FULL>(LdsWindow{s, tile_words}, s_lut8, s_tail, s_len, rsrc, dst, n, base,
-                           lane, ng, emax, raw_mode, raw_lanes != 0, vec_out, st);
+        // 8 symbols per window unless a coded group of the tile averages
+        // more than 5 bits per value (its windows would often overrun)
+        if (__ballot(!raw_mode && glen > 5 * ng) == 0)
+            decode_group<FULL, 8>(LdsWindow{s, tile_words}, s_lut8, s_tail, s_len, rsrc, dst, n,
+                                  base, lane, ng, emax, raw_mode, raw_lanes != 0, vec_out, st);
+        else
+            decode_group<FULL, 4>(LdsWindow{s, tile_words}, s_lut8, s_tail, s_len, rsrc, dst, n,
+                                  base, lane, ng, emax, raw_mode, raw_lanes != 0, vec_out, st);
     } else {
-        decode_group<FULL>(GlobalWindow{gstream, tile_words}, s_lut8, s_tail, s_len, rsrc, dst, n,
-                           base, lane, ng, emax, raw_mode, raw_lanes != 0, vec_out, st);
+        decode_group<FULL, 4>(GlobalWindow{gstream, tile_words}, s_lut8, s_tail, s_len, rsrc, dst,
+                              n, base, lane, ng, emax, raw_mode, raw_lanes != 0, vec_out, st);
     }
     if (err == 0 && ng > 0) {
         if (st.pos != off + glen)
