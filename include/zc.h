@@ -95,6 +95,11 @@ size_t zc_workspace_bytes(const int64_t* counts, int32_t num_chunks);
  * Returns ZC_OK once the work is queued, or an error before anything is
  * queued (ZC_EINVAL, ZC_ENOSPC) or when a launch fails (ZC_EHIP).  Calls that
  * share a workspace must be ordered on one stream.
+ * Every wait inside the kernel is bounded: a tile whose look-back finds a
+ * predecessor unpublished after a fixed number of polls recomputes that
+ * predecessor's size from the input, which gives the same stream.  The
+ * environment variable ZC_LOOKBACK_SPIN_LIMIT (a decimal poll count, read at
+ * each call) overrides that bound; tests set it to 0 to run that path.
  */
 int zc_compress(const uint16_t* d_in, const int64_t* counts,
                 int32_t num_chunks, void* d_out, size_t out_capacity,

@@ -6,19 +6,25 @@
 // statistics); the sign+mantissa byte is stored raw, which is how a 16-bit
 // value reaches about 11 bits (pith.science, Figure 6 caption).
 //
-// GPU mapping (MI355X, wave64; 4 independent waves per workgroup share the
-// code tables in LDS):
-//  * one wave owns one tile of 8192 values; lane l owns group 64t + l, whose
-//    values are 8 consecutive bf16 (one 16-byte load) at each of 16 steps, so
-//    every global load and store of the raw data is fully coalesced and the
-//    group maximum is lane-local;
+// GPU mapping (MI355X, wave64; the code tables live in LDS):
+//  * a tile holds 8192 values in 64 groups; group 64t + l takes 8 consecutive
+//    bf16 (one 16-byte load) at each of 16 steps, so every global load and
+//    store of the raw data is fully coalesced;
+//  * compress gives a tile to one workgroup of four waves: lane l of each
+//    wave works on group l, wave w on steps 4w..4w+3, and the four partial
+//    maxima and code lengths meet in LDS; decompress gives a tile to one
+//    wave, lane l decoding group l;
 //  * a wave prefix sum over the 64 group lengths places the lane streams in
 //    an LDS copy of the tile stream (the pages stage data in shared memory,
 //    Figure 7 caption), which is stored coalesced;
 //  * the byte offset of a tile inside its chunk's exponent section is an
 //    exclusive scan over the tiles of the chunk, done in the same pass with a
-//    decoupled look-back over per-tile status words; tiles are taken from a
-//    ticket counter, so every tile a wave waits on is already running;
+//    decoupled look-back over per-tile status words.  Equal chunks take their
+//    tiles from per-chunk ticket counters, so every tile a workgroup waits on
+//    is already running; uneven chunks take them in grid order (one shared
+//    counter would serialize a large chunk's workgroups).  Every wait is
+//    bounded: past the bound a missing predecessor's size is recomputed from
+//    its input;
 //  * all chunks of a call form one flat list of tiles, so uneven chunk sizes
 //    (the imbalance of Figure 8) still fill the GPU;
 //  * the inner loops are branch-free: the encoder appends one code word per
@@ -31,6 +37,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -47,6 +54,9 @@
 #endif
 #ifndef ZC_STATUS_STRIDE
 #define ZC_STATUS_STRIDE 8       // 8-byte look-back status words, one per this many
+#endif
+#ifndef ZC_POLL_LANES
+#define ZC_POLL_LANES 16         // predecessors read per look-back poll
 #endif
 #ifndef ZC_EARLY_POLL
 #define ZC_EARLY_POLL 0          // first look-back poll issued before emission
@@ -81,7 +91,8 @@ constexpr int kLutBits = ZC_T1_LUT_BITS;          // first decode level (byte en
 constexpr int kTailBits = ZC_T1_TAIL_BITS;        // second level
 constexpr int kLutRaw = 1 << kLutBits;            // raw-mode byte entries follow
 constexpr uint32_t kTicketStride = 32;             // one 128-byte line per chunk counter
-// Look-back status words sit one per 128-byte line: a tile's status is
+constexpr uint32_t kSpinLimit = 1u << 14;          // look-back polls before recomputing
+// Look-back status words sit one per 64-byte line: a tile's status is
 // written through to device-coherent memory, and tiles sharing a line would
 // serialize those writes.
 constexpr uint32_t kStatusStride = ZC_STATUS_STRIDE;
@@ -106,6 +117,8 @@ struct ChunkTable {
     int32_t nchunks;
     uint32_t nitems;
     uint32_t uniform_tiles;        // > 0: every chunk has this many tiles
+    uint32_t grid_order;           // compress: tile order from the grid, not from tickets
+    uint32_t spin_limit;           // compress: look-back polls before recomputing
     uint32_t item_begin[kMaxChunks + 1];
     uint32_t n[kMaxChunks];
     uint64_t voff[kMaxChunks];     // value offset of the chunk (bf16 side)
@@ -288,6 +301,7 @@ struct EncShared {
     uint32_t part_bits[kWaves][kLanes];
     EncTables tb;
     uint32_t tile;
+    uint32_t spin_limit;
 };
 
 struct TileCtx {
@@ -374,26 +388,62 @@ __device__ inline uint64_t look_back_poll(const uint64_t* __restrict__ status, i
 {
     const int64_t idx = top - static_cast<int64_t>(lane);
     uint64_t s = 0;
-    if (idx >= static_cast<int64_t>(first))
+    if (lane < ZC_POLL_LANES && idx >= static_cast<int64_t>(first))
         s = __hip_atomic_load(&status[idx * kStatusStride], __ATOMIC_RELAXED,
                               __HIP_MEMORY_SCOPE_AGENT);
     return s;
+}
+
+// The byte count of tile `t` of a chunk (`src`, `n` values) recomputed from
+// its input: the encoder's group maxima, code lengths and mode, one group
+// per lane.  The look-back falls back on it for a predecessor that has not
+// published within the spin limit, so that no wait is unbounded.
+__device__ inline uint32_t tile_bytes_from_input(
+    const uint16_t* __restrict__ src, uint32_t n, uint32_t t, uint32_t lane,
+    const uint8_t* __restrict__ len)
+{
+    const uint32_t base = t * kTile;
+    const uint32_t ng = group_members(min(n - base, static_cast<uint32_t>(kTile)), lane);
+    uint32_t emax = 0;
+#pragma unroll 1
+    for (int k = 0; k < kSteps; ++k)
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t i = base + k * 512 + lane * 8 + j;
+            if (i < n)
+                emax = max(emax, (static_cast<uint32_t>(src[i]) >> 7) & 0xFF);
+        }
+    uint32_t bits = 0;
+#pragma unroll 1
+    for (int k = 0; k < kSteps; ++k)
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t i = base + k * 512 + lane * 8 + j;
+            if (i < n)
+                bits += len[emax - ((static_cast<uint32_t>(src[i]) >> 7) & 0xFF)];
+        }
+    const uint32_t glen = (ng > 0 && bits >= 8 * ng) ? 8 * ng : bits;
+    return ((wave_sum(glen) + 31) >> 5) * 4;
 }
 
 // The exclusive byte offset of tile `t`: sums predecessors' sizes down to
 // the nearest one whose inclusive prefix is known, then publishes this
 // tile's inclusive prefix.  `s` is the first poll (of the window below the
 // tile), issued earlier by the caller so that its latency overlaps work.
+// After `spin_limit` polls that still miss a predecessor, the missing sizes
+// are recomputed from the input instead (the chunk is `src`, `n` values).
 __device__ inline uint32_t look_back_resolve(uint64_t* __restrict__ status, uint32_t item,
                                              uint32_t t, uint32_t first, uint32_t tile_bytes,
-                                             uint32_t lane, uint64_t s)
+                                             uint32_t lane, uint64_t s,
+                                             const uint16_t* __restrict__ src, uint32_t n,
+                                             const uint8_t* __restrict__ len, uint32_t spin_limit)
 {
     if (t == 0)
         return 0;
     int64_t top = static_cast<int64_t>(item) - 1;
     uint32_t acc = 0;
+    uint32_t spins = 0;
     while (true) {
-        const bool in_range = top - static_cast<int64_t>(lane) >= static_cast<int64_t>(first);
+        const bool in_range = lane < ZC_POLL_LANES &&
+                              top - static_cast<int64_t>(lane) >= static_cast<int64_t>(first);
         const uint32_t flag = static_cast<uint32_t>(s >> 62);
         const uint64_t inc_mask = __ballot(in_range && flag == 2);
         const uint64_t zero_mask = __ballot(in_range && flag == 0);
@@ -406,13 +456,26 @@ __device__ inline uint32_t look_back_resolve(uint64_t* __restrict__ status, uint
             }
         } else if (zero_mask == 0) {
             acc += wave_sum(static_cast<uint32_t>(s));
-            top -= kLanes;
+            top -= ZC_POLL_LANES;
             s = look_back_poll(status, top, first, lane);
             continue;
         }
-        // a predecessor has not published yet: poll the same window again
-        __builtin_amdgcn_s_sleep(1);
-        s = look_back_poll(status, top, first, lane);
+        if (spins < spin_limit) {
+            // a predecessor has not published yet: poll the same window again
+            ++spins;
+            __builtin_amdgcn_s_sleep(1);
+            s = look_back_poll(status, top, first, lane);
+            continue;
+        }
+        // waited too long: recompute the missing sizes (the chunk's first
+        // tile counts as an inclusive prefix)
+        for (uint64_t miss = zero_mask; miss; miss &= miss - 1) {
+            const int i = __ffsll(static_cast<unsigned long long>(miss)) - 1;
+            const uint32_t p = static_cast<uint32_t>(top - i);
+            const uint32_t bytes = tile_bytes_from_input(src, n, p - first, lane, len);
+            if (lane == static_cast<uint32_t>(i))
+                s = (p == first ? kFlagInc : kFlagAgg) | bytes;
+        }
     }
     if (lane == 0)
         __hip_atomic_store(&status[item * kStatusStride], kFlagInc | (acc + tile_bytes),
@@ -511,6 +574,32 @@ __device__ inline void store_stream(uint8_t* gdst, const uint32_t* __restrict__ 
         st_nt1(g + done + lane, s[done + lane]);
 }
 
+// Wave 0 of a tile: the tile's index entries; the last tile of a chunk also
+// writes the header, the zero gaps and the chunk's size.
+__device__ inline void write_tile_index(const TileCtx& x, uint32_t toff, uint32_t tile_bytes,
+                                        uint32_t emax, uint32_t glen,
+                                        int64_t* __restrict__ comp_sizes)
+{
+    const uint32_t lane = x.lane;
+    if (lane == 0)
+        *reinterpret_cast<uint32_t*>(x.dst + 32 + 4ull * x.t) = toff;
+    x.dst[32 + 4ull * x.G.T + 64ull * x.t + lane] = static_cast<uint8_t>(emax);
+    *reinterpret_cast<uint16_t*>(x.dst + 32 + 68ull * x.G.T + 2ull * (64ull * x.t + lane)) =
+        static_cast<uint16_t>(glen);
+    if (x.t == x.G.T - 1) {
+        const uint64_t comp = x.G.X + toff + tile_bytes;
+        if (lane < 8)
+            reinterpret_cast<uint32_t*>(x.dst)[lane] = header_word(lane, x.n, comp);
+        const uint64_t g1 = 32 + 196ull * x.G.T;
+        if (g1 + lane < x.G.R)
+            x.dst[g1 + lane] = 0;
+        if (x.G.R + x.n + lane < x.G.X)
+            x.dst[x.G.R + x.n + lane] = 0;
+        if (lane == 0)
+            comp_sizes[x.c] = static_cast<int64_t>(comp);
+    }
+}
+
 // Everything after the loads: the partial maxima of the four waves are in
 // sh.part_max (written before the barrier that precedes this call).
 template <bool FULL>
@@ -583,7 +672,8 @@ __device__ void compress_tile_back(const TileCtx& x, uint32_t (&dd)[kQSteps][2],
     // 5. wave 0: the tile's offset, the stream, the index arrays
     if (!ZC_EARLY_POLL && x.t != 0)
         poll = look_back_poll(status, static_cast<int64_t>(x.item) - 1, x.first, lane);
-    const uint32_t toff = look_back_resolve(status, x.item, x.t, x.first, tile_bytes, lane, poll);
+    const uint32_t toff = look_back_resolve(status, x.item, x.t, x.first, tile_bytes, lane, poll,
+                                            x.src, x.n, sh.tb.len, sh.spin_limit);
     if (ZC_STORE_X4) {
         store_stream(x.dst + x.G.X + toff, sh.stage, tile_words, lane);
     } else {
@@ -600,25 +690,7 @@ __device__ void compress_tile_back(const TileCtx& x, uint32_t (&dd)[kQSteps][2],
                     st_nt1(gstream + r0 + i * kLanes + lane, v[i]);
         }
     }
-    if (lane == 0)
-        *reinterpret_cast<uint32_t*>(x.dst + 32 + 4ull * x.t) = toff;
-    x.dst[32 + 4ull * x.G.T + 64ull * x.t + lane] = static_cast<uint8_t>(emax);
-    *reinterpret_cast<uint16_t*>(x.dst + 32 + 68ull * x.G.T + 2ull * (64ull * x.t + lane)) =
-        static_cast<uint16_t>(glen);
-
-    // 6. the last tile finishes the chunk: header, gaps, size
-    if (x.t == x.G.T - 1) {
-        const uint64_t comp = x.G.X + toff + tile_bytes;
-        if (lane < 8)
-            reinterpret_cast<uint32_t*>(x.dst)[lane] = header_word(lane, x.n, comp);
-        const uint64_t g1 = 32 + 196ull * x.G.T;
-        if (g1 + lane < x.G.R)
-            x.dst[g1 + lane] = 0;
-        if (x.G.R + x.n + lane < x.G.X)
-            x.dst[x.G.R + x.n + lane] = 0;
-        if (lane == 0)
-            comp_sizes[x.c] = static_cast<int64_t>(comp);
-    }
+    write_tile_index(x, toff, tile_bytes, emax, glen, comp_sizes);
 }
 
 // Tiles that are partial (a chunk's last tile) or unaligned: kept out of
@@ -681,9 +753,15 @@ void zc_compress_kernel(const uint16_t* __restrict__ in, uint8_t* __restrict__ o
     else
         x.c = find_chunk(tab, item);
     if (tid == 0)
-        sh.tile = atomicAdd(&tickets[x.c * kTicketStride], 1u);
-    __syncthreads();
-    x.t = sh.tile;
+        sh.spin_limit = tab.spin_limit;
+    if (!tab.grid_order) {
+        if (tid == 0)
+            sh.tile = atomicAdd(&tickets[x.c * kTicketStride], 1u);
+        __syncthreads();
+        x.t = sh.tile;
+    } else {
+        x.t = item - tab.item_begin[x.c];
+    }
     x.n = tab.n[x.c];
     x.first = tab.item_begin[x.c];
     x.item = x.first + x.t;
@@ -1206,6 +1284,19 @@ Counts check_counts(const int64_t* counts, int32_t num_chunks)
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
+// Look-back polls a tile makes before it recomputes a missing predecessor's
+// size from the input.  The environment variable ZC_LOOKBACK_SPIN_LIMIT
+// overrides the default (tests set 0 to run the recomputation path).
+uint32_t lookback_spin_limit()
+{
+    const char* e = std::getenv("ZC_LOOKBACK_SPIN_LIMIT");
+    if (!e || !*e)
+        return kSpinLimit;
+    char* end = nullptr;
+    const unsigned long v = std::strtoul(e, &end, 10);
+    return (end && *end == 0 && v <= 0xFFFFFFFFul) ? static_cast<uint32_t>(v) : kSpinLimit;
+}
+
 constexpr size_t kWsHeader = kMaxChunks * kTicketStride * 4;   // per-chunk ticket counters
 
 
@@ -1269,6 +1360,7 @@ int zc_compress(const uint16_t* d_in, const int64_t* counts, int32_t num_chunks,
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint32_t* ticket = static_cast<uint32_t*>(d_ws);
+    const uint32_t spin_limit = lookback_spin_limit();
     uint64_t* status = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(d_ws) + kWsHeader);
     uint8_t* out = static_cast<uint8_t*>(d_out);
 
@@ -1296,6 +1388,11 @@ int zc_compress(const uint16_t* d_in, const int64_t* counts, int32_t num_chunks,
         for (int32_t i = 0; i < m && tab.uniform_tiles; ++i)
             if (tab.item_begin[i + 1] - tab.item_begin[i] != tab.uniform_tiles || tab.n[i] == 0)
                 tab.uniform_tiles = 0;
+        // Equal chunks are interleaved and take tiles from per-chunk tickets;
+        // otherwise the grid order is the tile order (a shared ticket would
+        // serialize the workgroups of a large chunk).
+        tab.grid_order = (ZC_ENC_INTERLEAVE && tab.uniform_tiles) ? 0u : 1u;
+        tab.spin_limit = spin_limit;
 
         // the ticket word and the look-back status words start at zero
         const uint32_t twords = static_cast<uint32_t>(kWsHeader / 4);

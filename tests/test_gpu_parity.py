@@ -197,6 +197,24 @@ def test_workload_full_size(oracle, cfg):
         assert ratio > 1.3
 
 
+# ------------------------------------------------ look-back fallback ---
+
+@pytest.mark.parametrize("layout", ["equal", "ragged"])
+def test_lookback_recompute_path(oracle, monkeypatch, layout):
+    # A spin limit of 0: every tile that finds a predecessor unpublished
+    # recomputes that predecessor's size from its input at once.  The
+    # streams must not change, with tiles taken from tickets (equal chunks)
+    # and in grid order (uneven chunks).
+    monkeypatch.setenv("ZC_LOOKBACK_SPIN_LIMIT", "0")
+    if layout == "equal":
+        cnt = np.full(8, 6 * TILE, np.int64)
+    else:
+        cnt = np.array([3, 40 * TILE + 5, 7 * TILE, 0, 2 * TILE + 1], np.int64)
+    w = synth.gaussian_bits(int(cnt.sum()), 0.02, seed=31)
+    w[::997] = 0
+    check_against_oracle(oracle, w, cnt, label="spin limit 0, %s chunks" % layout)
+
+
 # ---------------------------------------------------------- errors ---
 
 def test_capacity_and_argument_errors():
