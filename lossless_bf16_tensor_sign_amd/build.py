@@ -23,6 +23,9 @@ HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
     # keep packed fp32 instructions out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # a single-lane atomic stays one atomic whose result is waited for where
+    # it is used (the optimizer's wave reduction waits at once)
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -103,13 +103,36 @@ static_assert(ZC_T1_NSYM == 17, "table_id 1 has 17 symbols");
 static_assert(ZC_T1_TAIL_OK == 1, "long code words must share the all-ones prefix");
 static_assert(ZC_T1_MAXLEN <= kLutBits + kTailBits, "code words must fit two lookup levels");
 static_assert(kEscLen + 8 <= 32, "escape payload must fit the window");
-static_assert(kLutBits >= 8 && (1 << kLutBits) % (16 * kBlock) == 0,
+static_assert(kLutBits >= 8 && (1 << kLutBits) == 16 * kBlock,
               "the first level is loaded as one 16-byte word per thread");
 
 __constant__ __align__(16) uint8_t c_lut[1 << kLutBits] = ZC_T1_LUT_INIT;
-__constant__ uint16_t c_tail[1 << kTailBits] = ZC_T1_TAIL_INIT;
 __constant__ uint8_t c_len[ZC_T1_NSYM] = ZC_T1_LEN_INIT;
 __constant__ uint32_t c_code[ZC_T1_NSYM] = ZC_T1_CODE_INIT;
+
+// The lengths and second-level entries of table_id 1 as compile-time
+// constants: the decoder's threads pick theirs with selects, so its small
+// LDS tables are set up without a memory round trip.
+constexpr uint32_t kLenT1[ZC_T1_NSYM] = ZC_T1_LEN_INIT;
+constexpr uint32_t kTailT1[1 << kTailBits] = ZC_T1_TAIL_INIT;
+
+__device__ inline uint32_t len_of(uint32_t s)
+{
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < ZC_T1_NSYM; ++i)
+        v = s == static_cast<uint32_t>(i) ? kLenT1[i] : v;
+    return v;
+}
+
+__device__ inline uint32_t tail_of(uint32_t i)
+{
+    uint32_t v = 0;
+#pragma unroll
+    for (int j = 0; j < (1 << kTailBits); ++j)
+        v = i == static_cast<uint32_t>(j) ? kTailT1[j] : v;
+    return v;
+}
 
 // Chunks of one launch.  Work item = one tile; an empty chunk gets one item
 // that only writes its header.
@@ -264,19 +287,6 @@ __global__ void zc_clear_kernel(uint32_t* __restrict__ tickets, uint32_t ticket_
     }
 }
 
-// Encoder entry for d = 0..255 used when escapes occur: code bits 0..21 (an
-// escape carries its code followed by 8 zero bits for the exponent), length
-// in bits 24..28, bit 31 set for escapes.
-__device__ inline uint32_t enc_entry(uint32_t d)
-{
-    const uint32_t s = d < static_cast<uint32_t>(kEsc) ? d : static_cast<uint32_t>(kEsc);
-    uint32_t code = c_code[s], len = c_len[s];
-    if (s == static_cast<uint32_t>(kEsc)) {
-        code <<= 8;
-        len += 8;
-    }
-    return code | (len << 24) | (s == static_cast<uint32_t>(kEsc) ? 0x80000000u : 0u);
-}
 
 struct EncTables {
     uint32_t esc[256];    // enc_entry(d)
@@ -730,33 +740,41 @@ void zc_compress_kernel(const uint16_t* __restrict__ in, uint8_t* __restrict__ o
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & (kLanes - 1);
     const uint32_t wave = tid / kLanes;
-    {
-        const uint32_t e = enc_entry(tid);
-        sh.tb.esc[tid] = e;
-        sh.tb.len[tid] = static_cast<uint8_t>((e >> 24) & 31);
-        const uint32_t s = tid < static_cast<uint32_t>(kEsc) ? tid : static_cast<uint32_t>(kEsc);
-        sh.tb.code[tid] = static_cast<uint16_t>(c_code[s]);
-    }
-    for (uint32_t i = tid * 4; i < static_cast<uint32_t>(kEncStage); i += kBlock * 4)
-        *reinterpret_cast<uint4*>(&sh.stage[i]) = make_uint4(0, 0, 0, 0);
 
     // The workgroup's chunk comes from its position in the grid: round-robin
     // over the chunks when they all have the same number of tiles, so that
     // few tiles of one chunk are in flight at once; chunk by chunk otherwise.
-    // Its tile within the chunk comes from that chunk's ticket counter, so a
-    // tile only waits for lower tickets of its chunk, held by workgroups that
-    // are already running.
+    // With equal chunks its tile within the chunk comes from that chunk's
+    // ticket counter (requested first, so that the round trip overlaps the
+    // table set-up), and a tile only waits for lower tickets of its chunk,
+    // held by workgroups that are already running.
     const uint32_t item = blockIdx.x;
     TileCtx x;
     if (ZC_ENC_INTERLEAVE && tab.uniform_tiles)
         x.c = static_cast<int>(item % static_cast<uint32_t>(tab.nchunks));
     else
         x.c = find_chunk(tab, item);
+    uint32_t ticket = 0;
+    if (!tab.grid_order && tid == 0)
+        ticket = atomicAdd(&tickets[x.c * kTicketStride], 1u);
+    {
+        const uint32_t s = tid < static_cast<uint32_t>(kEsc) ? tid : static_cast<uint32_t>(kEsc);
+        uint32_t code = c_code[s], len = c_len[s];
+        sh.tb.code[tid] = static_cast<uint16_t>(code);
+        if (s == static_cast<uint32_t>(kEsc)) {   // escape: code word, then 8 exponent bits
+            code <<= 8;
+            len += 8;
+        }
+        sh.tb.esc[tid] = code | (len << 24) | (s == static_cast<uint32_t>(kEsc) ? 0x80000000u : 0u);
+        sh.tb.len[tid] = static_cast<uint8_t>(len);
+    }
+    for (uint32_t i = tid * 4; i < static_cast<uint32_t>(kEncStage); i += kBlock * 4)
+        *reinterpret_cast<uint4*>(&sh.stage[i]) = make_uint4(0, 0, 0, 0);
     if (tid == 0)
         sh.spin_limit = tab.spin_limit;
     if (!tab.grid_order) {
         if (tid == 0)
-            sh.tile = atomicAdd(&tickets[x.c * kTicketStride], 1u);
+            sh.tile = ticket;
         __syncthreads();
         x.t = sh.tile;
     } else {
@@ -1072,13 +1090,32 @@ __device__ inline void decode_all_raw(const uint32_t* __restrict__ gstream,
     }
 }
 
+// A tile's header word, offsets and group metadata, loaded together (only
+// once the chunk's readable bytes are known to hold its index arrays).
+struct TileMeta {
+    uint32_t hw, toff, tnext, emax, glen;
+};
+
+__device__ inline TileMeta load_meta(const uint8_t* __restrict__ src, const Geom& G, uint32_t t,
+                                     uint32_t lane)
+{
+    TileMeta m;
+    m.hw = lane < 8 ? reinterpret_cast<const uint32_t*>(src)[lane] : 0u;
+    const uint32_t* toffs = reinterpret_cast<const uint32_t*>(src + 32);
+    m.toff = toffs[t];
+    m.tnext = (t + 1 < G.T) ? toffs[t + 1] : 0u;
+    m.emax = src[32 + 4ull * G.T + 64ull * t + lane];
+    m.glen = *reinterpret_cast<const uint16_t*>(src + 32 + 68ull * G.T + 2ull * (64ull * t + lane));
+    return m;
+}
+
 template <bool FULL>
 __device__ void decompress_tile(const uint8_t* __restrict__ src, uint16_t* __restrict__ dst,
                                 int32_t* __restrict__ status, int c, uint32_t n, uint32_t t,
                                 uint64_t bavail, uint32_t lane, uint32_t* __restrict__ s,
                                 const uint8_t* __restrict__ s_lut8,
                                 const uint16_t* __restrict__ s_tail,
-                                const uint8_t* __restrict__ s_len)
+                                const uint8_t* __restrict__ s_len, const TileMeta& meta)
 {
     const Geom G = geometry(n);
     const uint32_t base = t * kTile;
@@ -1089,15 +1126,8 @@ __device__ void decompress_tile(const uint8_t* __restrict__ src, uint16_t* __res
             report(status, ZC_REASON_SIZE, c);
         return;
     }
-
-    // header, tile offsets and group metadata, all loaded at once
-    const uint32_t hw = lane < 8 ? reinterpret_cast<const uint32_t*>(src)[lane] : 0u;
-    const uint32_t* toffs = reinterpret_cast<const uint32_t*>(src + 32);
-    const uint32_t toff = toffs[t];
-    const uint32_t tnext = (t + 1 < G.T) ? toffs[t + 1] : 0u;
-    const uint32_t emax = src[32 + 4ull * G.T + 64ull * t + lane];
-    const uint32_t glen =
-        *reinterpret_cast<const uint16_t*>(src + 32 + 68ull * G.T + 2ull * (64ull * t + lane));
+    const uint32_t hw = meta.hw, toff = meta.toff, tnext = meta.tnext, emax = meta.emax,
+                   glen = meta.glen;
 
     const uint32_t h0 = __shfl(hw, 0), h1 = __shfl(hw, 1), h2 = __shfl(hw, 2),
                    h3 = __shfl(hw, 3), h4 = __shfl(hw, 4), h5 = __shfl(hw, 5),
@@ -1204,9 +1234,9 @@ __device__ __attribute__((noinline)) void decompress_tile_partial(
     const uint8_t* __restrict__ src, uint16_t* __restrict__ dst, int32_t* __restrict__ status,
     int c, uint32_t n, uint32_t t, uint64_t bavail, uint32_t lane, uint32_t* __restrict__ s,
     const uint8_t* __restrict__ s_lut8, const uint16_t* __restrict__ s_tail,
-    const uint8_t* __restrict__ s_len)
+    const uint8_t* __restrict__ s_len, TileMeta meta)
 {
-    decompress_tile<false>(src, dst, status, c, n, t, bavail, lane, s, s_lut8, s_tail, s_len);
+    decompress_tile<false>(src, dst, status, c, n, t, bavail, lane, s, s_lut8, s_tail, s_len, meta);
 }
 
 __global__ __launch_bounds__(kBlock, kMinWavesDec)
@@ -1220,24 +1250,37 @@ void zc_decompress_kernel(const uint8_t* __restrict__ in, uint16_t* __restrict__
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & (kLanes - 1);
-    const uint32_t wave = tid / kLanes;
-    for (uint32_t i = tid; i < (1u << kLutBits) / 16; i += kBlock)
-        reinterpret_cast<uint4*>(s_lut8)[i] = reinterpret_cast<const uint4*>(c_lut)[i];
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kLanes);
+    // The first-level table is the only one read from memory: its load is
+    // issued first and written to LDS just before the barrier, after this
+    // wave's chunk lookup (scalar loads) and tile metadata loads.
+    const uint4 lut_part = reinterpret_cast<const uint4*>(c_lut)[tid];
     // raw groups: 8 bits b decode to 255 - b
     s_lut8[kLutRaw + tid] = static_cast<uint8_t>(255u - tid);
     if (tid < (1u << kTailBits))
-        s_tail[tid] = c_tail[tid];
+        s_tail[tid] = static_cast<uint16_t>(tail_of(tid));
     {
         const uint32_t s = tid < static_cast<uint32_t>(kEsc) ? tid : static_cast<uint32_t>(kEsc);
-        s_len[tid] = static_cast<uint8_t>(c_len[s] + (s == static_cast<uint32_t>(kEsc) ? 8 : 0));
+        s_len[tid] = static_cast<uint8_t>(len_of(s) + (s == static_cast<uint32_t>(kEsc) ? 8 : 0));
     }
+    const uint32_t item = blockIdx.x * kWaves + wave;
+    const bool live = item < tab.nitems;
+    int c = 0;
+    uint32_t n = 0, t = 0;
+    TileMeta meta = {0, 0, 0, 0, 0};
+    if (live) {
+        c = find_chunk(tab, item);
+        n = tab.n[c];
+        t = item - tab.item_begin[c];
+        const Geom G = geometry(n);
+        if (n != 0 && G.X <= tab.bavail[c])
+            meta = load_meta(in + tab.boff[c], G, t, lane);
+    }
+    reinterpret_cast<uint4*>(s_lut8)[tid] = lut_part;
     __syncthreads();
 
-    const uint32_t item = blockIdx.x * kWaves + wave;
-    if (item >= tab.nitems)
+    if (!live)
         return;
-    const int c = find_chunk(tab, item);
-    const uint32_t n = tab.n[c];
     if (n == 0) {
         // a header-only stream
         const uint8_t* src = in + tab.boff[c];
@@ -1246,16 +1289,15 @@ void zc_decompress_kernel(const uint8_t* __restrict__ in, uint16_t* __restrict__
             report(status, ZC_REASON_HEADER, c);
         return;
     }
-    const uint32_t t = item - tab.item_begin[c];
     const uint8_t* src = in + tab.boff[c];
     uint16_t* dst = out + tab.voff[c];
     const uint32_t rem = min(n - t * kTile, static_cast<uint32_t>(kTile));
     if (rem == kTile)
         decompress_tile<true>(src, dst, status, c, n, t, tab.bavail[c], lane, s_stage[wave],
-                              s_lut8, s_tail, s_len);
+                              s_lut8, s_tail, s_len, meta);
     else
         decompress_tile_partial(src, dst, status, c, n, t, tab.bavail[c], lane, s_stage[wave],
-                                s_lut8, s_tail, s_len);
+                                s_lut8, s_tail, s_len, meta);
 }
 
 // ------------------------------------------------------------ host side
