@@ -928,23 +928,25 @@ struct DecState {
 };
 
 // Decodes the 128 members of this lane's group from a window source and
-// writes the values.
-template <bool FULL, int kSym, class Win>
+// writes the values.  MIXED: the wave has raw groups (otherwise the lookup
+// parameters are constants).
+template <bool FULL, int kSym, bool MIXED, class Win>
 __device__ inline void decode_group(const Win& win, const uint8_t* __restrict__ s_lut8,
                                     const uint16_t* __restrict__ s_tail,
                                     const uint8_t* __restrict__ s_len, const uint8_t* __restrict__ rsrc,
                                     uint16_t* __restrict__ dst, uint32_t n, uint32_t base,
                                     uint32_t lane, uint32_t ng, uint32_t emax, bool raw_mode,
-                                    bool any_raw, bool vec_out, DecState& st)
+                                    bool vec_out, DecState& st)
 {
+    const bool raw = MIXED && raw_mode;
     LaneCode q;
-    q.ish = raw_mode ? 24u : static_cast<uint32_t>(32 - kLutBits);
-    q.base = raw_mode ? static_cast<uint32_t>(kLutRaw) : 0u;
-    q.sym_sh = raw_mode ? 0u : 4u;
-    q.smask = raw_mode ? 0u : 15u;
-    q.sor = raw_mode ? 8u : 0u;
-    q.lmark = raw_mode ? 256u : 0u;
-    q.emax_eff = raw_mode ? 255u : emax;
+    q.ish = raw ? 24u : static_cast<uint32_t>(32 - kLutBits);
+    q.base = raw ? static_cast<uint32_t>(kLutRaw) : 0u;
+    q.sym_sh = raw ? 0u : 4u;
+    q.smask = raw ? 0u : 15u;
+    q.sor = raw ? 8u : 0u;
+    q.lmark = raw ? 256u : 0u;
+    q.emax_eff = raw ? 255u : emax;
 
     // sign+mantissa bytes, prefetched three steps ahead
     const uint2* rsrc2 = reinterpret_cast<const uint2*>(rsrc + base) + lane;
@@ -1011,7 +1013,7 @@ __device__ inline void decode_group(const Win& win, const uint8_t* __restrict__ 
                 if (static_cast<uint32_t>(k * 8 + j) < ng)
                     st.seen_max = max(st.seen_max, e8[j]);
         }
-        if (any_raw) {
+        if (MIXED) {
             // a raw group must not have been codable in fewer bits
             if (raw_mode) {
 #pragma unroll
@@ -1199,15 +1201,25 @@ __device__ void decompress_tile(const uint8_t* __restrict__ src, uint16_t* __res
         wave_lds_sync();
         // 8 symbols per window unless a coded group of the tile averages
         // more than 5 bits per value (its windows would often overrun)
-        if (__ballot(!raw_mode && glen > 5 * ng) == 0)
-            decode_group<FULL, 8>(LdsWindow{s, tile_words}, s_lut8, s_tail, s_len, rsrc, dst, n,
-                                  base, lane, ng, emax, raw_mode, raw_lanes != 0, vec_out, st);
-        else
-            decode_group<FULL, 4>(LdsWindow{s, tile_words}, s_lut8, s_tail, s_len, rsrc, dst, n,
-                                  base, lane, ng, emax, raw_mode, raw_lanes != 0, vec_out, st);
+        const LdsWindow lw{s, tile_words};
+        if (__ballot(!raw_mode && glen > 5 * ng) == 0) {
+            if (raw_lanes == 0)
+                decode_group<FULL, 8, false>(lw, s_lut8, s_tail, s_len, rsrc, dst, n, base, lane,
+                                             ng, emax, raw_mode, vec_out, st);
+            else
+                decode_group<FULL, 8, true>(lw, s_lut8, s_tail, s_len, rsrc, dst, n, base, lane,
+                                            ng, emax, raw_mode, vec_out, st);
+        } else {
+            if (raw_lanes == 0)
+                decode_group<FULL, 4, false>(lw, s_lut8, s_tail, s_len, rsrc, dst, n, base, lane,
+                                             ng, emax, raw_mode, vec_out, st);
+            else
+                decode_group<FULL, 4, true>(lw, s_lut8, s_tail, s_len, rsrc, dst, n, base, lane,
+                                            ng, emax, raw_mode, vec_out, st);
+        }
     } else {
-        decode_group<FULL, 4>(GlobalWindow{gstream, tile_words}, s_lut8, s_tail, s_len, rsrc, dst,
-                              n, base, lane, ng, emax, raw_mode, raw_lanes != 0, vec_out, st);
+        decode_group<FULL, 4, true>(GlobalWindow{gstream, tile_words}, s_lut8, s_tail, s_len, rsrc,
+                                    dst, n, base, lane, ng, emax, raw_mode, vec_out, st);
     }
     if (err == 0 && ng > 0) {
         if (st.pos != off + glen)
