@@ -661,6 +661,7 @@ __device__ void compress_tile_back(const TileCtx& x, uint32_t (&dd)[kQSteps][2],
         pre = 8 * min(ng, first);
     uint32_t tile_bits;
     const uint32_t off = wave_excl_scan(glen, lane, &tile_bits);
+    tile_bits = __builtin_amdgcn_readfirstlane(tile_bits);
     const uint32_t tile_words = (tile_bits + 31) >> 5;
     const uint32_t tile_bytes = tile_words * 4;
     uint64_t poll = 0;
@@ -776,7 +777,7 @@ void zc_compress_kernel(const uint16_t* __restrict__ in, uint8_t* __restrict__ o
         if (tid == 0)
             sh.tile = ticket;
         __syncthreads();
-        x.t = sh.tile;
+        x.t = __builtin_amdgcn_readfirstlane(sh.tile);
     } else {
         x.t = item - tab.item_begin[x.c];
     }
