@@ -158,6 +158,9 @@ def main():
                     help="CPU seconds (summed over threads) of the oracle run")
     ap.add_argument("--copies", type=int, default=3,
                     help="timed plain device copies of the input after the steps")
+    ap.add_argument("--device-counts", action="store_true",
+                    help="time zc_compress_dev / zc_decompress_dev, with the chunk "
+                         "counts in device memory (the MoE router's split)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -177,10 +180,17 @@ def main():
     n = int(counts.sum())
     in_bytes = 2 * n
     x = torch.from_numpy(w.view(np.int16)).to(dev)
-    cap = zc.zc_bound(counts)
+    if args.device_counts:
+        cap = zc.zc_bound_max(n, len(counts))
+        wsb = zc.zc_workspace_bytes_max(n, len(counts))
+    else:
+        cap = zc.zc_bound(counts)
+        wsb = zc.zc_workspace_bytes(counts)
     buf = torch.empty(cap, dtype=torch.uint8, device=dev)
     sizes = torch.empty(len(counts), dtype=torch.int64, device=dev)
-    ws = torch.empty(zc.zc_workspace_bytes(counts), dtype=torch.uint8, device=dev)
+    slots = torch.empty(len(counts), dtype=torch.int64, device=dev)
+    dcounts = torch.from_numpy(np.asarray(counts, np.int64)).to(dev)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     y = torch.empty(n, dtype=torch.int16, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -193,13 +203,19 @@ def main():
         flush.fill_(i & 0xFF)
         e0, e1, e2, e3 = ev(), ev(), ev(), ev()
         e0.record(stream)
-        r = zc.zc_compress(x, counts, buf, sizes, ws, stream=stream)
+        if args.device_counts:
+            r = zc.zc_compress_dev(x, dcounts, n, buf, sizes, slots, ws, stream=stream)
+        else:
+            r = zc.zc_compress(x, counts, buf, sizes, ws, stream=stream)
         e1.record(stream)
         if r != zc.ZC_OK:
             raise zc.ZcError(r, "zc_compress")
         flush.fill_((i + 1) & 0xFF)
         e2.record(stream)
-        r = zc.zc_decompress(buf, counts, y, status, stream=stream)
+        if args.device_counts:
+            r = zc.zc_decompress_dev(buf, dcounts, n, y, status, ws, stream=stream)
+        else:
+            r = zc.zc_decompress(buf, counts, y, status, stream=stream)
         e3.record(stream)
         if r != zc.ZC_OK:
             raise zc.ZcError(r, "zc_decompress")
@@ -253,7 +269,8 @@ def main():
     alg_d = alg_bytes / d_mean / 1e9
     dom = "decompress" if d_mean >= c_mean else "compress"
     achieved = alg_d if dom == "decompress" else alg_c
-    traffic = read_traffic(synth.NAMES[args.workload])
+    # the counter summaries cover the host-count kernels only
+    traffic = None if args.device_counts else read_traffic(synth.NAMES[args.workload])
     dom_traffic = traffic.get(KERNEL_NAMES[dom]) if traffic else None
 
     line = {
@@ -275,8 +292,9 @@ def main():
             "chunks": int(len(counts)),
             "bytes_in": in_bytes,
             "seed": seed,
-            "step": "zc_compress + zc_decompress of every chunk, "
-                    "1 GiB cache flush before each call (untimed)",
+            "step": ("zc_compress_dev + zc_decompress_dev (counts in device memory)"
+                     if args.device_counts else "zc_compress + zc_decompress") +
+                    " of every chunk, 1 GiB cache flush before each call (untimed)",
         },
         "compress_GBps": round(comp_gbps, 2),
         "decompress_GBps": round(dec_gbps, 2),

@@ -143,6 +143,71 @@ int zc_decompress(const void* d_in, size_t in_bytes,
 #define ZC_REASON_RAWMODE 10  /* raw group whose coded form is shorter     */
 #define ZC_REASON_PADDING 11  /* nonzero pad bit                           */
 
+/*
+ * Device-resident split.  In an MoE all-to-all the per-destination counts
+ * come out of the router on the GPU (pith.science, Figure 2: the All-to-All;
+ * Figure 8: unevenly loaded experts).  These calls take the counts (and, for
+ * decoding, the stream offsets) in device memory, so no host synchronisation
+ * sits between the router and the codec.  The host gives only the number of
+ * chunks and the total number of values, which fix the launch sizes and the
+ * capacity bounds.  A one-wave planning kernel builds, on the device, the
+ * chunk table the host calls build from host counts; the codec kernels are
+ * the same, so the streams are byte-identical to zc_compress's.
+ */
+
+/*
+ * The largest zc_bound over every split of total_values values into
+ * num_chunks chunks: 2 t + 200 (floor(t / 8192) + C) + 317 C for t values
+ * and C chunks.  Host only; 0 if an argument is invalid (negative, or
+ * values without chunks).
+ */
+size_t zc_bound_max(int64_t total_values, int32_t num_chunks);
+
+/*
+ * Device workspace bytes that zc_compress_dev and zc_decompress_dev need for
+ * any split of total_values values into num_chunks chunks.  Host only; 0 if
+ * an argument is invalid.
+ */
+size_t zc_workspace_bytes_max(int64_t total_values, int32_t num_chunks);
+
+/*
+ * zc_compress with the counts in device memory.
+ *   d_counts      device int64[num_chunks], 8-byte aligned: values per chunk,
+ *                 each in 0 .. ZC_MAX_CHUNK_VALUES, summing to total_values
+ *   d_slot_off    device int64[num_chunks], written: the byte offset of chunk
+ *                 c's stream in d_out (the slot layout of those counts)
+ *   d_out         out_capacity >= zc_bound_max(total_values, num_chunks)
+ *   d_ws          256-byte aligned, ws_bytes >= zc_workspace_bytes_max(...),
+ *                 contents need not be initialised
+ *   other arguments as zc_compress.
+ * The counts are checked on the device.  If they are out of range or do not
+ * sum to total_values, nothing is compressed and every d_comp_sizes and
+ * d_slot_off entry of the affected launch (up to 64 chunks) is -1.
+ * Returns as zc_compress.
+ */
+int zc_compress_dev(const uint16_t* d_in, const int64_t* d_counts,
+                    int32_t num_chunks, int64_t total_values, void* d_out,
+                    size_t out_capacity, int64_t* d_comp_sizes,
+                    int64_t* d_slot_off, void* d_ws, size_t ws_bytes,
+                    void* stream);
+
+/*
+ * zc_decompress with the counts and offsets in device memory.
+ *   d_in_offsets  device int64[num_chunks], 8-byte aligned: byte offset of
+ *                 stream c in d_in (16-byte aligned), for example the
+ *                 d_slot_off of zc_compress_dev; or NULL for the slot layout
+ *   d_counts      device int64[num_chunks], summing to total_values
+ *   d_ws          256-byte aligned, ws_bytes >= zc_workspace_bytes_max(...)
+ *   other arguments as zc_decompress.
+ * Counts or offsets that are out of range record ZC_REASON_SIZE in
+ * *d_status and decode nothing of the affected launch.
+ */
+int zc_decompress_dev(const void* d_in, size_t in_bytes,
+                      const int64_t* d_in_offsets, const int64_t* d_counts,
+                      int32_t num_chunks, int64_t total_values,
+                      uint16_t* d_out, int32_t* d_status, void* d_ws,
+                      size_t ws_bytes, void* stream);
+
 /* Static text for a zc_status_t value. */
 const char* zc_strerror(int code);
 

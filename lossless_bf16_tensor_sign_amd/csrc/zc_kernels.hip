@@ -155,6 +155,7 @@ struct Geom {
 };
 
 __host__ __device__ inline uint64_t align16(uint64_t x) { return (x + 15) & ~uint64_t(15); }
+__host__ __device__ inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 __host__ __device__ inline Geom geometry(uint64_t n)
 {
@@ -730,11 +731,12 @@ __device__ __attribute__((noinline)) void compress_tile_partial(
     compress_tile_back<false>(x, dd, comp_sizes, status, *sh);
 }
 
-__global__ __launch_bounds__(kBlock, kMinWavesEnc)
-void zc_compress_kernel(const uint16_t* __restrict__ in, uint8_t* __restrict__ out,
-                        int64_t* __restrict__ comp_sizes,
-                        uint64_t* __restrict__ status, uint32_t* __restrict__ tickets,
-                        ChunkTable tab)
+__device__ __forceinline__ void compress_body(const uint16_t* __restrict__ in,
+                                              uint8_t* __restrict__ out,
+                                              int64_t* __restrict__ comp_sizes,
+                                              uint64_t* __restrict__ status,
+                                              uint32_t* __restrict__ tickets,
+                                              const ChunkTable& tab)
 {
     __shared__ __align__(16) EncShared sh;
 
@@ -809,6 +811,29 @@ void zc_compress_kernel(const uint16_t* __restrict__ in, uint8_t* __restrict__ o
         compress_tile_partial(x.src, x.dst, x.n, x.t, x.item, x.first, lane, wave, x.c,
                               comp_sizes, status, &sh);
     }
+}
+
+__global__ __launch_bounds__(kBlock, kMinWavesEnc)
+void zc_compress_kernel(const uint16_t* __restrict__ in, uint8_t* __restrict__ out,
+                        int64_t* __restrict__ comp_sizes,
+                        uint64_t* __restrict__ status, uint32_t* __restrict__ tickets,
+                        ChunkTable tab)
+{
+    compress_body(in, out, comp_sizes, status, tickets, tab);
+}
+
+// The same with the chunk table in device memory (built on the device from
+// device-resident counts); the grid is an upper bound on the tile count and
+// workgroups past the table's tiles return at once.
+__global__ __launch_bounds__(kBlock, kMinWavesEnc)
+void zc_compress_dev_kernel(const uint16_t* __restrict__ in, uint8_t* __restrict__ out,
+                            int64_t* __restrict__ comp_sizes,
+                            uint64_t* __restrict__ status, uint32_t* __restrict__ tickets,
+                            const ChunkTable* __restrict__ tab)
+{
+    if (blockIdx.x >= tab->nitems)
+        return;
+    compress_body(in, out, comp_sizes, status, tickets, *tab);
 }
 
 // ------------------------------------------------------------ decompress
@@ -1252,9 +1277,10 @@ __device__ __attribute__((noinline)) void decompress_tile_partial(
     decompress_tile<false>(src, dst, status, c, n, t, bavail, lane, s, s_lut8, s_tail, s_len, meta);
 }
 
-__global__ __launch_bounds__(kBlock, kMinWavesDec)
-void zc_decompress_kernel(const uint8_t* __restrict__ in, uint16_t* __restrict__ out,
-                          int32_t* __restrict__ status, ChunkTable tab)
+__device__ __forceinline__ void decompress_body(const uint8_t* __restrict__ in,
+                                                uint16_t* __restrict__ out,
+                                                int32_t* __restrict__ status,
+                                                const ChunkTable& tab)
 {
     __shared__ __align__(16) uint32_t s_stage[kWaves][kStageAlloc];
     __shared__ __align__(16) uint8_t s_lut8[kLutRaw + 256];
@@ -1313,6 +1339,131 @@ void zc_decompress_kernel(const uint8_t* __restrict__ in, uint16_t* __restrict__
                                 s_lut8, s_tail, s_len, meta);
 }
 
+__global__ __launch_bounds__(kBlock, kMinWavesDec)
+void zc_decompress_kernel(const uint8_t* __restrict__ in, uint16_t* __restrict__ out,
+                          int32_t* __restrict__ status, ChunkTable tab)
+{
+    decompress_body(in, out, status, tab);
+}
+
+// The same with the chunk table in device memory; waves past the table's
+// tiles pass the table barrier and return.
+__global__ __launch_bounds__(kBlock, kMinWavesDec)
+void zc_decompress_dev_kernel(const uint8_t* __restrict__ in, uint16_t* __restrict__ out,
+                              int32_t* __restrict__ status, const ChunkTable* __restrict__ tab)
+{
+    decompress_body(in, out, status, *tab);
+}
+
+// ------------------------------------------------------------ device-resident split
+
+__device__ inline uint64_t wave_excl_scan64(uint64_t x, uint32_t lane, uint64_t* total)
+{
+    uint64_t incl = x;
+#pragma unroll
+    for (int o = 1; o < kLanes; o <<= 1) {
+        const uint64_t y = __shfl_up(incl, o);
+        if (lane >= static_cast<uint32_t>(o))
+            incl += y;
+    }
+    *total = __shfl(incl, kLanes - 1);
+    return incl - x;
+}
+
+__device__ inline uint64_t wave_sum64(uint64_t x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        x += __shfl_xor(x, o);
+    return x;
+}
+
+// Builds the chunk table of one launch (chunks c0 .. c0 + m - 1 of
+// num_chunks) in device memory from counts that live on the device: the
+// same table the host builds from host counts.  One wave; lane c handles
+// chunk c0 + c.  The whole split is checked first: every count within
+// 0 .. ZC_MAX_CHUNK_VALUES and their sum equal to `total` (and, when
+// decoding from explicit offsets, each offset 16-byte aligned with a header's
+// room in the input).  An invalid split leaves a table without tiles, so the
+// codec kernels that follow do nothing, and is reported: compress writes -1
+// to the launch's comp_sizes and slot_off entries, decompress records
+// ZC_REASON_SIZE in *status.
+__global__ __launch_bounds__(kLanes)
+void zc_plan_kernel(const int64_t* __restrict__ counts, int32_t num_chunks, int32_t c0, int32_t m,
+                    int64_t total, const int64_t* __restrict__ in_offsets, uint64_t in_bytes,
+                    uint32_t max_items, uint32_t spin_limit, int32_t decode,
+                    ChunkTable* __restrict__ tab, int64_t* __restrict__ slot_off,
+                    int64_t* __restrict__ comp_sizes, int32_t* __restrict__ status)
+{
+    const uint32_t lane = threadIdx.x;
+    uint64_t sum = 0, slot_before = 0, voff_before = 0;
+    bool bad = false;
+    for (int32_t c = static_cast<int32_t>(lane); c < num_chunks; c += kLanes) {
+        const int64_t n = counts[c];
+        if (n < 0 || n > ZC_MAX_CHUNK_VALUES) {
+            bad = true;
+            continue;
+        }
+        sum += static_cast<uint64_t>(n);
+        if (c < c0) {
+            slot_before += align256(chunk_bound(static_cast<uint64_t>(n)));
+            voff_before += static_cast<uint64_t>(n);
+        }
+    }
+    sum = wave_sum64(sum);
+    slot_before = wave_sum64(slot_before);
+    voff_before = wave_sum64(voff_before);
+    bad = __ballot(bad) != 0 || total < 0 || sum != static_cast<uint64_t>(total);
+
+    const bool mine = lane < static_cast<uint32_t>(m);
+    const uint64_t n = (mine && !bad) ? static_cast<uint64_t>(counts[c0 + lane]) : 0u;
+    const uint32_t T = static_cast<uint32_t>((n + kTile - 1) / kTile);
+    const uint32_t items_c = mine ? (T ? T : 1u) : 0u;
+    uint32_t items;
+    const uint32_t ibegin = wave_excl_scan(items_c, lane, &items);
+    uint64_t vtotal, stotal;
+    const uint64_t voff = voff_before + wave_excl_scan64(n, lane, &vtotal);
+    const uint64_t slot = slot_before +
+                          wave_excl_scan64(mine ? align256(chunk_bound(n)) : 0u, lane, &stotal);
+    uint64_t boff = slot;
+    if (decode && in_offsets && mine) {
+        const int64_t o = in_offsets[c0 + lane];
+        boff = static_cast<uint64_t>(o);
+        if (o < 0 || (o & 15) || static_cast<uint64_t>(o) + 32 > in_bytes)
+            bad = true;
+    } else if (decode && mine && boff + 32 > in_bytes) {
+        bad = true;
+    }
+    bad = __ballot(bad) != 0 || items > max_items;
+
+    // equal chunks (all non-empty with the same tile count) are interleaved
+    const uint32_t first_items = __shfl(items_c, 0);
+    const bool same = !mine || (items_c == first_items && n > 0);
+    const uint32_t uniform = (__ballot(!same) == 0 && m > 0) ? first_items : 0u;
+    if (mine) {
+        tab->item_begin[lane] = ibegin;
+        tab->n[lane] = static_cast<uint32_t>(n);
+        tab->voff[lane] = voff;
+        tab->boff[lane] = boff;
+        tab->bavail[lane] = in_bytes > boff ? in_bytes - boff : 0u;
+        if (!decode) {
+            slot_off[c0 + lane] = bad ? -1 : static_cast<int64_t>(boff);
+            if (bad)
+                comp_sizes[c0 + lane] = -1;
+        }
+    }
+    if (lane == 0) {
+        tab->item_begin[m] = items;
+        tab->nchunks = m;
+        tab->nitems = bad ? 0u : items;
+        tab->uniform_tiles = uniform;
+        tab->grid_order = (ZC_ENC_INTERLEAVE && uniform) ? 0u : 1u;
+        tab->spin_limit = spin_limit;
+        if (decode && bad && status)
+            atomicCAS(status, 0, (ZC_REASON_SIZE << 24) | (c0 & 0xFFFFFF));
+    }
+}
+
 // ------------------------------------------------------------ host side
 
 struct Counts {
@@ -1337,7 +1488,6 @@ Counts check_counts(const int64_t* counts, int32_t num_chunks)
     return r;
 }
 
-uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 // Look-back polls a tile makes before it recomputes a missing predecessor's
 // size from the input.  The environment variable ZC_LOOKBACK_SPIN_LIMIT
@@ -1354,6 +1504,33 @@ uint32_t lookback_spin_limit()
 
 constexpr size_t kWsHeader = kMaxChunks * kTicketStride * 4;   // per-chunk ticket counters
 
+
+}  // namespace
+
+namespace {
+
+// ---- device-resident split: bounds and workspace layout
+
+// Tiles of one launch of m chunks holding at most `total` values:
+// sum of max(1, ceil(n_c / 8192)) <= floor(total / 8192) + m.
+uint64_t dev_max_items(int64_t total, int32_t m)
+{
+    return static_cast<uint64_t>(total) / kTile + static_cast<uint64_t>(m);
+}
+
+bool dev_args_ok(int64_t total, int32_t num_chunks)
+{
+    return num_chunks >= 0 && total >= 0 && (num_chunks > 0 || total == 0) &&
+           dev_max_items(total, num_chunks < kMaxChunks ? num_chunks : kMaxChunks) < (1ull << 31);
+}
+
+// Workspace layout of the device-split calls: ticket counters, look-back
+// status words for the largest launch, then one chunk table per launch.
+uint64_t dev_tables_offset(int64_t total, int32_t num_chunks)
+{
+    const int32_t m = num_chunks < kMaxChunks ? num_chunks : kMaxChunks;
+    return align256(kWsHeader + 8ull * kStatusStride * dev_max_items(total, m));
+}
 
 }  // namespace
 
@@ -1457,6 +1634,107 @@ int zc_compress(const uint16_t* d_in, const int64_t* counts, int32_t num_chunks,
                            status, items);
         hipLaunchKernelGGL(zc_compress_kernel, dim3(items), dim3(kBlock), 0, s, d_in,
                            out, d_comp_sizes + c0, status, ticket, tab);
+        if (hipGetLastError() != hipSuccess)
+            return ZC_EHIP;
+    }
+    return ZC_OK;
+}
+
+size_t zc_bound_max(int64_t total_values, int32_t num_chunks)
+{
+    if (!dev_args_ok(total_values, num_chunks))
+        return 0;
+    // per chunk: align256(bound(n)) <= 317 + 200 T + 2n, and the T sum to at
+    // most floor(total / 8192) + num_chunks
+    const uint64_t t = static_cast<uint64_t>(total_values), c = static_cast<uint64_t>(num_chunks);
+    return static_cast<size_t>(2 * t + 200 * (t / kTile + c) + 317 * c);
+}
+
+size_t zc_workspace_bytes_max(int64_t total_values, int32_t num_chunks)
+{
+    if (!dev_args_ok(total_values, num_chunks))
+        return 0;
+    const uint64_t launches = (static_cast<uint64_t>(num_chunks) + kMaxChunks - 1) / kMaxChunks;
+    return static_cast<size_t>(dev_tables_offset(total_values, num_chunks) +
+                               launches * align256(sizeof(ChunkTable)));
+}
+
+int zc_compress_dev(const uint16_t* d_in, const int64_t* d_counts, int32_t num_chunks,
+                    int64_t total_values, void* d_out, size_t out_capacity,
+                    int64_t* d_comp_sizes, int64_t* d_slot_off, void* d_ws, size_t ws_bytes,
+                    void* stream)
+{
+    if (!dev_args_ok(total_values, num_chunks))
+        return ZC_EINVAL;
+    if (num_chunks == 0)
+        return ZC_OK;
+    if (!d_counts || !d_out || !d_comp_sizes || !d_slot_off || !d_ws || (total_values && !d_in))
+        return ZC_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(d_out) & 15) || (reinterpret_cast<uintptr_t>(d_in) & 1)
+        || (reinterpret_cast<uintptr_t>(d_ws) & 255) || (reinterpret_cast<uintptr_t>(d_counts) & 7)
+        || (reinterpret_cast<uintptr_t>(d_comp_sizes) & 7) || (reinterpret_cast<uintptr_t>(d_slot_off) & 7))
+        return ZC_EINVAL;
+    if (out_capacity < zc_bound_max(total_values, num_chunks))
+        return ZC_ENOSPC;
+    if (ws_bytes < zc_workspace_bytes_max(total_values, num_chunks))
+        return ZC_ENOSPC;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(d_ws);
+    uint32_t* ticket = reinterpret_cast<uint32_t*>(ws);
+    uint64_t* status = reinterpret_cast<uint64_t*>(ws + kWsHeader);
+    uint8_t* tables = ws + dev_tables_offset(total_values, num_chunks);
+    const uint32_t spin_limit = lookback_spin_limit();
+    for (int32_t c0 = 0, g = 0; c0 < num_chunks; c0 += kMaxChunks, ++g) {
+        const int32_t m = num_chunks - c0 < kMaxChunks ? num_chunks - c0 : kMaxChunks;
+        const uint32_t items = static_cast<uint32_t>(dev_max_items(total_values, m));
+        ChunkTable* tab = reinterpret_cast<ChunkTable*>(tables + g * align256(sizeof(ChunkTable)));
+        const uint32_t twords = static_cast<uint32_t>(kWsHeader / 4);
+        const uint32_t words = items + twords;
+        const uint32_t cblocks = (words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024;
+        hipLaunchKernelGGL(zc_clear_kernel, dim3(cblocks), dim3(256), 0, s, ticket, twords,
+                           status, items);
+        hipLaunchKernelGGL(zc_plan_kernel, dim3(1), dim3(kLanes), 0, s, d_counts, num_chunks, c0, m,
+                           total_values, static_cast<const int64_t*>(nullptr), uint64_t(0), items,
+                           spin_limit, 0, tab, d_slot_off, d_comp_sizes, static_cast<int32_t*>(nullptr));
+        hipLaunchKernelGGL(zc_compress_dev_kernel, dim3(items), dim3(kBlock), 0, s, d_in,
+                           static_cast<uint8_t*>(d_out), d_comp_sizes + c0, status, ticket,
+                           static_cast<const ChunkTable*>(tab));
+        if (hipGetLastError() != hipSuccess)
+            return ZC_EHIP;
+    }
+    return ZC_OK;
+}
+
+int zc_decompress_dev(const void* d_in, size_t in_bytes, const int64_t* d_in_offsets,
+                      const int64_t* d_counts, int32_t num_chunks, int64_t total_values,
+                      uint16_t* d_out, int32_t* d_status, void* d_ws, size_t ws_bytes, void* stream)
+{
+    if (!dev_args_ok(total_values, num_chunks))
+        return ZC_EINVAL;
+    if (num_chunks == 0)
+        return ZC_OK;
+    if (!d_in || !d_counts || !d_status || !d_ws || (total_values && !d_out))
+        return ZC_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(d_in) & 15) || (reinterpret_cast<uintptr_t>(d_out) & 1)
+        || (reinterpret_cast<uintptr_t>(d_status) & 3) || (reinterpret_cast<uintptr_t>(d_ws) & 255)
+        || (reinterpret_cast<uintptr_t>(d_counts) & 7) || (reinterpret_cast<uintptr_t>(d_in_offsets) & 7))
+        return ZC_EINVAL;
+    if (ws_bytes < zc_workspace_bytes_max(total_values, num_chunks))
+        return ZC_ENOSPC;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* tables = static_cast<uint8_t*>(d_ws) + dev_tables_offset(total_values, num_chunks);
+    const uint8_t* in = static_cast<const uint8_t*>(d_in);
+    for (int32_t c0 = 0, g = 0; c0 < num_chunks; c0 += kMaxChunks, ++g) {
+        const int32_t m = num_chunks - c0 < kMaxChunks ? num_chunks - c0 : kMaxChunks;
+        const uint32_t items = static_cast<uint32_t>(dev_max_items(total_values, m));
+        ChunkTable* tab = reinterpret_cast<ChunkTable*>(tables + g * align256(sizeof(ChunkTable)));
+        hipLaunchKernelGGL(zc_plan_kernel, dim3(1), dim3(kLanes), 0, s, d_counts, num_chunks, c0, m,
+                           total_values, d_in_offsets, static_cast<uint64_t>(in_bytes), items, 0u, 1,
+                           tab, static_cast<int64_t*>(nullptr), static_cast<int64_t*>(nullptr), d_status);
+        hipLaunchKernelGGL(zc_decompress_dev_kernel, dim3((items + kWaves - 1) / kWaves), dim3(kBlock),
+                           0, s, in, d_out, d_status, static_cast<const ChunkTable*>(tab));
         if (hipGetLastError() != hipSuccess)
             return ZC_EHIP;
     }

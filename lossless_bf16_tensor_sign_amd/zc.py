@@ -54,6 +54,18 @@ def lib():
                                     ct.c_int32, ct.c_void_p, ct.c_void_p,
                                     ct.c_void_p]
         L.zc_decompress.restype = ct.c_int
+        L.zc_bound_max.argtypes = [ct.c_int64, ct.c_int32]
+        L.zc_bound_max.restype = ct.c_size_t
+        L.zc_workspace_bytes_max.argtypes = [ct.c_int64, ct.c_int32]
+        L.zc_workspace_bytes_max.restype = ct.c_size_t
+        L.zc_compress_dev.argtypes = [ct.c_void_p, ct.c_void_p, ct.c_int32, ct.c_int64,
+                                      ct.c_void_p, ct.c_size_t, ct.c_void_p, ct.c_void_p,
+                                      ct.c_void_p, ct.c_size_t, ct.c_void_p]
+        L.zc_compress_dev.restype = ct.c_int
+        L.zc_decompress_dev.argtypes = [ct.c_void_p, ct.c_size_t, ct.c_void_p, ct.c_void_p,
+                                        ct.c_int32, ct.c_int64, ct.c_void_p, ct.c_void_p,
+                                        ct.c_void_p, ct.c_size_t, ct.c_void_p]
+        L.zc_decompress_dev.restype = ct.c_int
         L.zc_strerror.argtypes = [ct.c_int]
         L.zc_strerror.restype = ct.c_char_p
         L.zc_code_table.argtypes = [ct.c_int32, ct.POINTER(ct.c_int32),
@@ -96,6 +108,14 @@ def zc_workspace_bytes(counts) -> int:
     return int(lib().zc_workspace_bytes(p, len(a)))
 
 
+def zc_bound_max(total_values: int, num_chunks: int) -> int:
+    return int(lib().zc_bound_max(int(total_values), int(num_chunks)))
+
+
+def zc_workspace_bytes_max(total_values: int, num_chunks: int) -> int:
+    return int(lib().zc_workspace_bytes_max(int(total_values), int(num_chunks)))
+
+
 def zc_strerror(code: int) -> str:
     return lib().zc_strerror(int(code)).decode()
 
@@ -136,6 +156,26 @@ def zc_decompress(d_in, counts, d_out, d_status, in_offsets=None,
                                    _ptr(d_status), _stream(stream)))
 
 
+def zc_compress_dev(d_in, d_counts, total_values, d_out, d_comp_sizes, d_slot_off, d_ws,
+                    stream=None, out_capacity=None, ws_bytes=None) -> int:
+    """Queue compression with the counts in a device int64 tensor."""
+    cap = d_out.numel() * d_out.element_size() if out_capacity is None else out_capacity
+    wsb = d_ws.numel() * d_ws.element_size() if ws_bytes is None else ws_bytes
+    return int(lib().zc_compress_dev(_ptr(d_in), _ptr(d_counts), d_counts.numel(),
+                                     int(total_values), _ptr(d_out), cap, _ptr(d_comp_sizes),
+                                     _ptr(d_slot_off), _ptr(d_ws), wsb, _stream(stream)))
+
+
+def zc_decompress_dev(d_in, d_counts, total_values, d_out, d_status, d_ws, d_in_offsets=None,
+                      stream=None, in_bytes=None, ws_bytes=None) -> int:
+    """Queue decompression with the counts (and offsets) in device tensors."""
+    nb = d_in.numel() * d_in.element_size() if in_bytes is None else in_bytes
+    wsb = d_ws.numel() * d_ws.element_size() if ws_bytes is None else ws_bytes
+    return int(lib().zc_decompress_dev(_ptr(d_in), nb, _ptr(d_in_offsets), _ptr(d_counts),
+                                       d_counts.numel(), int(total_values), _ptr(d_out),
+                                       _ptr(d_status), _ptr(d_ws), wsb, _stream(stream)))
+
+
 # ------------------------------------------------ allocating conveniences
 
 def compress(x, counts, stream=None):
@@ -168,5 +208,44 @@ def decompress(buf, counts, in_offsets=None, stream=None, check=True):
         st = int(status.item())
         if st != 0:
             raise ZcError(ZC_ECORRUPT, "zc_decompress: %s in chunk %d"
+                          % (REASONS.get(st >> 24, st >> 24), st & 0xFFFFFF))
+    return out, status
+
+
+def compress_dev(x, d_counts, stream=None):
+    """Compress with the split in a device int64 tensor (no host copy of it).
+
+    Returns (buffer, int64 device sizes, int64 device slot offsets)."""
+    import torch
+    dev = x.device
+    total, nc = x.numel(), d_counts.numel()
+    out = torch.empty(max(zc_bound_max(total, nc), 16), dtype=torch.uint8, device=dev)
+    sizes = torch.empty(max(nc, 1), dtype=torch.int64, device=dev)
+    slots = torch.empty(max(nc, 1), dtype=torch.int64, device=dev)
+    ws = torch.empty(max(zc_workspace_bytes_max(total, nc), 256), dtype=torch.uint8, device=dev)
+    r = zc_compress_dev(x, d_counts, total, out, sizes, slots, ws, stream=stream)
+    if r != ZC_OK:
+        raise ZcError(r, "zc_compress_dev")
+    return out, sizes[:nc], slots[:nc]
+
+
+def decompress_dev(buf, d_counts, total_values, d_in_offsets=None, stream=None, check=True):
+    """Decode with the split (and offsets) in device tensors."""
+    import torch
+    dev = buf.device
+    nc = d_counts.numel()
+    out = torch.empty(max(int(total_values), 1), dtype=torch.int16, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(zc_workspace_bytes_max(total_values, nc), 256), dtype=torch.uint8,
+                     device=dev)
+    r = zc_decompress_dev(buf, d_counts, total_values, out, status, ws, d_in_offsets=d_in_offsets,
+                          stream=stream)
+    if r != ZC_OK:
+        raise ZcError(r, "zc_decompress_dev")
+    out = out[:int(total_values)]
+    if check:
+        st = int(status.item())
+        if st != 0:
+            raise ZcError(ZC_ECORRUPT, "zc_decompress_dev: %s in chunk %d"
                           % (REASONS.get(st >> 24, st >> 24), st & 0xFFFFFF))
     return out, status

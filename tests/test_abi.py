@@ -101,3 +101,66 @@ def test_argument_errors_before_any_gpu_work():
                              ct.c_void_p(0x3000), None) == zc.ZC_EINVAL
     for code in (0, -1, -2, -3, -4):
         assert zc.zc_strerror(code) != "unknown status"
+
+
+def _splits(rng):
+    """Splits of one total into C chunks, including the extreme ones."""
+    for _ in range(30):
+        c = int(rng.integers(1, 200))
+        cnt = rng.integers(0, 60000, size=c)
+        cnt[rng.random(c) < 0.3] = 0
+        yield cnt
+    yield np.array([0] * 64)
+    yield np.array([1] * 200)
+    yield np.array([8193] * 70)
+    yield np.array([(1 << 22) * 3 + 5] + [0] * 63)
+    yield np.array([8192] * 64)
+
+
+def test_bound_max_covers_every_split(oracle):
+    rng = np.random.default_rng(5)
+    for cnt in _splits(rng):
+        total, c = int(cnt.sum()), len(cnt)
+        assert zc.zc_bound_max(total, c) >= oracle.slot_offsets(cnt)[1], cnt
+        # the tiles of any launch (64 chunks) stay within floor(total / 8192) + 64
+        for c0 in range(0, c, 64):
+            part = cnt[c0:c0 + 64]
+            items = int(np.maximum(1, (part + 8191) // 8192).sum())
+            assert items <= total // 8192 + len(part)
+        assert zc.zc_workspace_bytes_max(total, c) >= zc.zc_workspace_bytes(cnt)
+    assert zc.zc_bound_max(0, 0) == 0
+    assert zc.zc_bound_max(5, 0) == 0
+    assert zc.zc_bound_max(-1, 3) == 0
+    assert zc.zc_workspace_bytes_max(10, -1) == 0
+
+
+def test_device_split_argument_errors_before_any_gpu_work():
+    lib = zc.lib()
+    import ctypes as ct
+    V = ct.c_void_p
+    big = 1 << 30
+    # values without chunks, negative totals, null pointers
+    assert lib.zc_compress_dev(V(0x1000), V(0x2000), 0, 10, V(0x3000), big, V(0x4000),
+                               V(0x5000), V(0x6000), big, None) == zc.ZC_EINVAL
+    assert lib.zc_compress_dev(V(0x1000), V(0x2000), 2, -1, V(0x3000), big, V(0x4000),
+                               V(0x5000), V(0x6000), big, None) == zc.ZC_EINVAL
+    assert lib.zc_compress_dev(V(0x1000), None, 2, 10, V(0x3000), big, V(0x4000),
+                               V(0x5000), V(0x6000), big, None) == zc.ZC_EINVAL
+    # misaligned workspace (256 bytes) and counts (8 bytes)
+    assert lib.zc_compress_dev(V(0x1000), V(0x2000), 2, 10, V(0x3000), big, V(0x4000),
+                               V(0x5000), V(0x6010), big, None) == zc.ZC_EINVAL
+    assert lib.zc_compress_dev(V(0x1000), V(0x2004), 2, 10, V(0x3000), big, V(0x4000),
+                               V(0x5000), V(0x6000), big, None) == zc.ZC_EINVAL
+    # capacity and workspace below the bounds for that total
+    assert lib.zc_compress_dev(V(0x1000), V(0x2000), 2, 10, V(0x3000),
+                               zc.zc_bound_max(10, 2) - 1, V(0x4000), V(0x5000), V(0x6000),
+                               big, None) == zc.ZC_ENOSPC
+    assert lib.zc_compress_dev(V(0x1000), V(0x2000), 2, 10, V(0x3000), big, V(0x4000),
+                               V(0x5000), V(0x6000), zc.zc_workspace_bytes_max(10, 2) - 1,
+                               None) == zc.ZC_ENOSPC
+    assert lib.zc_decompress_dev(V(0x1000), 4096, None, V(0x2000), 2, 10, V(0x3000),
+                                 V(0x4000), V(0x5000), 8, None) == zc.ZC_ENOSPC
+    assert lib.zc_decompress_dev(V(0x1008), 4096, None, V(0x2000), 2, 10, V(0x3000),
+                                 V(0x4000), V(0x5000), big, None) == zc.ZC_EINVAL
+    assert lib.zc_compress_dev(None, None, 0, 0, None, 0, None, None, None, 0,
+                               None) == zc.ZC_OK

@@ -215,6 +215,104 @@ def test_lookback_recompute_path(oracle, monkeypatch, layout):
     check_against_oracle(oracle, w, cnt, label="spin limit 0, %s chunks" % layout)
 
 
+# -------------------------------------------- device-resident split ---
+
+def _zipf_split(total, chunks, seed):
+    p = 1.0 / np.arange(1, chunks + 1) ** 1.1
+    return np.random.default_rng(seed).multinomial(total, p / p.sum()).astype(np.int64)
+
+
+DEV_SPLITS = {
+    "ragged": np.array([0, 1, 7, 8192, 0, 8193, 13, 20000, 0, 3], np.int64),
+    "equal": np.full(8, 3 * TILE, np.int64),
+    "zipf64": _zipf_split(400_000, 64, 3),
+    "150 chunks": np.random.default_rng(4).integers(0, 9000, 150).astype(np.int64),
+}
+
+
+@pytest.mark.parametrize("name", list(DEV_SPLITS))
+def test_device_split_matches_host_path(oracle, name):
+    # Counts that live on the device give the host path's streams, byte for
+    # byte, at the same slot offsets; both decoders restore the input.
+    cnt = DEV_SPLITS[name]
+    total = int(cnt.sum())
+    w = synth.gaussian_bits(total, 0.02, seed=40 + len(cnt))
+    w[::611] = 0
+    say("device split %s: %d chunks, %d values" % (name, len(cnt), total))
+    hbuf, hsizes = gpu_compress(w, cnt)
+    dc = torch.from_numpy(cnt).to(DEV)
+    out, sizes, slots = zc.compress_dev(to_dev(w), dc)
+    torch.cuda.synchronize()
+    off, _ = oracle.slot_offsets(cnt)
+    sizes, slots, ob = sizes.cpu().numpy(), slots.cpu().numpy(), out.cpu().numpy()
+    assert np.array_equal(slots, off[:len(cnt)])
+    assert np.array_equal(sizes, hsizes)
+    vo = np.concatenate([[0], np.cumsum(cnt)])
+    for c in range(len(cnt)):
+        got = ob[off[c]:off[c] + sizes[c]]
+        assert np.array_equal(got, hbuf[off[c]:off[c] + sizes[c]]), (name, c)
+        if c % 7 == 0:
+            assert np.array_equal(got, oracle.compress_chunk(w[vo[c]:vo[c + 1]])), (name, c)
+    back, st = zc.decompress_dev(out, dc, total)
+    assert int(st.item()) == 0
+    assert np.array_equal(back.cpu().numpy().view(np.uint16), w)
+    # explicit device offsets: the streams packed back to back
+    packed = np.zeros(int(sum(((s + 15) // 16) * 16 for s in sizes)) + 16, np.uint8)
+    poff, pos = [], 0
+    for c in range(len(cnt)):
+        packed[pos:pos + sizes[c]] = ob[off[c]:off[c] + sizes[c]]
+        poff.append(pos)
+        pos += ((int(sizes[c]) + 15) // 16) * 16
+    doff = torch.tensor(poff, dtype=torch.int64, device=DEV)
+    back, st = zc.decompress_dev(torch.from_numpy(packed).to(DEV), dc, total, d_in_offsets=doff)
+    assert int(st.item()) == 0
+    assert np.array_equal(back.cpu().numpy().view(np.uint16), w)
+
+
+def test_device_split_full_moe_layout(oracle):
+    # The MoE all-to-all workload at full size (64 Zipf-sized chunks): the
+    # device-split call writes the host path's streams; compared on the GPU.
+    w, cnt = synth.make(4, workers=8)
+    total = int(cnt.sum())
+    say("device split, MoE layout: %d values" % total)
+    x = to_dev(w)
+    hbuf, hsizes = zc.compress(x, cnt)
+    dc = torch.from_numpy(cnt).to(DEV)
+    dbuf, dsizes, dslots = zc.compress_dev(x, dc)
+    torch.cuda.synchronize()
+    off, _ = oracle.slot_offsets(cnt)
+    assert np.array_equal(dslots.cpu().numpy(), off[:len(cnt)])
+    assert torch.equal(hsizes, dsizes)
+    for c, s in enumerate(dsizes.cpu().tolist()):
+        assert torch.equal(hbuf[off[c]:off[c] + s], dbuf[off[c]:off[c] + s]), c
+    back, st = zc.decompress_dev(dbuf, dc, total)
+    assert int(st.item()) == 0 and torch.equal(back, x)
+
+
+def test_device_split_rejects_bad_counts():
+    cnt = np.array([100, 200, 300], np.int64)
+    w = synth.gaussian_bits(600, 0.02, seed=3)
+    x = to_dev(w)
+    for bad in ([100, 200, 299], [100, -5, 505]):
+        dc = torch.tensor(bad, dtype=torch.int64, device=DEV)
+        total = 600
+        out = torch.zeros(zc.zc_bound_max(total, 3), dtype=torch.uint8, device=DEV)
+        sizes = torch.zeros(3, dtype=torch.int64, device=DEV)
+        slots = torch.zeros(3, dtype=torch.int64, device=DEV)
+        ws = torch.empty(zc.zc_workspace_bytes_max(total, 3), dtype=torch.uint8, device=DEV)
+        assert zc.zc_compress_dev(x, dc, total, out, sizes, slots, ws) == zc.ZC_OK
+        torch.cuda.synchronize()
+        assert sizes.cpu().tolist() == [-1, -1, -1]
+        assert slots.cpu().tolist() == [-1, -1, -1]
+        assert int(out.sum().item()) == 0
+        status = torch.zeros(1, dtype=torch.int32, device=DEV)
+        y = torch.empty(600, dtype=torch.int16, device=DEV)
+        assert zc.zc_decompress_dev(out, dc, total, y, status, ws) == zc.ZC_OK
+        torch.cuda.synchronize()
+        assert int(status.item()) >> 24 == 2     # SIZE
+    assert cnt.sum() == 600
+
+
 # ---------------------------------------------------------- errors ---
 
 def test_capacity_and_argument_errors():
