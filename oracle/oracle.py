@@ -74,6 +74,8 @@ def lib():
                                            ct.c_int64, ct.c_void_p]
         L.zco_compress.argtypes = [ct.c_void_p, i64p, ct.c_int, ct.c_void_p,
                                    ct.c_int64, i64p, ct.POINTER(_Stats)]
+        L.zco_reduce_bf16_f32.argtypes = [ct.c_void_p, ct.c_int64, ct.c_int, ct.c_void_p]
+        L.zco_reduce_bf16_f32.restype = None
         L.zco_decompress.argtypes = [ct.c_void_p, ct.c_int64, i64p, i64p,
                                      ct.c_int, ct.c_void_p, ip]
         _lib = L
@@ -213,3 +215,12 @@ def decompress(buf: np.ndarray, counts, offsets=None):
     r = lib().zco_decompress(buf.ctypes.data, buf.size, op, cp, len(counts),
                              out.ctypes.data, ct.byref(bad))
     return r, bad.value, out[:int(counts.sum())]
+
+
+def reduce_bf16_f32(x: np.ndarray, n: int, num_chunks: int) -> np.ndarray:
+    """Chunk-order fp32 sums of num_chunks contributions of n bf16 values."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    assert x.size == n * num_chunks
+    out = np.empty(n, np.float32)
+    lib().zco_reduce_bf16_f32(x.ctypes.data, n, num_chunks, out.ctypes.data)
+    return out

@@ -600,3 +600,27 @@ int zco_decompress(const uint8_t *in, int64_t in_bytes, const int64_t *offsets,
     }
     return 0;
 }
+
+/* ---------------------------------------------------------------- reduce */
+
+/* A bf16 bit pattern is the top half of the fp32 with the same value. */
+static float bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+void zco_reduce_bf16_f32(const uint16_t *x, int64_t n, int num_chunks,
+                         float *out)
+{
+    int64_t i;
+    int c;
+    for (i = 0; i < n; ++i) {
+        float acc = 0.0f;
+        for (c = 0; c < num_chunks; ++c)
+            acc = acc + bf16_to_f32(x[(int64_t)c * n + i]);
+        out[i] = acc;
+    }
+}

@@ -68,6 +68,14 @@ int zco_decompress(const uint8_t *in, int64_t in_bytes, const int64_t *offsets,
                    const int64_t *counts, int num_chunks, uint16_t *out,
                    int *bad_chunk);
 
+/* Receive side of a reduce-scatter (pith.science, Figure 5: zipccl
+ * ReduceScatter; Figure 3: ReduceScatter): num_chunks decoded contributions
+ * of n bf16 values each, contribution c at x[c * n .. c * n + n), summed
+ * element by element in fp32, in chunk order, from +0:
+ *   out[i] = (((+0 + x_0[i]) + x_1[i]) + ...) + x_{C-1}[i]. */
+void zco_reduce_bf16_f32(const uint16_t *x, int64_t n, int num_chunks,
+                         float *out);
+
 #ifdef __cplusplus
 }
 #endif
