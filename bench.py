@@ -161,6 +161,10 @@ def main():
     ap.add_argument("--device-counts", action="store_true",
                     help="time zc_compress_dev / zc_decompress_dev, with the chunk "
                          "counts in device memory (the MoE router's split)")
+    ap.add_argument("--reduce", action="store_true",
+                    help="decode with zc_decompress_reduce: the chunks are one rank's "
+                         "shard as received from each peer, summed in fp32 in chunk "
+                         "order (equal chunks only)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -180,6 +184,10 @@ def main():
     n = int(counts.sum())
     in_bytes = 2 * n
     x = torch.from_numpy(w.view(np.int16)).to(dev)
+    if args.reduce and (args.device_counts or np.any(counts != counts[0])):
+        print("--reduce needs equal chunks and host counts", file=sys.stderr)
+        sys.exit(2)
+    shard = int(counts[0])
     if args.device_counts:
         cap = zc.zc_bound_max(n, len(counts))
         wsb = zc.zc_workspace_bytes_max(n, len(counts))
@@ -192,6 +200,7 @@ def main():
     dcounts = torch.from_numpy(np.asarray(counts, np.int64)).to(dev)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     y = torch.empty(n, dtype=torch.int16, device=dev)
+    red = torch.empty(shard if args.reduce else 4, dtype=torch.float32, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
@@ -212,7 +221,9 @@ def main():
             raise zc.ZcError(r, "zc_compress")
         flush.fill_((i + 1) & 0xFF)
         e2.record(stream)
-        if args.device_counts:
+        if args.reduce:
+            r = zc.zc_decompress_reduce(buf, shard, len(counts), red, status, y, stream=stream)
+        elif args.device_counts:
             r = zc.zc_decompress_dev(buf, dcounts, n, y, status, ws, stream=stream)
         else:
             r = zc.zc_decompress(buf, counts, y, status, stream=stream)
@@ -239,6 +250,13 @@ def main():
     td = np.array([c.elapsed_time(d) for _, _, c, d in times]) * 1e-3
     st = int(status.item())
     ok = st == 0 and torch.equal(x, y)
+    if args.reduce:
+        acc = torch.zeros(shard, dtype=torch.float32, device=dev)
+        for k in range(len(counts)):
+            acc = acc + (x[k * shard:(k + 1) * shard].to(torch.int32) << 16).view(torch.float32)
+        same = (acc.view(torch.int32) == red.view(torch.int32)) | (acc.isnan() & red.isnan())
+        ok = ok and bool(same.all())
+        del acc
     comp = int(sizes.sum().item())
     if not ok:
         log("ROUND TRIP FAILED (status %#x)" % st)
@@ -266,8 +284,11 @@ def main():
     value = in_bytes / step_s / 1e9
     alg_bytes = in_bytes + comp              # read 2n + write C, or read C + write 2n
     alg_c = alg_bytes / c_mean / 1e9
-    alg_d = alg_bytes / d_mean / 1e9
-    dom = "decompress" if d_mean >= c_mean else "compress"
+    # decode and sum: read C + write 4 n/C (the staged bf16 values are
+    # written and read once more between the two kernels)
+    alg_bytes_d = comp + 4 * shard if args.reduce else alg_bytes
+    alg_d = alg_bytes_d / d_mean / 1e9
+    dom = "decompress" if d_mean >= c_mean and not args.reduce else "compress"
     achieved = alg_d if dom == "decompress" else alg_c
     # the counter summaries cover the host-count kernels only
     traffic = None if args.device_counts else read_traffic(synth.NAMES[args.workload])
@@ -293,7 +314,10 @@ def main():
             "bytes_in": in_bytes,
             "seed": seed,
             "step": ("zc_compress_dev + zc_decompress_dev (counts in device memory)"
-                     if args.device_counts else "zc_compress + zc_decompress") +
+                     if args.device_counts else
+                     "zc_compress + zc_decompress_reduce (fp32 chunk-order sum of %d "
+                     "shards of %d values)" % (len(counts), shard)
+                     if args.reduce else "zc_compress + zc_decompress") +
                     " of every chunk, 1 GiB cache flush before each call (untimed)",
         },
         "compress_GBps": round(comp_gbps, 2),

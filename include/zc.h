@@ -208,6 +208,35 @@ int zc_decompress_dev(const void* d_in, size_t in_bytes,
                       uint16_t* d_out, int32_t* d_status, void* d_ws,
                       size_t ws_bytes, void* stream);
 
+/*
+ * Receive side of a compressed reduce-scatter (pith.science, Figure 5: the
+ * zipccl ReduceScatter workflow; Figure 3: ReduceScatter).  A rank receives
+ * one compressed copy of its shard from each of num_chunks peers, decodes
+ * them, and sums them element by element:
+ *   d_out[i] = (((+0 + x_0[i]) + x_1[i]) + ...) + x_{C-1}[i]
+ * in fp32 with round-to-nearest-even, added in chunk order c = 0 .. C-1, where
+ * x_c[i] is value i of stream c widened exactly from bf16.  The result is
+ * bit-identical to that order of additions; only NaN sign and payload are
+ * unspecified.
+ *   d_in, in_bytes, in_offsets  as for zc_decompress; every stream must hold
+ *               exactly n values
+ *   n           values per stream (the shard length), 0 .. ZC_MAX_CHUNK_VALUES
+ *   num_chunks  streams to sum, >= 0 (0 writes n zeros)
+ *   d_out       device fp32[n], 16-byte aligned
+ *   d_status    device int32, 0 on entry; as for zc_decompress.  If it is
+ *               nonzero after the stream has run, d_out is undefined.
+ *   d_scratch   device, 16-byte aligned, scratch_bytes >= 2 n num_chunks:
+ *               the decoded bf16 contributions are staged there (stream c at
+ *               element offset c n); caller-owned, contents undefined after
+ *   stream      hipStream_t; both launches (decode, then sum) are queued on it
+ * Returns ZC_OK once queued; ZC_EINVAL for a bad argument, ZC_ENOSPC for a
+ * short scratch buffer (nothing queued), ZC_EHIP if a launch fails.
+ */
+int zc_decompress_reduce(const void* d_in, size_t in_bytes,
+                         const int64_t* in_offsets, int64_t n,
+                         int32_t num_chunks, float* d_out, int32_t* d_status,
+                         void* d_scratch, size_t scratch_bytes, void* stream);
+
 /* Static text for a zc_status_t value. */
 const char* zc_strerror(int code);
 

@@ -40,6 +40,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "zc.h"
 #include "zc_table.h"
@@ -1355,6 +1356,68 @@ void zc_decompress_dev_kernel(const uint8_t* __restrict__ in, uint16_t* __restri
     decompress_body(in, out, status, *tab);
 }
 
+// ------------------------------------------------------------ reduce
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ inline void add8(float (&acc)[8], const uint4 v)
+{
+    acc[0] = acc[0] + bf16_lo(v.x);
+    acc[1] = acc[1] + bf16_hi(v.x);
+    acc[2] = acc[2] + bf16_lo(v.y);
+    acc[3] = acc[3] + bf16_hi(v.y);
+    acc[4] = acc[4] + bf16_lo(v.z);
+    acc[5] = acc[5] + bf16_hi(v.z);
+    acc[6] = acc[6] + bf16_lo(v.w);
+    acc[7] = acc[7] + bf16_hi(v.w);
+}
+
+// Receive side of a reduce-scatter (pith.science, Figure 5: zipccl
+// ReduceScatter): num_chunks decoded contributions of n bf16 values each
+// (contribution c at x + c n) summed element by element in fp32, in chunk
+// order, from +0.  Each thread owns 8 consecutive elements; rows are read
+// with 16-byte nontemporal loads, 8 contributions in flight at a time, and
+// the sums are added strictly in chunk order.
+__global__ __launch_bounds__(kBlock)
+void zc_reduce_kernel(const uint16_t* __restrict__ x, uint64_t n, int32_t num_chunks,
+                      float* __restrict__ out)
+{
+    const uint64_t i0 = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) * 8;
+    if (i0 >= n)
+        return;
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        acc[j] = 0.0f;
+    if ((n & 7) == 0) {
+        const uint16_t* p = x + i0;
+        int32_t c = 0;
+        for (; c + 8 <= num_chunks; c += 8) {
+            uint4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                v[u] = ld_nt4(p + static_cast<uint64_t>(c + u) * n);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                add8(acc, v[u]);
+        }
+        for (; c < num_chunks; ++c)
+            add8(acc, ld_nt4(p + static_cast<uint64_t>(c) * n));
+        st_nt4(out + i0, make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]),
+                                    __float_as_uint(acc[2]), __float_as_uint(acc[3])));
+        st_nt4(out + i0 + 4, make_uint4(__float_as_uint(acc[4]), __float_as_uint(acc[5]),
+                                        __float_as_uint(acc[6]), __float_as_uint(acc[7])));
+    } else {
+        for (int j = 0; j < 8 && i0 + j < n; ++j) {
+            float a = 0.0f;
+            for (int32_t c = 0; c < num_chunks; ++c)
+                a = a + bf16_lo(x[static_cast<uint64_t>(c) * n + i0 + j]);
+            out[i0 + j] = a;
+        }
+    }
+}
+
 // ------------------------------------------------------------ device-resident split
 
 __device__ inline uint64_t wave_excl_scan64(uint64_t x, uint32_t lane, uint64_t* total)
@@ -1739,6 +1802,35 @@ int zc_decompress_dev(const void* d_in, size_t in_bytes, const int64_t* d_in_off
             return ZC_EHIP;
     }
     return ZC_OK;
+}
+
+int zc_decompress_reduce(const void* d_in, size_t in_bytes, const int64_t* in_offsets,
+                         int64_t n, int32_t num_chunks, float* d_out, int32_t* d_status,
+                         void* d_scratch, size_t scratch_bytes, void* stream)
+{
+    if (n < 0 || n > ZC_MAX_CHUNK_VALUES || num_chunks < 0)
+        return ZC_EINVAL;
+    if (n == 0)
+        return ZC_OK;
+    if (!d_out || !d_status || (num_chunks > 0 && (!d_in || !d_scratch)))
+        return ZC_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(d_out) & 15) || (reinterpret_cast<uintptr_t>(d_scratch) & 15))
+        return ZC_EINVAL;
+    if (scratch_bytes < 2ull * static_cast<uint64_t>(n) * static_cast<uint64_t>(num_chunks))
+        return ZC_ENOSPC;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (num_chunks > 0) {
+        std::vector<int64_t> counts(static_cast<size_t>(num_chunks), n);
+        const int r = zc_decompress(d_in, in_bytes, in_offsets, counts.data(), num_chunks,
+                                    static_cast<uint16_t*>(d_scratch), d_status, stream);
+        if (r != ZC_OK)
+            return r;
+    }
+    const uint64_t threads = (static_cast<uint64_t>(n) + 7) / 8;
+    hipLaunchKernelGGL(zc_reduce_kernel, dim3(static_cast<uint32_t>((threads + kBlock - 1) / kBlock)),
+                       dim3(kBlock), 0, s, static_cast<const uint16_t*>(d_scratch),
+                       static_cast<uint64_t>(n), num_chunks, d_out);
+    return hipGetLastError() == hipSuccess ? ZC_OK : ZC_EHIP;
 }
 
 int zc_decompress(const void* d_in, size_t in_bytes, const int64_t* in_offsets,

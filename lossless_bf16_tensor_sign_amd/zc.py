@@ -66,6 +66,10 @@ def lib():
                                         ct.c_int32, ct.c_int64, ct.c_void_p, ct.c_void_p,
                                         ct.c_void_p, ct.c_size_t, ct.c_void_p]
         L.zc_decompress_dev.restype = ct.c_int
+        L.zc_decompress_reduce.argtypes = [ct.c_void_p, ct.c_size_t, i64p, ct.c_int64,
+                                           ct.c_int32, ct.c_void_p, ct.c_void_p, ct.c_void_p,
+                                           ct.c_size_t, ct.c_void_p]
+        L.zc_decompress_reduce.restype = ct.c_int
         L.zc_strerror.argtypes = [ct.c_int]
         L.zc_strerror.restype = ct.c_char_p
         L.zc_code_table.argtypes = [ct.c_int32, ct.POINTER(ct.c_int32),
@@ -176,6 +180,22 @@ def zc_decompress_dev(d_in, d_counts, total_values, d_out, d_status, d_ws, d_in_
                                        _ptr(d_status), _ptr(d_ws), wsb, _stream(stream)))
 
 
+def zc_decompress_reduce(d_in, n, num_chunks, d_out, d_status, d_scratch, in_offsets=None,
+                         stream=None, in_bytes=None, scratch_bytes=None) -> int:
+    """Queue decode of num_chunks streams of n values and their fp32 sum."""
+    nb = d_in.numel() * d_in.element_size() if in_bytes is None else in_bytes
+    sb = d_scratch.numel() * d_scratch.element_size() if scratch_bytes is None else scratch_bytes
+    if in_offsets is not None:
+        off, op = _counts(in_offsets)
+        if len(off) < int(num_chunks):
+            raise ValueError("in_offsets has fewer entries than num_chunks")
+    else:
+        off, op = None, None
+    return int(lib().zc_decompress_reduce(_ptr(d_in), nb, op, int(n), int(num_chunks),
+                                          _ptr(d_out), _ptr(d_status), _ptr(d_scratch), sb,
+                                          _stream(stream)))
+
+
 # ------------------------------------------------ allocating conveniences
 
 def compress(x, counts, stream=None):
@@ -247,5 +267,27 @@ def decompress_dev(buf, d_counts, total_values, d_in_offsets=None, stream=None, 
         st = int(status.item())
         if st != 0:
             raise ZcError(ZC_ECORRUPT, "zc_decompress_dev: %s in chunk %d"
+                          % (REASONS.get(st >> 24, st >> 24), st & 0xFFFFFF))
+    return out, status
+
+
+def decompress_reduce(buf, n, num_chunks, in_offsets=None, stream=None, check=True):
+    """Decode num_chunks streams of n values each and sum them in fp32.
+
+    Returns (float32 device tensor of n sums, int32 device status)."""
+    import torch
+    dev = buf.device
+    out = torch.empty(max(int(n), 4), dtype=torch.float32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    scratch = torch.empty(max(2 * int(n) * int(num_chunks), 16), dtype=torch.uint8, device=dev)
+    r = zc_decompress_reduce(buf, n, num_chunks, out, status, scratch, in_offsets=in_offsets,
+                             stream=stream)
+    if r != ZC_OK:
+        raise ZcError(r, "zc_decompress_reduce")
+    out = out[:int(n)]
+    if check:
+        st = int(status.item())
+        if st != 0:
+            raise ZcError(ZC_ECORRUPT, "zc_decompress_reduce: %s in chunk %d"
                           % (REASONS.get(st >> 24, st >> 24), st & 0xFFFFFF))
     return out, status

@@ -1,0 +1,161 @@
+"""GPU parity of the reduce-scatter receive step (decode, then ordered sum).
+
+zc_decompress_reduce decodes num_chunks compressed contributions of n bf16
+values and sums them element by element in fp32, in chunk order, from +0.
+The bar is bit-exactness against the oracle's chunk-order sum (NaN results
+compared as NaN, since their sign and payload are unspecified).  At full size
+a sample of positions is compared with the oracle and every position with a
+chunk-order sum written as plain PyTorch fp32 additions.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from lossless_bf16_tensor_sign_amd import synth, zc
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(msg):
+    print("[gpu] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(w):
+    return torch.from_numpy(np.ascontiguousarray(w).view(np.int16)).to(DEV)
+
+
+def same_f32(got, want):
+    """Bit-equal, except that NaN only has to meet NaN."""
+    got = np.asarray(got, np.float32)
+    want = np.asarray(want, np.float32)
+    gn, wn = np.isnan(got), np.isnan(want)
+    assert np.array_equal(gn, wn), "NaN positions differ, first %d" % np.nonzero(gn != wn)[0][0]
+    gb, wb = got.view(np.uint32), want.view(np.uint32)
+    bad = np.nonzero((gb != wb) & ~wn)[0]
+    assert bad.size == 0, "first differing sum at %d: %#x vs %#x" % (
+        bad[0], gb[bad[0]], wb[bad[0]])
+
+
+def gpu_reduce(w, n, c):
+    buf, sizes = zc.compress(to_dev(w), [n] * c)
+    out, status = zc.decompress_reduce(buf, n, c, check=False)
+    torch.cuda.synchronize()
+    return int(status.item()), out.cpu().numpy()
+
+
+def special_mix(size, seed):
+    """Random bf16 patterns with zeros of both signs, subnormals, Inf and NaN."""
+    rng = np.random.default_rng(seed)
+    w = synth.gaussian_bits(size, 0.02, seed)
+    pick = rng.random(size)
+    w[pick < 0.02] = rng.integers(0, 1 << 16, int((pick < 0.02).sum()), dtype=np.uint16)
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x807F, 0x7F80, 0xFF80, 0x7FC0, 0x7F7F,
+                         0xFF7F, 0x0080], np.uint16)
+    m = (pick >= 0.02) & (pick < 0.03)
+    w[m] = specials[rng.integers(0, specials.size, int(m.sum()))]
+    return w
+
+
+@pytest.mark.parametrize("n,c", [(20000, 8), (20003, 8), (24576, 11), (8192, 1),
+                                 (1, 5), (7, 3), (65536 + 40, 17)])
+def test_reduce_matches_oracle(oracle, n, c):
+    w = special_mix(n * c, 1000 + n + c)
+    say("reduce n=%d chunks=%d" % (n, c))
+    st, got = gpu_reduce(w, n, c)
+    assert st == 0, "status %#x" % st
+    same_f32(got, oracle.reduce_bf16_f32(w, n, c))
+
+
+def test_reduce_addition_order_is_chunk_order(oracle):
+    # 2^24 + 1 rounds back to 2^24 in fp32, so the sum in chunk order is 0
+    # while any order that adds the 1 last gives 1.
+    n = 1024
+    w = np.concatenate([np.full(n, 0x4B80, np.uint16), np.full(n, 0x3F80, np.uint16),
+                        np.full(n, 0xCB80, np.uint16)])
+    say("reduce order pin")
+    st, got = gpu_reduce(w, n, 3)
+    assert st == 0
+    want = oracle.reduce_bf16_f32(w, n, 3)
+    assert np.all(want == 0.0) and not np.signbit(want).any()
+    same_f32(got, want)
+
+
+def test_reduce_of_negative_zeros_is_positive_zero(oracle):
+    n = 4096
+    w = np.full(n * 4, 0x8000, np.uint16)
+    st, got = gpu_reduce(w, n, 4)
+    assert st == 0
+    assert np.all(got.view(np.uint32) == 0)
+
+
+def test_reduce_zero_chunks_writes_zeros():
+    n = 1000
+    out = torch.full((n,), 7.0, dtype=torch.float32, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    scratch = torch.empty(16, dtype=torch.uint8, device=DEV)
+    dummy = torch.empty(16, dtype=torch.uint8, device=DEV)
+    r = zc.zc_decompress_reduce(dummy, n, 0, out, status, scratch)
+    assert r == zc.ZC_OK
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert torch.all(out.view(torch.int32) == 0)
+
+
+def test_reduce_argument_errors():
+    n, c = 4096, 4
+    w = synth.gaussian_bits(n * c, 0.02, 5)
+    buf, _ = zc.compress(to_dev(w), [n] * c)
+    out = torch.empty(n + 4, dtype=torch.float32, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    scratch = torch.empty(2 * n * c, dtype=torch.uint8, device=DEV)
+    assert zc.zc_decompress_reduce(buf, n, c, out, status, scratch,
+                                   scratch_bytes=2 * n * c - 1) == zc.ZC_ENOSPC
+    assert zc.zc_decompress_reduce(buf, n, c, out[1:], status, scratch) == zc.ZC_EINVAL
+    assert zc.zc_decompress_reduce(buf, -1, c, out, status, scratch) == zc.ZC_EINVAL
+    assert zc.zc_decompress_reduce(buf, n, -1, out, status, scratch) == zc.ZC_EINVAL
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+
+
+def test_reduce_reports_corrupt_stream(oracle):
+    n, c = 20000, 4
+    w = synth.gaussian_bits(n * c, 0.02, 6)
+    buf, sizes = zc.compress(to_dev(w), [n] * c)
+    torch.cuda.synchronize()
+    hb = buf.cpu().numpy().copy()
+    off, _ = oracle.slot_offsets([n] * c)
+    hb[off[2]] ^= 0xFF                      # magic of stream 2
+    out, status = zc.decompress_reduce(torch.from_numpy(hb).to(DEV), n, c, check=False)
+    torch.cuda.synchronize()
+    st = int(status.item())
+    assert st >> 24 == 1 and (st & 0xFFFFFF) == 2, hex(st)
+
+
+def test_reduce_full_size_gradient_buffer(oracle):
+    # The gradient reduce-scatter workload at its real shape: one rank
+    # receives a compressed copy of its 4M-value shard from each of 64 peers.
+    w, cnt = synth.make(3, workers=8)
+    c, n = len(cnt), int(cnt[0])
+    assert np.all(cnt == n)
+    say("reduce full size: %d x %d" % (c, n))
+    x = to_dev(w)
+    buf, sizes = zc.compress(x, cnt)
+    out, status = zc.decompress_reduce(buf, n, c, check=False)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    # every position: chunk-order fp32 additions, one elementwise add per chunk
+    xs = x.view(c, n)
+    acc = torch.zeros(n, dtype=torch.float32, device=DEV)
+    for k in range(c):
+        acc = acc + (xs[k].to(torch.int32) << 16).view(torch.float32)
+    torch.cuda.synchronize()
+    same_f32(out.cpu().numpy(), acc.cpu().numpy())
+    # sampled positions (and both ends) against the oracle
+    rng = np.random.default_rng(31)
+    idx = np.unique(np.concatenate([rng.integers(0, n, 4096), [0, 1, n - 2, n - 1]]))
+    cols = np.ascontiguousarray(w.reshape(c, n)[:, idx])
+    same_f32(out.cpu().numpy()[idx], oracle.reduce_bf16_f32(cols.ravel(), idx.size, c))
