@@ -354,6 +354,38 @@ def main():
         "kernel_sources_sha256": kernel_sources_sha256(),
     }
 
+    # sampled size estimate (8 tiles per chunk) and the switch's break-even
+    # link speeds from this run's codec rates and stream sizes
+    est = torch.empty(len(counts), dtype=torch.int64, device=dev)
+    te = []
+    for i in range(3):
+        flush.fill_((i + 11) & 0xFF)
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        r = zc.zc_estimate(x, dcounts, n, 8, est, stream=stream)
+        e1.record(stream)
+        if r != zc.ZC_OK:
+            raise zc.ZcError(r, "zc_estimate")
+        te.append((e0, e1))
+    torch.cuda.synchronize()
+    est_total = int(est.sum().item())
+    line["estimate"] = {
+        "samples_per_chunk": 8,
+        "ms": round(float(np.mean([a.elapsed_time(b) for a, b in te])), 4),
+        "comp_bytes_estimated": est_total,
+        "rel_error": round(est_total / comp - 1.0, 5),
+    }
+    sw = {}
+    # (with --reduce the decode rate is that of decode + sum)
+    colls = ["reduce_scatter"] if args.reduce else ["allgather", "alltoall"]
+    for ranks in (8, 64):
+        for coll in colls:
+            st_, res = zc.zc_switch_decide(coll, ranks, in_bytes, est_total, 100.0, 0.0,
+                                           comp_gbps, dec_gbps, dec_gbps)
+            if st_ == zc.ZC_OK:
+                sw["%s_%d" % (coll, ranks)] = round(res["breakeven_GBps"], 1)
+    line["switch_breakeven_link_GBps"] = sw
+
     if not args.no_cpu_baseline:
         threads = max(1, min(args.cpu_threads, os.cpu_count() or 1, len(counts)))
         log("cpu baseline: oracle, %d threads" % threads)

@@ -237,6 +237,74 @@ int zc_decompress_reduce(const void* d_in, size_t in_bytes,
                          int32_t num_chunks, float* d_out, int32_t* d_status,
                          void* d_scratch, size_t scratch_bytes, void* stream);
 
+/*
+ * Adaptive switch (abstract, technique (3): compressed or plain collective,
+ * chosen from the workload and the system; pith.science, Figure 15 caption:
+ * the adaptive switcher).  zc_estimate predicts the compressed size from a
+ * sample of tiles; zc_switch_decide compares the two collectives' times.
+ */
+
+/*
+ * Estimated ZCB1 stream bytes of each chunk, from samples_per_chunk tiles
+ * spread evenly over it (tile floor(i T / k), i < k = min(samples, T) of its
+ * T tiles): the stream's fixed part (header, index, raw bytes: X) plus the
+ * sampled tiles' exponent-stream bytes scaled by T / k, rounded half up.
+ * With samples_per_chunk >= T the estimate is the exact comp_bytes that
+ * zc_compress writes.
+ *   d_in         device bf16[total_values], chunks back to back
+ *   d_counts     device int64[num_chunks], summing to total_values
+ *   d_est        device int64[num_chunks]: the estimates, or -1 in every
+ *                entry if a count is outside 0 .. ZC_MAX_CHUNK_VALUES or the
+ *                counts do not sum to total_values
+ * Reads every count once per chunk (one workgroup per chunk).  Returns ZC_OK
+ * once queued, ZC_EINVAL (samples_per_chunk < 1, negative sizes, null
+ * pointers) or ZC_EHIP.
+ */
+int zc_estimate(const uint16_t* d_in, const int64_t* d_counts,
+                int32_t num_chunks, int64_t total_values,
+                int32_t samples_per_chunk, int64_t* d_est, void* stream);
+
+/* Collectives modelled by zc_switch_decide. */
+#define ZC_COLL_ALLGATHER 0
+#define ZC_COLL_REDUCE_SCATTER 1
+#define ZC_COLL_ALLTOALL 2
+
+typedef struct {
+    double link_GBps;        /* per-rank bandwidth of the plain collective   */
+    double step_latency_us;  /* latency of each of its ranks - 1 steps       */
+    double compress_GBps;    /* codec rates, in GB/s of uncompressed bytes:  */
+    double decompress_GBps;  /*   zc_compress, zc_decompress,                */
+    double reduce_GBps;      /*   zc_decompress_reduce (reduce-scatter only) */
+} zc_switch_params;
+
+typedef struct {
+    int32_t use_compressed;  /* 1 if the compressed collective is faster     */
+    double plain_us;         /* modelled time of the plain collective        */
+    double compressed_us;    /* ... of compress, exchange, decompress        */
+    double breakeven_GBps;   /* compression wins on links slower than this;
+                                0 if it never does                          */
+} zc_switch_result;
+
+/*
+ * Host-only cost model of one collective on `ranks` ranks.  Per rank, with
+ * S = bytes (the uncompressed collective buffer), C = comp_bytes (its
+ * compressed size, e.g. the sum of zc_estimate), W = S (P-1)/P and
+ * W_c = C (P-1)/P:
+ *   plain       (P-1) a + W / B
+ *   compressed  (P-1) a + W_c / B + codec, with codec =
+ *     ZC_COLL_ALLGATHER       (S/P) / R_comp + W / R_dec
+ *     ZC_COLL_ALLTOALL        S / R_comp + W / R_dec
+ *     ZC_COLL_REDUCE_SCATTER  S / R_comp + S / R_red  (all-to-all, then
+ *                             decode and sum: pith.science, Figure 5)
+ * so compression wins exactly below B* = (W - W_c) / codec.  Returns ZC_OK,
+ * or ZC_EINVAL for an unknown collective, ranks < 1, negative or non-finite
+ * sizes, C = 0 with S > 0, or a rate the collective needs that is not
+ * positive and finite.
+ */
+int zc_switch_decide(int32_t collective, int32_t ranks, double bytes,
+                     double comp_bytes, const zc_switch_params* params,
+                     zc_switch_result* result);
+
 /* Static text for a zc_status_t value. */
 const char* zc_strerror(int code);
 

@@ -50,6 +50,7 @@ def build(verbose: bool = False) -> str:
     cmd = [HIPCC, *HIP_FLAGS, "-shared",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-I", BUILD,
            os.path.join(CSRC, "zc_kernels.hip"), os.path.join(CSRC, "zc_table.cpp"),
+           os.path.join(CSRC, "zc_switch.cpp"),
            "-o", tmp]
     if verbose:
         print(" ".join(cmd))

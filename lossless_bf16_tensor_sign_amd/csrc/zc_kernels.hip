@@ -1527,6 +1527,132 @@ void zc_plan_kernel(const int64_t* __restrict__ counts, int32_t num_chunks, int3
     }
 }
 
+// ------------------------------------------------------------ size estimate
+
+__device__ inline uint32_t exp_of(const uint4& v, int j)
+{
+    const uint32_t w = j < 2 ? v.x : j < 4 ? v.y : j < 6 ? v.z : v.w;
+    return (w >> ((j & 1) ? 23 : 7)) & 0xFFu;
+}
+
+// Bytes of tile t's exponent stream, from the input values: per group (one
+// per lane) the maximum exponent, the code length of every member (escape:
+// code word plus 8 bits), and raw mode when that reaches 8 bits per member;
+// the tile's bits rounded up to whole 32-bit words.  This is the size the
+// encoder writes for the tile.  A whole, 16-byte aligned tile is read with
+// all of a lane's 16 loads in flight; other tiles value by value.  bits_of[d]
+// is the stream length of a member d below its group's maximum.
+__device__ inline uint32_t tile_stream_bytes(const uint16_t* __restrict__ chunk, uint32_t n,
+                                             uint32_t t, uint32_t lane,
+                                             const uint8_t* __restrict__ bits_of)
+{
+    const uint16_t* src = chunk + static_cast<uint64_t>(t) * kTile;
+    const uint32_t rem = min(n - t * kTile, static_cast<uint32_t>(kTile));
+    uint32_t bits = 0;
+    if (rem == kTile && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+        uint4 v[kSteps];
+#pragma unroll
+        for (int k = 0; k < kSteps; ++k)
+            v[k] = *reinterpret_cast<const uint4*>(src + k * 512 + lane * 8);
+        uint32_t emax = 0;
+#pragma unroll
+        for (int k = 0; k < kSteps; ++k)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                emax = max(emax, exp_of(v[k], j));
+#pragma unroll
+        for (int k = 0; k < kSteps; ++k)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                bits += bits_of[emax - exp_of(v[k], j)];
+    } else {
+        uint32_t emax = 0;
+#pragma unroll 1
+        for (uint32_t i = lane * 8; i < rem; i += (i & 7) == 7 ? 512 - 7 : 1)
+            emax = max(emax, (static_cast<uint32_t>(src[i]) >> 7) & 0xFFu);
+#pragma unroll 1
+        for (uint32_t i = lane * 8; i < rem; i += (i & 7) == 7 ? 512 - 7 : 1)
+            bits += bits_of[emax - ((static_cast<uint32_t>(src[i]) >> 7) & 0xFFu)];
+    }
+    const uint32_t ng = group_members(rem, lane);
+    const uint32_t glen = (ng > 0 && bits >= 8 * ng) ? 8 * ng : bits;
+    return ((wave_sum(glen) + 31) >> 5) * 4;
+}
+
+// Estimated stream size of each chunk, for the switch between compressed and
+// plain collectives (abstract, technique (3); pith.science, Figure 15
+// caption), which needs the compressed size before it decides.  Workgroup c
+// handles chunk c: it checks the split, finds the chunk's value offset, and
+// sizes `samples` tiles spread evenly over the chunk (tile floor(i T / k)
+// for i < k = min(samples, T)).  The estimate is the exact fixed part of the
+// stream plus the sampled tile bytes scaled by T / k, rounded half up; with
+// k = T it is the exact size zc_compress writes.  -1 for an invalid split.
+__global__ __launch_bounds__(kBlock)
+void zc_estimate_kernel(const uint16_t* __restrict__ in, const int64_t* __restrict__ counts,
+                        int32_t num_chunks, int64_t total, int32_t samples,
+                        int64_t* __restrict__ est)
+{
+    __shared__ uint64_t s_part[kWaves][3];
+    __shared__ uint8_t s_bits[256];
+    const uint32_t tid = threadIdx.x;
+    s_bits[tid] = static_cast<uint8_t>(tid < static_cast<uint32_t>(kEsc) ? len_of(tid)
+                                                                          : len_of(kEsc) + 8u);
+    const uint32_t lane = tid & (kLanes - 1);
+    const uint32_t wave = tid / kLanes;
+    const int32_t c = static_cast<int32_t>(blockIdx.x);
+    uint64_t before = 0, sum = 0, bad = 0;
+    for (int32_t j = static_cast<int32_t>(tid); j < num_chunks; j += kBlock) {
+        const int64_t v = counts[j];
+        if (v < 0 || v > ZC_MAX_CHUNK_VALUES)
+            bad = 1;
+        else {
+            sum += static_cast<uint64_t>(v);
+            before += j < c ? static_cast<uint64_t>(v) : 0u;
+        }
+    }
+    before = wave_sum64(before);
+    sum = wave_sum64(sum);
+    bad = wave_sum64(bad);
+    if (lane == 0) {
+        s_part[wave][0] = before;
+        s_part[wave][1] = sum;
+        s_part[wave][2] = bad;
+    }
+    __syncthreads();
+    before = sum = bad = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        before += s_part[w][0];
+        sum += s_part[w][1];
+        bad += s_part[w][2];
+    }
+    __syncthreads();
+    if (bad || sum != static_cast<uint64_t>(total)) {
+        if (tid == 0)
+            est[c] = -1;
+        return;
+    }
+    const uint32_t n = static_cast<uint32_t>(counts[c]);
+    const Geom G = geometry(n);
+    const uint32_t k = min(static_cast<uint32_t>(samples), G.T);
+    uint64_t bytes = 0;
+    for (uint32_t i = wave; i < k; i += kWaves) {
+        const uint32_t t = static_cast<uint32_t>((static_cast<uint64_t>(i) * G.T) / k);
+        bytes += tile_stream_bytes(in + before, n, t, lane, s_bits);
+    }
+    if (lane == 0)
+        s_part[wave][0] = bytes;
+    __syncthreads();
+    if (tid == 0) {
+        uint64_t s = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+            s += s_part[w][0];
+        const uint64_t scaled = k ? (s * G.T + k / 2) / k : 0;
+        est[c] = static_cast<int64_t>(G.X + scaled);
+    }
+}
+
 // ------------------------------------------------------------ host side
 
 struct Counts {
@@ -1802,6 +1928,22 @@ int zc_decompress_dev(const void* d_in, size_t in_bytes, const int64_t* d_in_off
             return ZC_EHIP;
     }
     return ZC_OK;
+}
+
+int zc_estimate(const uint16_t* d_in, const int64_t* d_counts, int32_t num_chunks,
+                int64_t total_values, int32_t samples_per_chunk, int64_t* d_est, void* stream)
+{
+    if (num_chunks < 0 || total_values < 0 || samples_per_chunk < 1 ||
+        (num_chunks == 0 && total_values != 0))
+        return ZC_EINVAL;
+    if (num_chunks == 0)
+        return ZC_OK;
+    if (!d_counts || !d_est || (total_values > 0 && !d_in))
+        return ZC_EINVAL;
+    hipLaunchKernelGGL(zc_estimate_kernel, dim3(static_cast<uint32_t>(num_chunks)), dim3(kBlock), 0,
+                       static_cast<hipStream_t>(stream), d_in, d_counts, num_chunks, total_values,
+                       samples_per_chunk, d_est);
+    return hipGetLastError() == hipSuccess ? ZC_OK : ZC_EHIP;
 }
 
 int zc_decompress_reduce(const void* d_in, size_t in_bytes, const int64_t* in_offsets,

@@ -21,6 +21,22 @@ REASONS = {
     7: "ESCAPE", 8: "LENGTH", 9: "EMAX", 10: "RAWMODE", 11: "PADDING",
 }
 
+ZC_COLL_ALLGATHER, ZC_COLL_REDUCE_SCATTER, ZC_COLL_ALLTOALL = 0, 1, 2
+COLLECTIVES = {"allgather": ZC_COLL_ALLGATHER, "reduce_scatter": ZC_COLL_REDUCE_SCATTER,
+               "alltoall": ZC_COLL_ALLTOALL}
+
+
+class SwitchParams(ct.Structure):
+    _fields_ = [("link_GBps", ct.c_double), ("step_latency_us", ct.c_double),
+                ("compress_GBps", ct.c_double), ("decompress_GBps", ct.c_double),
+                ("reduce_GBps", ct.c_double)]
+
+
+class SwitchResult(ct.Structure):
+    _fields_ = [("use_compressed", ct.c_int32), ("plain_us", ct.c_double),
+                ("compressed_us", ct.c_double), ("breakeven_GBps", ct.c_double)]
+
+
 _lib = None
 
 
@@ -70,6 +86,12 @@ def lib():
                                            ct.c_int32, ct.c_void_p, ct.c_void_p, ct.c_void_p,
                                            ct.c_size_t, ct.c_void_p]
         L.zc_decompress_reduce.restype = ct.c_int
+        L.zc_estimate.argtypes = [ct.c_void_p, ct.c_void_p, ct.c_int32, ct.c_int64,
+                                  ct.c_int32, ct.c_void_p, ct.c_void_p]
+        L.zc_estimate.restype = ct.c_int
+        L.zc_switch_decide.argtypes = [ct.c_int32, ct.c_int32, ct.c_double, ct.c_double,
+                                       ct.POINTER(SwitchParams), ct.POINTER(SwitchResult)]
+        L.zc_switch_decide.restype = ct.c_int
         L.zc_strerror.argtypes = [ct.c_int]
         L.zc_strerror.restype = ct.c_char_p
         L.zc_code_table.argtypes = [ct.c_int32, ct.POINTER(ct.c_int32),
@@ -196,6 +218,26 @@ def zc_decompress_reduce(d_in, n, num_chunks, d_out, d_status, d_scratch, in_off
                                           _stream(stream)))
 
 
+def zc_estimate(d_in, d_counts, total_values, samples_per_chunk, d_est, stream=None) -> int:
+    """Queue the sampled size estimate of each chunk (int64 device tensors)."""
+    return int(lib().zc_estimate(_ptr(d_in), _ptr(d_counts), d_counts.numel(),
+                                 int(total_values), int(samples_per_chunk), _ptr(d_est),
+                                 _stream(stream)))
+
+
+def zc_switch_decide(collective, ranks, nbytes, comp_bytes, link_GBps, step_latency_us,
+                     compress_GBps, decompress_GBps=0.0, reduce_GBps=0.0):
+    """Host cost model: returns (status, dict of the result fields)."""
+    coll = COLLECTIVES.get(collective, collective)
+    p = SwitchParams(float(link_GBps), float(step_latency_us), float(compress_GBps),
+                     float(decompress_GBps), float(reduce_GBps))
+    r = SwitchResult()
+    st = int(lib().zc_switch_decide(int(coll), int(ranks), float(nbytes), float(comp_bytes),
+                                    ct.byref(p), ct.byref(r)))
+    return st, {"use_compressed": bool(r.use_compressed), "plain_us": r.plain_us,
+                "compressed_us": r.compressed_us, "breakeven_GBps": r.breakeven_GBps}
+
+
 # ------------------------------------------------ allocating conveniences
 
 def compress(x, counts, stream=None):
@@ -291,3 +333,13 @@ def decompress_reduce(buf, n, num_chunks, in_offsets=None, stream=None, check=Tr
             raise ZcError(ZC_ECORRUPT, "zc_decompress_reduce: %s in chunk %d"
                           % (REASONS.get(st >> 24, st >> 24), st & 0xFFFFFF))
     return out, status
+
+
+def estimate(x, d_counts, samples_per_chunk=8, stream=None):
+    """Estimated stream bytes per chunk (int64 device tensor)."""
+    import torch
+    est = torch.empty(max(d_counts.numel(), 1), dtype=torch.int64, device=x.device)
+    r = zc_estimate(x, d_counts, x.numel(), samples_per_chunk, est, stream=stream)
+    if r != ZC_OK:
+        raise ZcError(r, "zc_estimate")
+    return est[:d_counts.numel()]

@@ -164,3 +164,17 @@ def test_device_split_argument_errors_before_any_gpu_work():
                                  V(0x4000), V(0x5000), big, None) == zc.ZC_EINVAL
     assert lib.zc_compress_dev(None, None, 0, 0, None, 0, None, None, None, 0,
                                None) == zc.ZC_OK
+
+
+def test_estimate_argument_errors_before_any_gpu_work():
+    lib = zc.lib()
+    import ctypes as ct
+    V = ct.c_void_p
+    assert lib.zc_estimate(V(0x1000), V(0x2000), 2, 10, 0, V(0x3000), None) == zc.ZC_EINVAL
+    assert lib.zc_estimate(V(0x1000), V(0x2000), -1, 10, 4, V(0x3000), None) == zc.ZC_EINVAL
+    assert lib.zc_estimate(V(0x1000), V(0x2000), 2, -1, 4, V(0x3000), None) == zc.ZC_EINVAL
+    assert lib.zc_estimate(V(0x1000), None, 2, 10, 4, V(0x3000), None) == zc.ZC_EINVAL
+    assert lib.zc_estimate(V(0x1000), V(0x2000), 2, 10, 4, None, None) == zc.ZC_EINVAL
+    assert lib.zc_estimate(None, V(0x2000), 2, 10, 4, V(0x3000), None) == zc.ZC_EINVAL
+    assert lib.zc_estimate(None, None, 0, 5, 4, None, None) == zc.ZC_EINVAL
+    assert lib.zc_estimate(None, None, 0, 0, 4, None, None) == zc.ZC_OK
