@@ -76,6 +76,10 @@ def lib():
                                    ct.c_int64, i64p, ct.POINTER(_Stats)]
         L.zco_reduce_bf16_f32.argtypes = [ct.c_void_p, ct.c_int64, ct.c_int, ct.c_void_p]
         L.zco_reduce_bf16_f32.restype = None
+        L.zco_reduce_bf16_bf16.argtypes = [ct.c_void_p, ct.c_int64, ct.c_int, ct.c_void_p]
+        L.zco_reduce_bf16_bf16.restype = None
+        L.zco_f32_to_bf16.argtypes = [ct.c_float]
+        L.zco_f32_to_bf16.restype = ct.c_uint16
         L.zco_decompress.argtypes = [ct.c_void_p, ct.c_int64, i64p, i64p,
                                      ct.c_int, ct.c_void_p, ip]
         _lib = L
@@ -223,4 +227,20 @@ def reduce_bf16_f32(x: np.ndarray, n: int, num_chunks: int) -> np.ndarray:
     assert x.size == n * num_chunks
     out = np.empty(n, np.float32)
     lib().zco_reduce_bf16_f32(x.ctypes.data, n, num_chunks, out.ctypes.data)
+    return out
+
+
+def f32_to_bf16(x) -> np.ndarray:
+    """fp32 values to bf16 bit patterns, to nearest with ties to even."""
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    f = lib().zco_f32_to_bf16
+    return np.array([f(float(v)) for v in x], np.uint16)
+
+
+def reduce_bf16_bf16(x: np.ndarray, n: int, num_chunks: int) -> np.ndarray:
+    """Chunk-order fp32 sums rounded once to bf16 (uint16 bit patterns)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    assert x.size == n * num_chunks
+    out = np.empty(n, np.uint16)
+    lib().zco_reduce_bf16_bf16(x.ctypes.data, n, num_chunks, out.ctypes.data)
     return out

@@ -624,3 +624,44 @@ void zco_reduce_bf16_f32(const uint16_t *x, int64_t n, int num_chunks,
         out[i] = acc;
     }
 }
+
+/* fp32 to bf16 with round to nearest, ties to even, at bf16's precision and
+ * range.  The two bf16 values that bracket x (the one toward zero and the next
+ * one out, 2^128 standing for the step past the largest finite value) are
+ * compared by distance in double precision, where the differences are exact;
+ * a tie takes the one with an even last significand bit.  A NaN becomes the
+ * quiet NaN 0x7FC0; infinities and zeros keep their sign. */
+uint16_t zco_f32_to_bf16(float x)
+{
+    uint32_t u;
+    uint16_t lo, hi;
+    double ax, dlo, dhi;
+    memcpy(&u, &x, sizeof u);
+    if (isnan(x))
+        return 0x7FC0;
+    lo = (uint16_t)(u >> 16);
+    if ((u & 0xFFFFu) == 0 || isinf(x))
+        return lo;
+    hi = (uint16_t)(lo + 1);
+    ax = fabs((double)x);
+    dlo = fabs((double)bf16_to_f32(lo));
+    dhi = ((hi & 0x7FFF) == 0x7F80) ? ldexp(1.0, 128) : fabs((double)bf16_to_f32(hi));
+    if (ax - dlo < dhi - ax)
+        return lo;
+    if (dhi - ax < ax - dlo)
+        return hi;
+    return (lo & 1) ? hi : lo;
+}
+
+void zco_reduce_bf16_bf16(const uint16_t *x, int64_t n, int num_chunks,
+                          uint16_t *out)
+{
+    int64_t i;
+    int c;
+    for (i = 0; i < n; ++i) {
+        float acc = 0.0f;
+        for (c = 0; c < num_chunks; ++c)
+            acc = acc + bf16_to_f32(x[(int64_t)c * n + i]);
+        out[i] = zco_f32_to_bf16(acc);
+    }
+}

@@ -76,6 +76,14 @@ int zco_decompress(const uint8_t *in, int64_t in_bytes, const int64_t *offsets,
 void zco_reduce_bf16_f32(const uint16_t *x, int64_t n, int num_chunks,
                          float *out);
 
+/* fp32 to bf16, round to nearest with ties to even (NaN -> 0x7FC0). */
+uint16_t zco_f32_to_bf16(float x);
+
+/* The same sum delivered in bf16: accumulated in fp32 exactly as
+ * zco_reduce_bf16_f32, then rounded once, to nearest with ties to even. */
+void zco_reduce_bf16_bf16(const uint16_t *x, int64_t n, int num_chunks,
+                          uint16_t *out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,3 +57,70 @@ def test_infinities_and_subnormals(oracle):
     # (no flush of subnormals to zero)
     out = oracle.reduce_bf16_f32(np.full(64, 0x0001, np.uint16), 1, 64)
     assert out[0] == np.float32(2.0 ** -127)
+
+
+# ---- fp32 -> bf16 rounding (round to nearest, ties to even) and the bf16 sum
+
+def f32(bits):
+    return np.asarray(bits, np.uint32).view(np.float32)
+
+
+def test_rounding_hand_cases(oracle):
+    cases = {
+        0x3F800000: 0x3F80,   # 1.0 exact
+        0x3F808000: 0x3F80,   # 1 + 2^-8: halfway, 1.0 has the even last bit
+        0x3F818000: 0x3F82,   # 1 + 3 * 2^-8: halfway, rounds up to the even one
+        0x3F808001: 0x3F81,   # just above halfway
+        0x3F807FFF: 0x3F80,   # just below halfway
+        0xBF808001: 0xBF81,   # sign is kept
+        0x7F7F7FFF: 0x7F7F,   # below the overflow midpoint: largest finite
+        0x7F7F8000: 0x7F80,   # the overflow midpoint ties to infinity (even)
+        0xFF7F8000: 0xFF80,
+        0x7F800000: 0x7F80,   # infinities and zeros stay
+        0xFF800000: 0xFF80,
+        0x80000000: 0x8000,
+        0x00008000: 0x0000,   # halfway to the smallest bf16 subnormal: to even 0
+        0x00018000: 0x0002,   # halfway between subnormals 1 and 2: to even 2
+        0x7FC00001: 0x7FC0,   # NaNs become the quiet NaN
+        0xFF800001: 0x7FC0,
+    }
+    got = oracle.f32_to_bf16(f32(list(cases)))
+    assert [hex(v) for v in got] == [hex(v) for v in cases.values()]
+
+
+def test_rounding_keeps_every_bf16_value(oracle):
+    b = np.arange(1 << 16, dtype=np.uint32)
+    got = oracle.f32_to_bf16(f32(b << 16)).astype(np.uint32)
+    nan = ((b & 0x7F80) == 0x7F80) & ((b & 0x7F) != 0)
+    assert np.array_equal(got[~nan], b[~nan])
+    assert np.all(got[nan] == 0x7FC0)
+
+
+def test_rounding_matches_torch_cpu_conversion(oracle):
+    # torch's CPU float32 -> bfloat16 conversion rounds to nearest even; on
+    # random bit patterns and near-halfway values the two must agree (NaN
+    # only as NaN)
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(17)
+    u = rng.integers(0, 1 << 32, 60000, dtype=np.uint64).astype(np.uint32)
+    ties = (rng.integers(0, 1 << 16, 20000, dtype=np.uint32) << 16) | 0x8000
+    near = ties + rng.integers(-2, 3, 20000).astype(np.int64).astype(np.uint32)
+    bits = np.concatenate([u, ties, near])
+    x = f32(bits)
+    got = oracle.f32_to_bf16(x)
+    want = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    isnan = np.isnan(x)
+    assert np.array_equal(got[~isnan], want[~isnan])
+    assert np.all(got[isnan] == 0x7FC0)
+
+
+def test_bf16_sum_rounds_once_at_the_end(oracle):
+    # 1 + 2^-8 + 2^-8: the fp32 sum is 1 + 2^-7 exactly, one bf16 step above
+    # 1.0; rounding after every addition would have kept 1.0 (each partial
+    # sum 1 + 2^-8 is a tie that goes to the even 1.0)
+    x = np.array([BF16_ONE, 0x3B80, 0x3B80], np.uint16)
+    assert oracle.reduce_bf16_bf16(x, 1, 3)[0] == 0x3F81
+    assert oracle.reduce_bf16_bf16(x[:2].copy(), 1, 2)[0] == 0x3F80   # a tie: to even 1.0
+    # a sum past the largest bf16 rounds to infinity
+    big = np.array([0x7F7F, 0x7F7F], np.uint16)
+    assert oracle.reduce_bf16_bf16(big, 1, 2)[0] == 0x7F80
