@@ -238,6 +238,21 @@ int zc_decompress_reduce(const void* d_in, size_t in_bytes,
                          void* d_scratch, size_t scratch_bytes, void* stream);
 
 /*
+ * zc_decompress_reduce delivering bf16: the same chunk-order fp32 sums,
+ * each rounded once to bf16, to nearest with ties to even (a sum beyond the
+ * largest bf16 becomes infinity; a NaN sum becomes 0x7FC0).  d_out is device
+ * uint16[n] of bf16 bit patterns, 16-byte aligned; everything else as for
+ * zc_decompress_reduce.  This is the dtype a bf16 gradient shard is kept in
+ * (pith.science, Figure 5: the zipped ReduceScatter hands the sum back to
+ * training).
+ */
+int zc_decompress_reduce_bf16(const void* d_in, size_t in_bytes,
+                              const int64_t* in_offsets, int64_t n,
+                              int32_t num_chunks, uint16_t* d_out,
+                              int32_t* d_status, void* d_scratch,
+                              size_t scratch_bytes, void* stream);
+
+/*
  * Adaptive switch (abstract, technique (3): compressed or plain collective,
  * chosen from the workload and the system; pith.science, Figure 15 caption:
  * the adaptive switcher).  zc_estimate predicts the compressed size from a

@@ -1373,15 +1373,29 @@ __device__ inline void add8(float (&acc)[8], const uint4 v)
     acc[7] = acc[7] + bf16_hi(v.w);
 }
 
+// fp32 to bf16, round to nearest with ties to even: adding 0x7FFF plus the
+// kept part's last bit carries into the kept half exactly when the dropped
+// half is above one half, or equal to it with an odd kept part (overflow
+// carries into the exponent and gives infinity).  NaN gives 0x7FC0.
+__device__ inline uint32_t f32_to_bf16_rne(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 // Receive side of a reduce-scatter (pith.science, Figure 5: zipccl
 // ReduceScatter): num_chunks decoded contributions of n bf16 values each
 // (contribution c at x + c n) summed element by element in fp32, in chunk
-// order, from +0.  Each thread owns 8 consecutive elements; rows are read
-// with 16-byte nontemporal loads, 8 contributions in flight at a time, and
-// the sums are added strictly in chunk order.
+// order, from +0; BF16OUT rounds each sum once to bf16 (to nearest even).
+// Each thread owns 8 consecutive elements; rows are read with 16-byte
+// nontemporal loads, 8 contributions in flight at a time, and the sums are
+// added strictly in chunk order.
+template <bool BF16OUT>
 __global__ __launch_bounds__(kBlock)
 void zc_reduce_kernel(const uint16_t* __restrict__ x, uint64_t n, int32_t num_chunks,
-                      float* __restrict__ out)
+                      void* __restrict__ out)
 {
     const uint64_t i0 = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) * 8;
     if (i0 >= n)
@@ -1404,16 +1418,30 @@ void zc_reduce_kernel(const uint16_t* __restrict__ x, uint64_t n, int32_t num_ch
         }
         for (; c < num_chunks; ++c)
             add8(acc, ld_nt4(p + static_cast<uint64_t>(c) * n));
-        st_nt4(out + i0, make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]),
-                                    __float_as_uint(acc[2]), __float_as_uint(acc[3])));
-        st_nt4(out + i0 + 4, make_uint4(__float_as_uint(acc[4]), __float_as_uint(acc[5]),
-                                        __float_as_uint(acc[6]), __float_as_uint(acc[7])));
+        if (BF16OUT) {
+            uint32_t h[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                h[j] = f32_to_bf16_rne(acc[j]);
+            st_nt4(static_cast<uint16_t*>(out) + i0,
+                   make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                              h[6] | (h[7] << 16)));
+        } else {
+            float* o = static_cast<float*>(out) + i0;
+            st_nt4(o, make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]),
+                                 __float_as_uint(acc[2]), __float_as_uint(acc[3])));
+            st_nt4(o + 4, make_uint4(__float_as_uint(acc[4]), __float_as_uint(acc[5]),
+                                     __float_as_uint(acc[6]), __float_as_uint(acc[7])));
+        }
     } else {
         for (int j = 0; j < 8 && i0 + j < n; ++j) {
             float a = 0.0f;
             for (int32_t c = 0; c < num_chunks; ++c)
                 a = a + bf16_lo(x[static_cast<uint64_t>(c) * n + i0 + j]);
-            out[i0 + j] = a;
+            if (BF16OUT)
+                static_cast<uint16_t*>(out)[i0 + j] = static_cast<uint16_t>(f32_to_bf16_rne(a));
+            else
+                static_cast<float*>(out)[i0 + j] = a;
         }
     }
 }
@@ -1723,6 +1751,46 @@ uint64_t dev_tables_offset(int64_t total, int32_t num_chunks)
 
 }  // namespace
 
+namespace {
+
+// Decode num_chunks streams of n values into the staging buffer, then sum
+// them (fp32 output, or bf16 when `bf16`).
+int decompress_reduce(const void* d_in, size_t in_bytes, const int64_t* in_offsets, int64_t n,
+                      int32_t num_chunks, void* d_out, bool bf16, int32_t* d_status,
+                      void* d_scratch, size_t scratch_bytes, void* stream)
+{
+    if (n < 0 || n > ZC_MAX_CHUNK_VALUES || num_chunks < 0)
+        return ZC_EINVAL;
+    if (n == 0)
+        return ZC_OK;
+    if (!d_out || !d_status || (num_chunks > 0 && (!d_in || !d_scratch)))
+        return ZC_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(d_out) & 15) || (reinterpret_cast<uintptr_t>(d_scratch) & 15))
+        return ZC_EINVAL;
+    if (scratch_bytes < 2ull * static_cast<uint64_t>(n) * static_cast<uint64_t>(num_chunks))
+        return ZC_ENOSPC;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (num_chunks > 0) {
+        std::vector<int64_t> counts(static_cast<size_t>(num_chunks), n);
+        const int r = zc_decompress(d_in, in_bytes, in_offsets, counts.data(), num_chunks,
+                                    static_cast<uint16_t*>(d_scratch), d_status, stream);
+        if (r != ZC_OK)
+            return r;
+    }
+    const uint64_t threads = (static_cast<uint64_t>(n) + 7) / 8;
+    const dim3 grid(static_cast<uint32_t>((threads + kBlock - 1) / kBlock));
+    const uint16_t* x = static_cast<const uint16_t*>(d_scratch);
+    if (bf16)
+        hipLaunchKernelGGL(zc_reduce_kernel<true>, grid, dim3(kBlock), 0, s, x,
+                           static_cast<uint64_t>(n), num_chunks, d_out);
+    else
+        hipLaunchKernelGGL(zc_reduce_kernel<false>, grid, dim3(kBlock), 0, s, x,
+                           static_cast<uint64_t>(n), num_chunks, d_out);
+    return hipGetLastError() == hipSuccess ? ZC_OK : ZC_EHIP;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t zc_chunk_bound(int64_t n)
@@ -1950,29 +2018,16 @@ int zc_decompress_reduce(const void* d_in, size_t in_bytes, const int64_t* in_of
                          int64_t n, int32_t num_chunks, float* d_out, int32_t* d_status,
                          void* d_scratch, size_t scratch_bytes, void* stream)
 {
-    if (n < 0 || n > ZC_MAX_CHUNK_VALUES || num_chunks < 0)
-        return ZC_EINVAL;
-    if (n == 0)
-        return ZC_OK;
-    if (!d_out || !d_status || (num_chunks > 0 && (!d_in || !d_scratch)))
-        return ZC_EINVAL;
-    if ((reinterpret_cast<uintptr_t>(d_out) & 15) || (reinterpret_cast<uintptr_t>(d_scratch) & 15))
-        return ZC_EINVAL;
-    if (scratch_bytes < 2ull * static_cast<uint64_t>(n) * static_cast<uint64_t>(num_chunks))
-        return ZC_ENOSPC;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (num_chunks > 0) {
-        std::vector<int64_t> counts(static_cast<size_t>(num_chunks), n);
-        const int r = zc_decompress(d_in, in_bytes, in_offsets, counts.data(), num_chunks,
-                                    static_cast<uint16_t*>(d_scratch), d_status, stream);
-        if (r != ZC_OK)
-            return r;
-    }
-    const uint64_t threads = (static_cast<uint64_t>(n) + 7) / 8;
-    hipLaunchKernelGGL(zc_reduce_kernel, dim3(static_cast<uint32_t>((threads + kBlock - 1) / kBlock)),
-                       dim3(kBlock), 0, s, static_cast<const uint16_t*>(d_scratch),
-                       static_cast<uint64_t>(n), num_chunks, d_out);
-    return hipGetLastError() == hipSuccess ? ZC_OK : ZC_EHIP;
+    return decompress_reduce(d_in, in_bytes, in_offsets, n, num_chunks, d_out, false, d_status,
+                             d_scratch, scratch_bytes, stream);
+}
+
+int zc_decompress_reduce_bf16(const void* d_in, size_t in_bytes, const int64_t* in_offsets,
+                              int64_t n, int32_t num_chunks, uint16_t* d_out, int32_t* d_status,
+                              void* d_scratch, size_t scratch_bytes, void* stream)
+{
+    return decompress_reduce(d_in, in_bytes, in_offsets, n, num_chunks, d_out, true, d_status,
+                             d_scratch, scratch_bytes, stream);
 }
 
 int zc_decompress(const void* d_in, size_t in_bytes, const int64_t* in_offsets,

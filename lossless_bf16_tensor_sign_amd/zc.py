@@ -86,6 +86,8 @@ def lib():
                                            ct.c_int32, ct.c_void_p, ct.c_void_p, ct.c_void_p,
                                            ct.c_size_t, ct.c_void_p]
         L.zc_decompress_reduce.restype = ct.c_int
+        L.zc_decompress_reduce_bf16.argtypes = L.zc_decompress_reduce.argtypes
+        L.zc_decompress_reduce_bf16.restype = ct.c_int
         L.zc_estimate.argtypes = [ct.c_void_p, ct.c_void_p, ct.c_int32, ct.c_int64,
                                   ct.c_int32, ct.c_void_p, ct.c_void_p]
         L.zc_estimate.restype = ct.c_int
@@ -203,8 +205,9 @@ def zc_decompress_dev(d_in, d_counts, total_values, d_out, d_status, d_ws, d_in_
 
 
 def zc_decompress_reduce(d_in, n, num_chunks, d_out, d_status, d_scratch, in_offsets=None,
-                         stream=None, in_bytes=None, scratch_bytes=None) -> int:
-    """Queue decode of num_chunks streams of n values and their fp32 sum."""
+                         stream=None, in_bytes=None, scratch_bytes=None, bf16=False) -> int:
+    """Queue decode of num_chunks streams of n values and their fp32 sum
+    (rounded once to bf16 into a 16-bit d_out when bf16=True)."""
     nb = d_in.numel() * d_in.element_size() if in_bytes is None else in_bytes
     sb = d_scratch.numel() * d_scratch.element_size() if scratch_bytes is None else scratch_bytes
     if in_offsets is not None:
@@ -213,9 +216,9 @@ def zc_decompress_reduce(d_in, n, num_chunks, d_out, d_status, d_scratch, in_off
             raise ValueError("in_offsets has fewer entries than num_chunks")
     else:
         off, op = None, None
-    return int(lib().zc_decompress_reduce(_ptr(d_in), nb, op, int(n), int(num_chunks),
-                                          _ptr(d_out), _ptr(d_status), _ptr(d_scratch), sb,
-                                          _stream(stream)))
+    fn = lib().zc_decompress_reduce_bf16 if bf16 else lib().zc_decompress_reduce
+    return int(fn(_ptr(d_in), nb, op, int(n), int(num_chunks), _ptr(d_out), _ptr(d_status),
+                  _ptr(d_scratch), sb, _stream(stream)))
 
 
 def zc_estimate(d_in, d_counts, total_values, samples_per_chunk, d_est, stream=None) -> int:
@@ -313,17 +316,18 @@ def decompress_dev(buf, d_counts, total_values, d_in_offsets=None, stream=None, 
     return out, status
 
 
-def decompress_reduce(buf, n, num_chunks, in_offsets=None, stream=None, check=True):
+def decompress_reduce(buf, n, num_chunks, in_offsets=None, stream=None, check=True, bf16=False):
     """Decode num_chunks streams of n values each and sum them in fp32.
 
-    Returns (float32 device tensor of n sums, int32 device status)."""
+    Returns (device tensor of n sums: float32, or int16 bf16 bit patterns
+    when bf16=True; int32 device status)."""
     import torch
     dev = buf.device
-    out = torch.empty(max(int(n), 4), dtype=torch.float32, device=dev)
+    out = torch.empty(max(int(n), 8), dtype=torch.int16 if bf16 else torch.float32, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     scratch = torch.empty(max(2 * int(n) * int(num_chunks), 16), dtype=torch.uint8, device=dev)
     r = zc_decompress_reduce(buf, n, num_chunks, out, status, scratch, in_offsets=in_offsets,
-                             stream=stream)
+                             stream=stream, bf16=bf16)
     if r != ZC_OK:
         raise ZcError(r, "zc_decompress_reduce")
     out = out[:int(n)]

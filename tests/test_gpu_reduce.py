@@ -159,3 +159,64 @@ def test_reduce_full_size_gradient_buffer(oracle):
     idx = np.unique(np.concatenate([rng.integers(0, n, 4096), [0, 1, n - 2, n - 1]]))
     cols = np.ascontiguousarray(w.reshape(c, n)[:, idx])
     same_f32(out.cpu().numpy()[idx], oracle.reduce_bf16_f32(cols.ravel(), idx.size, c))
+
+
+# ---- the same sums delivered in bf16 (rounded once, to nearest even) ----
+
+def gpu_reduce_bf16(w, n, c):
+    buf, sizes = zc.compress(to_dev(w), [n] * c)
+    out, status = zc.decompress_reduce(buf, n, c, check=False, bf16=True)
+    torch.cuda.synchronize()
+    return int(status.item()), out.cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("n,c", [(20000, 8), (20003, 8), (24576, 11), (1, 5), (7, 3),
+                                 (65536 + 40, 17)])
+def test_reduce_bf16_matches_oracle(oracle, n, c):
+    w = special_mix(n * c, 2000 + n + c)
+    say("reduce bf16 n=%d chunks=%d" % (n, c))
+    st, got = gpu_reduce_bf16(w, n, c)
+    assert st == 0, "status %#x" % st
+    want = oracle.reduce_bf16_bf16(w, n, c)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, "first differing sum at %d: %#x vs %#x" % (bad[0], got[bad[0]],
+                                                                  want[bad[0]])
+
+
+def test_reduce_bf16_rounds_once_at_the_end(oracle):
+    # 1 + 2^-8 + 2^-8 = 1 + 2^-7 in fp32 (one bf16 step above 1.0); two
+    # chunks give the tie 1 + 2^-8, which goes to the even 1.0; the largest
+    # bf16 twice overflows to infinity
+    n = 1024
+    rows = [np.full(n, v, np.uint16) for v in (0x3F80, 0x3B80, 0x3B80)]
+    st, got = gpu_reduce_bf16(np.concatenate(rows), n, 3)
+    assert st == 0 and np.all(got == 0x3F81)
+    st, got = gpu_reduce_bf16(np.concatenate(rows[:2]), n, 2)
+    assert st == 0 and np.all(got == 0x3F80)
+    st, got = gpu_reduce_bf16(np.full(2 * n, 0x7F7F, np.uint16), n, 2)
+    assert st == 0 and np.all(got == 0x7F80)
+
+
+def test_reduce_bf16_full_size_gradient_buffer(oracle):
+    w, cnt = synth.make(3, workers=8)
+    c, n = len(cnt), int(cnt[0])
+    say("reduce bf16 full size: %d x %d" % (c, n))
+    x = to_dev(w)
+    buf, sizes = zc.compress(x, cnt)
+    out, status = zc.decompress_reduce(buf, n, c, check=False, bf16=True)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    # every position: chunk-order PyTorch fp32 additions, then PyTorch's
+    # conversion to bfloat16 (round to nearest even)
+    xs = x.view(c, n)
+    acc = torch.zeros(n, dtype=torch.float32, device=DEV)
+    for k in range(c):
+        acc = acc + (xs[k].to(torch.int32) << 16).view(torch.float32)
+    want = acc.to(torch.bfloat16).view(torch.int16)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), want)
+    rng = np.random.default_rng(37)
+    idx = np.unique(np.concatenate([rng.integers(0, n, 4096), [0, n - 1]]))
+    cols = np.ascontiguousarray(w.reshape(c, n)[:, idx])
+    got = out.cpu().numpy().view(np.uint16)[idx]
+    assert np.array_equal(got, oracle.reduce_bf16_bf16(cols.ravel(), idx.size, c))
