@@ -158,6 +158,10 @@ def main():
                     help="CPU seconds (summed over threads) of the oracle run")
     ap.add_argument("--copies", type=int, default=3,
                     help="timed plain device copies of the input after the steps")
+    ap.add_argument("--flush", choices=["clean", "write"], default="clean",
+                    help="cache state before each timed call: 'write' = 1 GiB written "
+                         "(the Infinity Cache is left full of the flush's dirty lines); "
+                         "'clean' = the same 1 GiB then read back (cold and clean)")
     ap.add_argument("--device-counts", action="store_true",
                     help="time zc_compress_dev / zc_decompress_dev, with the chunk "
                          "counts in device memory (the MoE router's split)")
@@ -205,11 +209,20 @@ def main():
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
+    def evict(v):
+        # 1 GiB written, so that no input or output of the previous call is
+        # left in L2 or the Infinity Cache; with --flush clean it is then read
+        # back, which writes the flush's own dirty lines out before the timed
+        # call instead of during it
+        flush.fill_(v & 0xFF)
+        if args.flush == "clean":
+            flush.sum(dtype=torch.int64)
+
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
     def step(times=None, i=0):
-        flush.fill_(i & 0xFF)
+        evict(i)
         e0, e1, e2, e3 = ev(), ev(), ev(), ev()
         e0.record(stream)
         if args.device_counts:
@@ -219,7 +232,7 @@ def main():
         e1.record(stream)
         if r != zc.ZC_OK:
             raise zc.ZcError(r, "zc_compress")
-        flush.fill_((i + 1) & 0xFF)
+        evict(i + 1)
         e2.record(stream)
         if args.reduce:
             r = zc.zc_decompress_reduce(buf, shard, len(counts), red, status, y, stream=stream)
@@ -267,7 +280,7 @@ def main():
     # calibration kernel of the byte counters
     tcopy = []
     for i in range(args.copies):
-        flush.fill_((i + 7) & 0xFF)
+        evict(i + 7)
         e0, e1 = ev(), ev()
         e0.record(stream)
         y.copy_(x)
@@ -319,6 +332,8 @@ def main():
                      "shards of %d values)" % (len(counts), shard)
                      if args.reduce else "zc_compress + zc_decompress") +
                     " of every chunk, 1 GiB cache flush before each call (untimed)",
+            "flush": ("1 GiB written then read back (caches cold and clean)"
+                      if args.flush == "clean" else "1 GiB written (caches cold, dirty)"),
         },
         "compress_GBps": round(comp_gbps, 2),
         "decompress_GBps": round(dec_gbps, 2),
@@ -359,7 +374,7 @@ def main():
     est = torch.empty(len(counts), dtype=torch.int64, device=dev)
     te = []
     for i in range(3):
-        flush.fill_((i + 11) & 0xFF)
+        evict(i + 11)
         e0, e1 = ev(), ev()
         e0.record(stream)
         r = zc.zc_estimate(x, dcounts, n, 8, est, stream=stream)

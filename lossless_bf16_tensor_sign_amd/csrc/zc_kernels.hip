@@ -53,6 +53,12 @@
 #ifndef ZC_ENC_INTERLEAVE
 #define ZC_ENC_INTERLEAVE 1      // equal-size chunks: hand out tiles round-robin
 #endif
+#ifndef ZC_EARLY_LOAD
+#define ZC_EARLY_LOAD 1          // grid-ordered full tiles: loads issued before the table set-up
+#endif
+#ifndef ZC_ENC_TICKETS
+#define ZC_ENC_TICKETS 0         // round-robin tiles numbered by per-chunk tickets (else by grid position)
+#endif
 #ifndef ZC_STATUS_STRIDE
 #define ZC_STATUS_STRIDE 8       // 8-byte look-back status words, one per this many
 #endif
@@ -68,8 +74,14 @@
 #ifndef ZC_MIXED_PAIR
 #define ZC_MIXED_PAIR 1          // waves with raw groups may also emit pairs
 #endif
+#ifndef ZC_ENC_BATCH
+#define ZC_ENC_BATCH 0           // compress: a step's table lookups issued together (1 pairs, 2 escapes)
+#endif
+#ifndef ZC_DEC_RING
+#define ZC_DEC_RING 1            // decompress: steps of sign+mantissa bytes prefetched ahead
+#endif
 #ifndef ZC_DEC_WAVES
-#define ZC_DEC_WAVES 7           // decompress occupancy target, waves per SIMD
+#define ZC_DEC_WAVES 8           // decompress occupancy target, waves per SIMD
 #endif
 
 namespace {
@@ -104,17 +116,17 @@ static_assert(ZC_T1_NSYM == 17, "table_id 1 has 17 symbols");
 static_assert(ZC_T1_TAIL_OK == 1, "long code words must share the all-ones prefix");
 static_assert(ZC_T1_MAXLEN <= kLutBits + kTailBits, "code words must fit two lookup levels");
 static_assert(kEscLen + 8 <= 32, "escape payload must fit the window");
-static_assert(kLutBits >= 8 && (1 << kLutBits) == 16 * kBlock,
-              "the first level is loaded as one 16-byte word per thread");
+static_assert(kLutBits >= 8 && kLutBits <= 12, "first level of 256 to 4096 byte entries");
+constexpr int kLutWords = (1 << kLutBits) / 4;     // first level, 32-bit words
+constexpr int kLutPer = (kLutWords + kBlock - 1) / kBlock;   // words loaded per thread
 
 __constant__ __align__(16) uint8_t c_lut[1 << kLutBits] = ZC_T1_LUT_INIT;
-__constant__ uint8_t c_len[ZC_T1_NSYM] = ZC_T1_LEN_INIT;
-__constant__ uint32_t c_code[ZC_T1_NSYM] = ZC_T1_CODE_INIT;
 
 // The lengths and second-level entries of table_id 1 as compile-time
 // constants: the decoder's threads pick theirs with selects, so its small
 // LDS tables are set up without a memory round trip.
 constexpr uint32_t kLenT1[ZC_T1_NSYM] = ZC_T1_LEN_INIT;
+constexpr uint32_t kCodeT1[ZC_T1_NSYM] = ZC_T1_CODE_INIT;
 constexpr uint32_t kTailT1[1 << kTailBits] = ZC_T1_TAIL_INIT;
 
 __device__ inline uint32_t len_of(uint32_t s)
@@ -123,6 +135,15 @@ __device__ inline uint32_t len_of(uint32_t s)
 #pragma unroll
     for (int i = 0; i < ZC_T1_NSYM; ++i)
         v = s == static_cast<uint32_t>(i) ? kLenT1[i] : v;
+    return v;
+}
+
+__device__ inline uint32_t code_of(uint32_t s)
+{
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < ZC_T1_NSYM; ++i)
+        v = s == static_cast<uint32_t>(i) ? kCodeT1[i] : v;
     return v;
 }
 
@@ -137,11 +158,26 @@ __device__ inline uint32_t tail_of(uint32_t i)
 
 // Chunks of one launch.  Work item = one tile; an empty chunk gets one item
 // that only writes its header.
+// Compress tile orders.  Tickets: workgroups take the chunks round-robin and
+// number their tiles from per-chunk counters.  Chunks: grid position = tile
+// index, chunk by chunk.  RoundRobin: grid position g is tile g / C of chunk
+// g mod C (every chunk has the same number of tiles).
+constexpr uint32_t kOrderTickets = 0;
+constexpr uint32_t kOrderChunks = 1;
+constexpr uint32_t kOrderRoundRobin = 2;
+
+__host__ __device__ inline uint32_t tile_order(uint32_t uniform_tiles)
+{
+    if (!ZC_ENC_INTERLEAVE || !uniform_tiles)
+        return kOrderChunks;
+    return ZC_ENC_TICKETS ? kOrderTickets : kOrderRoundRobin;
+}
+
 struct ChunkTable {
     int32_t nchunks;
     uint32_t nitems;
     uint32_t uniform_tiles;        // > 0: every chunk has this many tiles
-    uint32_t grid_order;           // compress: tile order from the grid, not from tickets
+    uint32_t grid_order;           // compress tile order: kOrderTickets, kOrderChunks or kOrderRoundRobin
     uint32_t spin_limit;           // compress: look-back polls before recomputing
     uint32_t item_begin[kMaxChunks + 1];
     uint32_t n[kMaxChunks];
@@ -324,16 +360,13 @@ struct TileCtx {
     int c;
 };
 
-// Loads and splits this wave's four steps of the tile: raw bytes are stored
-// at once, exponents stay packed 4 per word, the maximum is returned.
-// FULL = 8192 values at a 16-byte aligned address.
+// Loads this wave's four steps of the tile (FULL = 8192 values at a 16-byte
+// aligned address; otherwise missing members read as 0).
 template <bool FULL>
-__device__ inline uint32_t load_split(const TileCtx& x, uint32_t (&ex)[kQSteps][2])
+__device__ inline void load_tile(const TileCtx& x, uint4 (&v)[kQSteps])
 {
     const uint32_t k0 = x.wave * kQSteps;
     const char* sbase = reinterpret_cast<const char*>(x.src + x.base) + k0 * 1024 + x.lane * 16;
-    char* rbase = reinterpret_cast<char*>(x.dst + x.G.R + x.base) + k0 * 512 + x.lane * 8;
-    uint4 v[kQSteps];
 #pragma unroll
     for (int k = 0; k < kQSteps; ++k) {
         if (FULL) {
@@ -350,6 +383,16 @@ __device__ inline uint32_t load_split(const TileCtx& x, uint32_t (&ex)[kQSteps][
             v[k].w = w[6] | (w[7] << 16);
         }
     }
+}
+
+// Splits the loaded steps: raw bytes are stored at once, exponents stay
+// packed 4 per word, the maximum exponent is returned.
+template <bool FULL>
+__device__ inline uint32_t split_tile(const TileCtx& x, const uint4 (&v)[kQSteps],
+                                      uint32_t (&ex)[kQSteps][2])
+{
+    const uint32_t k0 = x.wave * kQSteps;
+    char* rbase = reinterpret_cast<char*>(x.dst + x.G.R + x.base) + k0 * 512 + x.lane * 8;
     uint32_t mx = 0;
 #pragma unroll
     for (int k = 0; k < kQSteps; ++k) {
@@ -378,6 +421,14 @@ __device__ inline uint32_t load_split(const TileCtx& x, uint32_t (&ex)[kQSteps][
         }
     }
     return mx >> 7;   // missing members were loaded as 0
+}
+
+template <bool FULL>
+__device__ inline uint32_t load_split(const TileCtx& x, uint32_t (&ex)[kQSteps][2])
+{
+    uint4 v[kQSteps];
+    load_tile<FULL>(x, v);
+    return split_tile<FULL>(x, v, ex);
 }
 
 // Decoupled look-back over per-tile status words (flag in bits 62-63:
@@ -502,7 +553,7 @@ __device__ inline uint32_t look_back_resolve(uint64_t* __restrict__ status, uint
 // which no lane of the wave has an escape appends its code words two at a
 // time (at most 28 bits per pair).
 template <bool FULL, bool MIXED>
-__device__ inline void emit_quarter(uint32_t* __restrict__ s, const EncTables& tb,
+__device__ __forceinline__ void emit_quarter(uint32_t* __restrict__ s, const EncTables& tb,
                                     const uint32_t (&dd)[kQSteps][2], uint32_t emax,
                                     uint32_t ng, uint32_t first, bool raw_mode, uint32_t off)
 {
@@ -515,6 +566,15 @@ __device__ inline void emit_quarter(uint32_t* __restrict__ s, const EncTables& t
         const uint32_t d4[2] = {dd[k][0], dd[k][1]};
         const bool esc_here = coded && (((d4[0] | d4[1]) & 0xF0F0F0F0u) != 0);
         if ((!MIXED || ZC_MIXED_PAIR) && __ballot(esc_here) == 0) {
+            // the step's table lookups are all issued before its first LDS
+            // OR, so that they cost one LDS round trip, not one per pair
+            // (no escape here: each entry is code | length << 24)
+            uint32_t es[8];
+            if constexpr ((ZC_ENC_BATCH & 1) != 0) {
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj)
+                    es[jj] = tb.esc[(d4[jj >> 2] >> (8 * (jj & 3))) & 0xFF];
+            }
 #pragma unroll
             for (int j = 0; j < 8; j += 2) {
                 uint32_t c2[2], l2[2];
@@ -522,7 +582,14 @@ __device__ inline void emit_quarter(uint32_t* __restrict__ s, const EncTables& t
                 for (int u = 0; u < 2; ++u) {
                     const int jj = j + u;
                     const uint32_t d = (d4[jj >> 2] >> (8 * (jj & 3))) & 0xFF;
-                    uint32_t c = tb.code[d], l = tb.len[d];
+                    uint32_t c, l;
+                    if constexpr ((ZC_ENC_BATCH & 1) != 0) {
+                        c = es[jj] & 0x3FFFFFu;
+                        l = es[jj] >> 24;
+                    } else {
+                        c = tb.code[d];
+                        l = tb.len[d];
+                    }
                     if (MIXED) {
                         c = raw_mode ? ((emax - d) & 0xFF) : c;
                         l = raw_mode ? 8u : l;
@@ -541,10 +608,16 @@ __device__ inline void emit_quarter(uint32_t* __restrict__ s, const EncTables& t
                 nacc &= 31;
             }
         } else {
+            uint32_t es[8];
+            if constexpr ((ZC_ENC_BATCH & 2) != 0) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    es[j] = tb.esc[(d4[j >> 2] >> (8 * (j & 3))) & 0xFF];
+            }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const uint32_t d = (d4[j >> 2] >> (8 * (j & 3))) & 0xFF;
-                uint32_t ent = tb.esc[d];
+                uint32_t ent = ((ZC_ENC_BATCH & 2) != 0) ? es[j] : tb.esc[d];
                 if (MIXED && raw_mode)
                     ent = ((emax - d) & 0xFF) | (8u << 24);
                 const bool valid = FULL || first + static_cast<uint32_t>(k * 8 + j) < ng;
@@ -615,7 +688,7 @@ __device__ inline void write_tile_index(const TileCtx& x, uint32_t toff, uint32_
 // Everything after the loads: the partial maxima of the four waves are in
 // sh.part_max (written before the barrier that precedes this call).
 template <bool FULL>
-__device__ void compress_tile_back(const TileCtx& x, uint32_t (&dd)[kQSteps][2],
+__device__ __forceinline__ void compress_tile_back(const TileCtx& x, uint32_t (&dd)[kQSteps][2],
                                    int64_t* __restrict__ comp_sizes,
                                    uint64_t* __restrict__ status, EncShared& sh)
 {
@@ -759,11 +832,32 @@ __device__ __forceinline__ void compress_body(const uint16_t* __restrict__ in,
     else
         x.c = find_chunk(tab, item);
     uint32_t ticket = 0;
-    if (!tab.grid_order && tid == 0)
+    if (tab.grid_order == kOrderTickets && tid == 0)
         ticket = atomicAdd(&tickets[x.c * kTicketStride], 1u);
+    x.n = tab.n[x.c];
+    x.first = tab.item_begin[x.c];
+    x.lane = lane;
+    x.wave = wave;
+    x.src = in + tab.voff[x.c];
+    x.dst = out + tab.boff[x.c];
+    x.G = geometry(x.n);
+    const bool aligned = (reinterpret_cast<uintptr_t>(x.src) & 15) == 0;
+
+    // A grid-ordered tile is known at once: a full one issues its loads now,
+    // so that their latency covers the table set-up below.
+    uint4 v[kQSteps];
+    bool loaded = false;
+    if (tab.grid_order != kOrderTickets) {
+        x.t = tab.grid_order == kOrderRoundRobin ? item / static_cast<uint32_t>(tab.nchunks)
+                                                 : item - x.first;
+        x.base = x.t * kTile;
+        loaded = ZC_EARLY_LOAD && x.n != 0 && aligned && x.n - x.base >= static_cast<uint32_t>(kTile);
+        if (loaded)
+            load_tile<true>(x, v);
+    }
     {
         const uint32_t s = tid < static_cast<uint32_t>(kEsc) ? tid : static_cast<uint32_t>(kEsc);
-        uint32_t code = c_code[s], len = c_len[s];
+        uint32_t code = code_of(s), len = len_of(s);
         sh.tb.code[tid] = static_cast<uint16_t>(code);
         if (s == static_cast<uint32_t>(kEsc)) {   // escape: code word, then 8 exponent bits
             code <<= 8;
@@ -776,22 +870,13 @@ __device__ __forceinline__ void compress_body(const uint16_t* __restrict__ in,
         *reinterpret_cast<uint4*>(&sh.stage[i]) = make_uint4(0, 0, 0, 0);
     if (tid == 0)
         sh.spin_limit = tab.spin_limit;
-    if (!tab.grid_order) {
+    if (tab.grid_order == kOrderTickets) {
         if (tid == 0)
             sh.tile = ticket;
         __syncthreads();
         x.t = __builtin_amdgcn_readfirstlane(sh.tile);
-    } else {
-        x.t = item - tab.item_begin[x.c];
     }
-    x.n = tab.n[x.c];
-    x.first = tab.item_begin[x.c];
     x.item = x.first + x.t;
-    x.lane = lane;
-    x.wave = wave;
-    x.src = in + tab.voff[x.c];
-    x.dst = out + tab.boff[x.c];
-    x.G = geometry(x.n);
 
     if (x.n == 0) {
         if (tid < 8)
@@ -802,10 +887,12 @@ __device__ __forceinline__ void compress_body(const uint16_t* __restrict__ in,
     }
     x.base = x.t * kTile;
     x.rem = min(x.n - x.base, static_cast<uint32_t>(kTile));
-    const bool full = x.rem == kTile && ((reinterpret_cast<uintptr_t>(x.src) & 15) == 0);
+    const bool full = x.rem == kTile && aligned;
     if (full) {
+        if (!loaded)
+            load_tile<true>(x, v);
         uint32_t dd[kQSteps][2];
-        sh.part_max[wave][lane] = load_split<true>(x, dd);
+        sh.part_max[wave][lane] = split_tile<true>(x, v, dd);
         __syncthreads();
         compress_tile_back<true>(x, dd, comp_sizes, status, sh);
     } else {
@@ -882,8 +969,8 @@ struct GlobalWindow {
     }
 };
 
-// Per-lane decoding parameters.  Coded groups look the first 12 stream bits
-// up in (symbol << 4 | length) byte entries (every code word but the three
+// Per-lane decoding parameters.  Coded groups look the first 11 stream bits
+// up in (symbol << 4 | length) byte entries (every code word but the four
 // longest fits); raw groups look their 8 bits up in entries that hold 255 - e
 // and always advance by 8.
 struct LaneCode {
@@ -958,7 +1045,7 @@ struct DecState {
 // writes the values.  MIXED: the wave has raw groups (otherwise the lookup
 // parameters are constants).
 template <bool FULL, int kSym, bool MIXED, class Win>
-__device__ inline void decode_group(const Win& win, const uint8_t* __restrict__ s_lut8,
+__device__ __forceinline__ void decode_group(const Win& win, const uint8_t* __restrict__ s_lut8,
                                     const uint16_t* __restrict__ s_tail,
                                     const uint8_t* __restrict__ s_len, const uint8_t* __restrict__ rsrc,
                                     uint16_t* __restrict__ dst, uint32_t n, uint32_t base,
@@ -975,16 +1062,22 @@ __device__ inline void decode_group(const Win& win, const uint8_t* __restrict__ 
     q.lmark = raw ? 256u : 0u;
     q.emax_eff = raw ? 255u : emax;
 
-    // sign+mantissa bytes, prefetched three steps ahead
+    // Sign+mantissa bytes, prefetched kRing steps ahead into a ring that the
+    // unrolled inner loop indexes statically: each slot is reloaded right
+    // after its last use, so no register is copied while its load is in
+    // flight and each wait leaves the younger loads and stores outstanding.
+    constexpr int kRing = ZC_DEC_RING;
+    static_assert(kSteps % kRing == 0, "whole rounds of the prefetch ring");
     const uint2* rsrc2 = reinterpret_cast<const uint2*>(rsrc + base) + lane;
-    uint2 r0 = make_uint2(0, 0), r1 = r0, r2 = r0;
-    if (FULL) {
-        r0 = ld_nt2(rsrc2);
-        r1 = ld_nt2(rsrc2 + 64);
-        r2 = ld_nt2(rsrc2 + 128);
-    }
+    uint2 ring[kRing];
+#pragma unroll
+    for (int j = 0; j < kRing; ++j)
+        ring[j] = FULL ? ld_nt2(rsrc2 + j * 64) : make_uint2(0, 0);
 #pragma unroll 1
-    for (int k = 0; k < kSteps; ++k) {
+    for (int k0 = 0; k0 < kSteps; k0 += kRing)
+#pragma unroll
+    for (int kj = 0; kj < kRing; ++kj) {
+        const int k = k0 + kj;
         // kSym symbols per 64-bit window; a lane whose code words overrun
         // the window (several escapes) decodes them again one at a time
         uint32_t e8[8];
@@ -1049,14 +1142,9 @@ __device__ inline void decode_group(const Win& win, const uint8_t* __restrict__ 
                         st.raw_coded += s_len[(emax - e8[j]) & 0xFF];
             }
         }
-        const uint2 r = r0;
-        if (FULL) {
-            r0 = r1;
-            r1 = r2;
-            if (k + 3 < kSteps)
-                r2 = ld_nt2(rsrc2 + (k + 3) * 64);
-        }
-        put_values<FULL>(dst, rsrc, n, base + k * 512 + lane * 8, r, e8, vec_out);
+        put_values<FULL>(dst, rsrc, n, base + k * 512 + lane * 8, ring[kj], e8, vec_out);
+        if (FULL)   // the last round reloads the last row (in bounds, unused)
+            ring[kj] = ld_nt2(rsrc2 + min(k + kRing, kSteps - 1) * 64);
     }
 }
 
@@ -1139,7 +1227,7 @@ __device__ inline TileMeta load_meta(const uint8_t* __restrict__ src, const Geom
 }
 
 template <bool FULL>
-__device__ void decompress_tile(const uint8_t* __restrict__ src, uint16_t* __restrict__ dst,
+__device__ __forceinline__ void decompress_tile(const uint8_t* __restrict__ src, uint16_t* __restrict__ dst,
                                 int32_t* __restrict__ status, int c, uint32_t n, uint32_t t,
                                 uint64_t bavail, uint32_t lane, uint32_t* __restrict__ s,
                                 const uint8_t* __restrict__ s_lut8,
@@ -1212,7 +1300,8 @@ __device__ void decompress_tile(const uint8_t* __restrict__ src, uint16_t* __res
 
     const bool raw_mode = ng > 0 && glen == 8 * ng;
     const uint64_t raw_lanes = __ballot(raw_mode);
-    const bool vec_out = FULL && ((reinterpret_cast<uintptr_t>(dst) & 15) == 0);
+    // full tiles are only taken with 16-byte aligned output (decompress_body)
+    const bool vec_out = FULL;
     const uint8_t* rsrc = src + G.R;
     DecState st;
     st.pos = off;
@@ -1268,7 +1357,8 @@ __device__ void decompress_tile(const uint8_t* __restrict__ src, uint16_t* __res
     }
 }
 
-// A chunk's last, partial tile, kept out of line (see compress_tile_partial).
+// A chunk's last, partial tile, or any tile of an output that is not 16-byte
+// aligned, kept out of line (see compress_tile_partial).
 __device__ __attribute__((noinline)) void decompress_tile_partial(
     const uint8_t* __restrict__ src, uint16_t* __restrict__ dst, int32_t* __restrict__ status,
     int c, uint32_t n, uint32_t t, uint64_t bavail, uint32_t lane, uint32_t* __restrict__ s,
@@ -1294,7 +1384,11 @@ __device__ __forceinline__ void decompress_body(const uint8_t* __restrict__ in,
     // The first-level table is the only one read from memory: its load is
     // issued first and written to LDS just before the barrier, after this
     // wave's chunk lookup (scalar loads) and tile metadata loads.
-    const uint4 lut_part = reinterpret_cast<const uint4*>(c_lut)[tid];
+    uint32_t lut_part[kLutPer];
+#pragma unroll
+    for (int i = 0; i < kLutPer; ++i)
+        if (kLutWords % kBlock == 0 || tid + i * kBlock < static_cast<uint32_t>(kLutWords))
+            lut_part[i] = reinterpret_cast<const uint32_t*>(c_lut)[tid + i * kBlock];
     // raw groups: 8 bits b decode to 255 - b
     s_lut8[kLutRaw + tid] = static_cast<uint8_t>(255u - tid);
     if (tid < (1u << kTailBits))
@@ -1316,7 +1410,10 @@ __device__ __forceinline__ void decompress_body(const uint8_t* __restrict__ in,
         if (n != 0 && G.X <= tab.bavail[c])
             meta = load_meta(in + tab.boff[c], G, t, lane);
     }
-    reinterpret_cast<uint4*>(s_lut8)[tid] = lut_part;
+#pragma unroll
+    for (int i = 0; i < kLutPer; ++i)
+        if (kLutWords % kBlock == 0 || tid + i * kBlock < static_cast<uint32_t>(kLutWords))
+            reinterpret_cast<uint32_t*>(s_lut8)[tid + i * kBlock] = lut_part[i];
     __syncthreads();
 
     if (!live)
@@ -1332,7 +1429,7 @@ __device__ __forceinline__ void decompress_body(const uint8_t* __restrict__ in,
     const uint8_t* src = in + tab.boff[c];
     uint16_t* dst = out + tab.voff[c];
     const uint32_t rem = min(n - t * kTile, static_cast<uint32_t>(kTile));
-    if (rem == kTile)
+    if (rem == kTile && (reinterpret_cast<uintptr_t>(dst) & 15) == 0)
         decompress_tile<true>(src, dst, status, c, n, t, tab.bavail[c], lane, s_stage[wave],
                               s_lut8, s_tail, s_len, meta);
     else
@@ -1548,7 +1645,7 @@ void zc_plan_kernel(const int64_t* __restrict__ counts, int32_t num_chunks, int3
         tab->nchunks = m;
         tab->nitems = bad ? 0u : items;
         tab->uniform_tiles = uniform;
-        tab->grid_order = (ZC_ENC_INTERLEAVE && uniform) ? 0u : 1u;
+        tab->grid_order = tile_order(uniform);
         tab->spin_limit = spin_limit;
         if (decode && bad && status)
             atomicCAS(status, 0, (ZC_REASON_SIZE << 24) | (c0 & 0xFFFFFF));
@@ -1880,7 +1977,7 @@ int zc_compress(const uint16_t* d_in, const int64_t* counts, int32_t num_chunks,
         // Equal chunks are interleaved and take tiles from per-chunk tickets;
         // otherwise the grid order is the tile order (a shared ticket would
         // serialize the workgroups of a large chunk).
-        tab.grid_order = (ZC_ENC_INTERLEAVE && tab.uniform_tiles) ? 0u : 1u;
+        tab.grid_order = tile_order(tab.uniform_tiles);
         tab.spin_limit = spin_limit;
 
         // the ticket word and the look-back status words start at zero

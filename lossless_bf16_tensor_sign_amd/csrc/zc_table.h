@@ -9,8 +9,14 @@ constexpr int kEscapeFrom = 16;          // d >= 16 is escaped
 constexpr int kEscape = kEscapeFrom;     // symbol index of ESC
 constexpr int kSymbols = kEscapeFrom + 1;
 constexpr int kMaxCodeLen = 24;          // longest code word the kernels take
-constexpr int kLutBits = 12;             // decoder first-level lookup width
-constexpr int kTailBits = 2;             // second level (codes up to 14 bits)
+#ifndef ZC_LUT_BITS
+#define ZC_LUT_BITS 11
+#endif
+#ifndef ZC_TAIL_BITS
+#define ZC_TAIL_BITS (14 - ZC_LUT_BITS)
+#endif
+constexpr int kLutBits = ZC_LUT_BITS;    // decoder first-level lookup width
+constexpr int kTailBits = ZC_TAIL_BITS;  // second level (codes up to 14 bits)
 
 struct Table {
     double prob[kSymbols];
