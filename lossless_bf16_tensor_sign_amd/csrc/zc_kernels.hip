@@ -74,6 +74,12 @@
 #ifndef ZC_MIXED_PAIR
 #define ZC_MIXED_PAIR 1          // waves with raw groups may also emit pairs
 #endif
+#ifndef ZC_ENC_TILE_WAVES
+#define ZC_ENC_TILE_WAVES 4      // compress: waves that share one tile (2 or 4)
+#endif
+#ifndef ZC_ENC_REEXTRACT
+#define ZC_ENC_REEXTRACT 0       // compress: emission extracts d from the packed words again
+#endif
 #ifndef ZC_ENC_BATCH
 #define ZC_ENC_BATCH 0           // compress: a step's table lookups issued together (1 pairs, 2 escapes)
 #endif
@@ -326,8 +332,11 @@ __global__ void zc_clear_kernel(uint32_t* __restrict__ tickets, uint32_t ticket_
 }
 
 
+// Indexed by d = E_max - e (0..255).  esc[d] = code word | length << 24,
+// with bit 31 set and the code word shifted left by 8 for an escape (d >= 16),
+// whose 8 exponent bits follow it.
 struct EncTables {
-    uint32_t esc[256];    // enc_entry(d)
+    uint32_t esc[256];
     uint16_t code[256];   // code word of d (the escape code for d >= 16)
     uint8_t len[256];     // coded length of d, escape payload included
 };
@@ -338,15 +347,18 @@ struct EncTables {
 // lengths of a group meet in LDS, so each thread knows where its quarter of
 // the group's stream starts; the four waves then write their code words into
 // one LDS copy of the tile stream, and wave 0 places it in the chunk.
-constexpr int kQSteps = kSteps / kWaves;           // steps per wave
+constexpr int kEncWaves = ZC_ENC_TILE_WAVES;       // waves per compress workgroup (one tile)
+constexpr int kEncBlock = kLanes * kEncWaves;
+static_assert(kEncWaves == 2 || kEncWaves == 4, "a tile is shared by 2 or 4 waves");
+constexpr int kQSteps = kSteps / kEncWaves;        // steps per wave
 constexpr int kQMembers = kQSteps * 8;             // members per wave and group
 constexpr int kTileWordsMax = kTile / 4;           // an all-raw tile stream
 constexpr int kEncStage = kTileWordsMax + 8;       // + guard words
 
 struct EncShared {
     uint32_t stage[kEncStage];
-    uint32_t part_max[kWaves][kLanes];
-    uint32_t part_bits[kWaves][kLanes];
+    uint16_t part_max[kEncWaves][kLanes];   // at most 255
+    uint16_t part_bits[kEncWaves][kLanes];  // at most 64 * 22
     EncTables tb;
     uint32_t tile;
     uint32_t spin_limit;
@@ -360,15 +372,20 @@ struct TileCtx {
     int c;
 };
 
-// Loads this wave's four steps of the tile (FULL = 8192 values at a 16-byte
+// A wave loads its steps of the tile in batches of at most four (16 bytes
+// per lane each), which bounds the registers that hold loaded values.
+constexpr int kLoadBatch = kQSteps < 4 ? kQSteps : 4;
+constexpr int kBatches = kQSteps / kLoadBatch;
+
+// Loads batch `b` of this wave's steps (FULL = 8192 values at a 16-byte
 // aligned address; otherwise missing members read as 0).
 template <bool FULL>
-__device__ inline void load_tile(const TileCtx& x, uint4 (&v)[kQSteps])
+__device__ inline void load_tile(const TileCtx& x, uint4 (&v)[kLoadBatch], int b)
 {
-    const uint32_t k0 = x.wave * kQSteps;
+    const uint32_t k0 = x.wave * kQSteps + b * kLoadBatch;
     const char* sbase = reinterpret_cast<const char*>(x.src + x.base) + k0 * 1024 + x.lane * 16;
 #pragma unroll
-    for (int k = 0; k < kQSteps; ++k) {
+    for (int k = 0; k < kLoadBatch; ++k) {
         if (FULL) {
             v[k] = ld_nt4(sbase + k * 1024);
         } else {
@@ -385,18 +402,19 @@ __device__ inline void load_tile(const TileCtx& x, uint4 (&v)[kQSteps])
     }
 }
 
-// Splits the loaded steps: raw bytes are stored at once, exponents stay
+// Splits loaded batch `b`: raw bytes are stored at once, exponents stay
 // packed 4 per word, the maximum exponent is returned.
 template <bool FULL>
-__device__ inline uint32_t split_tile(const TileCtx& x, const uint4 (&v)[kQSteps],
-                                      uint32_t (&ex)[kQSteps][2])
+__device__ inline uint32_t split_tile(const TileCtx& x, const uint4 (&v)[kLoadBatch],
+                                      uint32_t (&ex)[kQSteps][2], int b)
 {
-    const uint32_t k0 = x.wave * kQSteps;
+    const uint32_t k0 = x.wave * kQSteps + b * kLoadBatch;
     char* rbase = reinterpret_cast<char*>(x.dst + x.G.R + x.base) + k0 * 512 + x.lane * 8;
     uint32_t mx = 0;
 #pragma unroll
-    for (int k = 0; k < kQSteps; ++k) {
-        const uint4 q = v[k];
+    for (int kb = 0; kb < kLoadBatch; ++kb) {
+        const int k = b * kLoadBatch + kb;
+        const uint4 q = v[kb];
         const uint32_t lo_a = __builtin_amdgcn_perm(q.y, q.x, 0x06040200u);
         const uint32_t hi_a = __builtin_amdgcn_perm(q.y, q.x, 0x07050301u);
         const uint32_t lo_b = __builtin_amdgcn_perm(q.w, q.z, 0x06040200u);
@@ -410,9 +428,9 @@ __device__ inline uint32_t split_tile(const TileCtx& x, const uint4 (&v)[kQSteps
         mx = max(mx, max(max(q.z & 0x7F80u, (q.z >> 16) & 0x7F80u),
                          max(q.w & 0x7F80u, (q.w >> 16) & 0x7F80u)));
         if (FULL) {
-            st_nt2(rbase + k * 512, make_uint2(raw_a, raw_b));
+            st_nt2(rbase + kb * 512, make_uint2(raw_a, raw_b));
         } else {
-            const uint32_t i0 = x.base + (k0 + k) * 512 + x.lane * 8;
+            const uint32_t i0 = x.base + (k0 + kb) * 512 + x.lane * 8;
             uint8_t* rdst = x.dst + x.G.R + i0;
 #pragma unroll
             for (int j = 0; j < 8; ++j)
@@ -426,9 +444,14 @@ __device__ inline uint32_t split_tile(const TileCtx& x, const uint4 (&v)[kQSteps
 template <bool FULL>
 __device__ inline uint32_t load_split(const TileCtx& x, uint32_t (&ex)[kQSteps][2])
 {
-    uint4 v[kQSteps];
-    load_tile<FULL>(x, v);
-    return split_tile<FULL>(x, v, ex);
+    uint32_t mx = 0;
+#pragma unroll
+    for (int b = 0; b < kBatches; ++b) {
+        uint4 v[kLoadBatch];
+        load_tile<FULL>(x, v, b);
+        mx = max(mx, split_tile<FULL>(x, v, ex, b));
+    }
+    return mx;
 }
 
 // Decoupled look-back over per-tile status words (flag in bits 62-63:
@@ -696,9 +719,11 @@ __device__ __forceinline__ void compress_tile_back(const TileCtx& x, uint32_t (&
     const uint32_t ng = FULL ? 128u : group_members(x.rem, lane);
     const uint32_t first = wave * kQMembers;     // group index of this thread's first member
 
-    // 1. the group maximum from four partial ones
-    const uint32_t emax = max(max(sh.part_max[0][lane], sh.part_max[1][lane]),
-                              max(sh.part_max[2][lane], sh.part_max[3][lane]));
+    // 1. the group maximum from the waves' partial ones
+    uint32_t emax = sh.part_max[0][lane];
+#pragma unroll
+    for (int w = 1; w < kEncWaves; ++w)
+        emax = max(emax, sh.part_max[w][lane]);
 
     // 2. distances d = E_max - e (bytes never borrow: e <= E_max) and the
     //    coded length of this thread's members
@@ -718,20 +743,28 @@ __device__ __forceinline__ void compress_tile_back(const TileCtx& x, uint32_t (&
             bits += (FULL || first + static_cast<uint32_t>(k * 8 + j) < ng) ? L : 0u;
         }
     }
-    sh.part_bits[wave][lane] = bits;
+    // The emission extracts each d again: an empty register constraint
+    // keeps the compiler from carrying the extracted bytes (two per value)
+    // across the barrier instead of the packed words.
+#if ZC_ENC_REEXTRACT
+#pragma unroll
+    for (int k = 0; k < kQSteps; ++k)
+        asm volatile("" : "+v"(dd[k][0]), "+v"(dd[k][1]));
+#endif
+    sh.part_bits[wave][lane] = static_cast<uint16_t>(bits);
     __syncthreads();
 
     // 3. the group's length and mode, where this thread's part starts, and
     //    the lane offsets of the tile stream
-    const uint32_t b0 = sh.part_bits[0][lane], b1 = sh.part_bits[1][lane],
-                   b2 = sh.part_bits[2][lane], b3 = sh.part_bits[3][lane];
-    const uint32_t gbits = b0 + b1 + b2 + b3;
+    uint32_t gbits = 0, pre = 0;
+#pragma unroll
+    for (int w = 0; w < kEncWaves; ++w) {
+        const uint32_t b = sh.part_bits[w][lane];
+        pre += wave > static_cast<uint32_t>(w) ? b : 0u;
+        gbits += b;
+    }
     const bool raw_mode = ng > 0 && gbits >= 8 * ng;
     const uint32_t glen = raw_mode ? 8 * ng : gbits;
-    uint32_t pre = 0;
-    pre += wave > 0 ? b0 : 0u;
-    pre += wave > 1 ? b1 : 0u;
-    pre += wave > 2 ? b2 : 0u;
     if (raw_mode)
         pre = 8 * min(ng, first);
     uint32_t tile_bits;
@@ -800,7 +833,7 @@ __device__ __attribute__((noinline)) void compress_tile_partial(
     x.base = t * kTile;
     x.rem = min(n - x.base, static_cast<uint32_t>(kTile));
     uint32_t dd[kQSteps][2];
-    sh->part_max[wave][lane] = load_split<false>(x, dd);
+    sh->part_max[wave][lane] = static_cast<uint16_t>(load_split<false>(x, dd));
     __syncthreads();
     compress_tile_back<false>(x, dd, comp_sizes, status, *sh);
 }
@@ -845,7 +878,7 @@ __device__ __forceinline__ void compress_body(const uint16_t* __restrict__ in,
 
     // A grid-ordered tile is known at once: a full one issues its loads now,
     // so that their latency covers the table set-up below.
-    uint4 v[kQSteps];
+    uint4 v[kLoadBatch];
     bool loaded = false;
     if (tab.grid_order != kOrderTickets) {
         x.t = tab.grid_order == kOrderRoundRobin ? item / static_cast<uint32_t>(tab.nchunks)
@@ -853,20 +886,21 @@ __device__ __forceinline__ void compress_body(const uint16_t* __restrict__ in,
         x.base = x.t * kTile;
         loaded = ZC_EARLY_LOAD && x.n != 0 && aligned && x.n - x.base >= static_cast<uint32_t>(kTile);
         if (loaded)
-            load_tile<true>(x, v);
+            load_tile<true>(x, v, 0);
     }
-    {
-        const uint32_t s = tid < static_cast<uint32_t>(kEsc) ? tid : static_cast<uint32_t>(kEsc);
+#pragma unroll
+    for (uint32_t i = tid; i < 256u; i += kEncBlock) {
+        const uint32_t s = i < static_cast<uint32_t>(kEsc) ? i : static_cast<uint32_t>(kEsc);
         uint32_t code = code_of(s), len = len_of(s);
-        sh.tb.code[tid] = static_cast<uint16_t>(code);
+        sh.tb.code[i] = static_cast<uint16_t>(code);
         if (s == static_cast<uint32_t>(kEsc)) {   // escape: code word, then 8 exponent bits
             code <<= 8;
             len += 8;
         }
-        sh.tb.esc[tid] = code | (len << 24) | (s == static_cast<uint32_t>(kEsc) ? 0x80000000u : 0u);
-        sh.tb.len[tid] = static_cast<uint8_t>(len);
+        sh.tb.esc[i] = code | (len << 24) | (s == static_cast<uint32_t>(kEsc) ? 0x80000000u : 0u);
+        sh.tb.len[i] = static_cast<uint8_t>(len);
     }
-    for (uint32_t i = tid * 4; i < static_cast<uint32_t>(kEncStage); i += kBlock * 4)
+    for (uint32_t i = tid * 4; i < static_cast<uint32_t>(kEncStage); i += kEncBlock * 4)
         *reinterpret_cast<uint4*>(&sh.stage[i]) = make_uint4(0, 0, 0, 0);
     if (tid == 0)
         sh.spin_limit = tab.spin_limit;
@@ -890,9 +924,15 @@ __device__ __forceinline__ void compress_body(const uint16_t* __restrict__ in,
     const bool full = x.rem == kTile && aligned;
     if (full) {
         if (!loaded)
-            load_tile<true>(x, v);
+            load_tile<true>(x, v, 0);
         uint32_t dd[kQSteps][2];
-        sh.part_max[wave][lane] = split_tile<true>(x, v, dd);
+        uint32_t mx = split_tile<true>(x, v, dd, 0);
+#pragma unroll
+        for (int b = 1; b < kBatches; ++b) {
+            load_tile<true>(x, v, b);
+            mx = max(mx, split_tile<true>(x, v, dd, b));
+        }
+        sh.part_max[wave][lane] = static_cast<uint16_t>(mx);
         __syncthreads();
         compress_tile_back<true>(x, dd, comp_sizes, status, sh);
     } else {
@@ -901,7 +941,7 @@ __device__ __forceinline__ void compress_body(const uint16_t* __restrict__ in,
     }
 }
 
-__global__ __launch_bounds__(kBlock, kMinWavesEnc)
+__global__ __launch_bounds__(kEncBlock, kMinWavesEnc)
 void zc_compress_kernel(const uint16_t* __restrict__ in, uint8_t* __restrict__ out,
                         int64_t* __restrict__ comp_sizes,
                         uint64_t* __restrict__ status, uint32_t* __restrict__ tickets,
@@ -913,7 +953,7 @@ void zc_compress_kernel(const uint16_t* __restrict__ in, uint8_t* __restrict__ o
 // The same with the chunk table in device memory (built on the device from
 // device-resident counts); the grid is an upper bound on the tile count and
 // workgroups past the table's tiles return at once.
-__global__ __launch_bounds__(kBlock, kMinWavesEnc)
+__global__ __launch_bounds__(kEncBlock, kMinWavesEnc)
 void zc_compress_dev_kernel(const uint16_t* __restrict__ in, uint8_t* __restrict__ out,
                             int64_t* __restrict__ comp_sizes,
                             uint64_t* __restrict__ status, uint32_t* __restrict__ tickets,
@@ -1986,7 +2026,7 @@ int zc_compress(const uint16_t* d_in, const int64_t* counts, int32_t num_chunks,
         const uint32_t cblocks = (words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024;
         hipLaunchKernelGGL(zc_clear_kernel, dim3(cblocks), dim3(256), 0, s, ticket, twords,
                            status, items);
-        hipLaunchKernelGGL(zc_compress_kernel, dim3(items), dim3(kBlock), 0, s, d_in,
+        hipLaunchKernelGGL(zc_compress_kernel, dim3(items), dim3(kEncBlock), 0, s, d_in,
                            out, d_comp_sizes + c0, status, ticket, tab);
         if (hipGetLastError() != hipSuccess)
             return ZC_EHIP;
@@ -2051,7 +2091,7 @@ int zc_compress_dev(const uint16_t* d_in, const int64_t* d_counts, int32_t num_c
         hipLaunchKernelGGL(zc_plan_kernel, dim3(1), dim3(kLanes), 0, s, d_counts, num_chunks, c0, m,
                            total_values, static_cast<const int64_t*>(nullptr), uint64_t(0), items,
                            spin_limit, 0, tab, d_slot_off, d_comp_sizes, static_cast<int32_t*>(nullptr));
-        hipLaunchKernelGGL(zc_compress_dev_kernel, dim3(items), dim3(kBlock), 0, s, d_in,
+        hipLaunchKernelGGL(zc_compress_dev_kernel, dim3(items), dim3(kEncBlock), 0, s, d_in,
                            static_cast<uint8_t*>(d_out), d_comp_sizes + c0, status, ticket,
                            static_cast<const ChunkTable*>(tab));
         if (hipGetLastError() != hipSuccess)
