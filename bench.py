@@ -216,7 +216,7 @@ def main():
         # call instead of during it
         flush.fill_(v & 0xFF)
         if args.flush == "clean":
-            flush.sum(dtype=torch.int64)
+            flush.view(torch.int64).sum()     # a plain 1 GiB read
 
     def ev():
         return torch.cuda.Event(enable_timing=True)

@@ -723,7 +723,7 @@ __device__ __forceinline__ void compress_tile_back(const TileCtx& x, uint32_t (&
     uint32_t emax = sh.part_max[0][lane];
 #pragma unroll
     for (int w = 1; w < kEncWaves; ++w)
-        emax = max(emax, sh.part_max[w][lane]);
+        emax = max(emax, static_cast<uint32_t>(sh.part_max[w][lane]));
 
     // 2. distances d = E_max - e (bytes never borrow: e <= E_max) and the
     //    coded length of this thread's members
