@@ -80,6 +80,13 @@
 #ifndef ZC_ENC_REEXTRACT
 #define ZC_ENC_REEXTRACT 0       // compress: emission extracts d from the packed words again
 #endif
+#ifndef ZC_LATE_PUBLISH
+#define ZC_LATE_PUBLISH 1        // compress: inclusive prefix published after the tile's stores
+#endif
+#ifndef ZC_ENC_PAIRS
+#define ZC_ENC_PAIRS 2           // compress: full tiles emit member pairs from one table entry
+                                 // (0 never, 1 in waves with raw groups, 2 always)
+#endif
 #ifndef ZC_ENC_BATCH
 #define ZC_ENC_BATCH 0           // compress: a step's table lookups issued together (1 pairs, 2 escapes)
 #endif
@@ -337,8 +344,10 @@ __global__ void zc_clear_kernel(uint32_t* __restrict__ tickets, uint32_t ticket_
 // whose 8 exponent bits follow it.
 struct EncTables {
     uint32_t esc[256];
+    uint32_t pcode[256];  // member pair (d0, d1 < 16) at index d0 | d1 << 4: code words back to back
     uint16_t code[256];   // code word of d (the escape code for d >= 16)
     uint8_t len[256];     // coded length of d, escape payload included
+    uint8_t plen[256];    // the pair's total length (at most 28)
 };
 
 // A tile is compressed by one workgroup of four waves.  Lane l of every wave
@@ -563,7 +572,7 @@ __device__ inline uint32_t look_back_resolve(uint64_t* __restrict__ status, uint
                 s = (p == first ? kFlagInc : kFlagAgg) | bytes;
         }
     }
-    if (lane == 0)
+    if (!ZC_LATE_PUBLISH && lane == 0)
         __hip_atomic_store(&status[item * kStatusStride], kFlagInc | (acc + tile_bytes),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return acc;
@@ -588,7 +597,50 @@ __device__ __forceinline__ void emit_quarter(uint32_t* __restrict__ s, const Enc
     for (int k = 0; k < kQSteps; ++k) {
         const uint32_t d4[2] = {dd[k][0], dd[k][1]};
         const bool esc_here = coded && (((d4[0] | d4[1]) & 0xF0F0F0F0u) != 0);
-        if ((!MIXED || ZC_MIXED_PAIR) && __ballot(esc_here) == 0) {
+        if (FULL && (ZC_ENC_PAIRS == 2 || (ZC_ENC_PAIRS == 1 && MIXED)) &&
+            __ballot(esc_here) == 0) {
+            // Every d of the step's coded lanes is below 16, so two members
+            // index one pair entry: d0 | d1 << 4 is read off the packed
+            // bytes as (w | w >> 4).  Four members go out with one LDS OR
+            // when their code words fit in 32 bits on every lane.
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t w = d4[h];
+                const uint32_t nib = w | (w >> 4);
+                uint32_t c01 = tb.pcode[nib & 0xFF], l01 = tb.plen[nib & 0xFF];
+                uint32_t c23 = tb.pcode[(nib >> 16) & 0xFF], l23 = tb.plen[(nib >> 16) & 0xFF];
+                if (MIXED && raw_mode) {
+                    // raw group: the exponents e = E_max - d as 8-bit words
+                    const uint32_t e4 = emax * 0x01010101u - w;
+                    c01 = __builtin_amdgcn_perm(0u, e4, 0x0c0c0001u);
+                    c23 = __builtin_amdgcn_perm(0u, e4, 0x0c0c0203u);
+                    l01 = 16;
+                    l23 = 16;
+                }
+                if (__ballot(l01 + l23 > 32u) == 0) {
+                    const uint32_t pl = l01 + l23;
+                    acc = (acc << pl) | ((c01 << l23) | c23);
+                    nacc += pl;
+                    const uint32_t wv = __builtin_amdgcn_alignbit(hi32(acc), lo32(acc), nacc);
+                    const uint32_t f = nacc >> 5;
+                    atomicOr(&s[wi], f ? wv : 0u);
+                    wi += f;
+                    nacc &= 31;
+                } else {
+                    const uint32_t cc[2] = {c01, c23}, ll[2] = {l01, l23};
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        acc = (acc << ll[u]) | cc[u];
+                        nacc += ll[u];
+                        const uint32_t wv = __builtin_amdgcn_alignbit(hi32(acc), lo32(acc), nacc);
+                        const uint32_t f = nacc >> 5;
+                        atomicOr(&s[wi], f ? wv : 0u);
+                        wi += f;
+                        nacc &= 31;
+                    }
+                }
+            }
+        } else if ((!MIXED || ZC_MIXED_PAIR) && __ballot(esc_here) == 0) {
             // the step's table lookups are all issued before its first LDS
             // OR, so that they cost one LDS round trip, not one per pair
             // (no escape here: each entry is code | length << 24)
@@ -810,6 +862,9 @@ __device__ __forceinline__ void compress_tile_back(const TileCtx& x, uint32_t (&
         }
     }
     write_tile_index(x, toff, tile_bytes, emax, glen, comp_sizes);
+    if (ZC_LATE_PUBLISH && x.t != 0 && lane == 0)
+        __hip_atomic_store(&status[x.item * kStatusStride], kFlagInc | (toff + tile_bytes),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Tiles that are partial (a chunk's last tile) or unaligned: kept out of
@@ -849,7 +904,7 @@ __device__ __forceinline__ void compress_body(const uint16_t* __restrict__ in,
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & (kLanes - 1);
-    const uint32_t wave = tid / kLanes;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kLanes);   // uniform: scalar
 
     // The workgroup's chunk comes from its position in the grid: round-robin
     // over the chunks when they all have the same number of tiles, so that
@@ -899,6 +954,9 @@ __device__ __forceinline__ void compress_body(const uint16_t* __restrict__ in,
         }
         sh.tb.esc[i] = code | (len << 24) | (s == static_cast<uint32_t>(kEsc) ? 0x80000000u : 0u);
         sh.tb.len[i] = static_cast<uint8_t>(len);
+        const uint32_t d0 = i & 15, d1 = i >> 4, l1 = len_of(d1);
+        sh.tb.pcode[i] = (code_of(d0) << l1) | code_of(d1);
+        sh.tb.plen[i] = static_cast<uint8_t>(len_of(d0) + l1);
     }
     for (uint32_t i = tid * 4; i < static_cast<uint32_t>(kEncStage); i += kEncBlock * 4)
         *reinterpret_cast<uint4*>(&sh.stage[i]) = make_uint4(0, 0, 0, 0);
