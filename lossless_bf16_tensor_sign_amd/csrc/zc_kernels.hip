@@ -151,15 +151,6 @@ __device__ inline uint32_t len_of(uint32_t s)
     return v;
 }
 
-__device__ inline uint32_t code_of(uint32_t s)
-{
-    uint32_t v = 0;
-#pragma unroll
-    for (int i = 0; i < ZC_T1_NSYM; ++i)
-        v = s == static_cast<uint32_t>(i) ? kCodeT1[i] : v;
-    return v;
-}
-
 __device__ inline uint32_t tail_of(uint32_t i)
 {
     uint32_t v = 0;
@@ -342,13 +333,37 @@ __global__ void zc_clear_kernel(uint32_t* __restrict__ tickets, uint32_t ticket_
 // Indexed by d = E_max - e (0..255).  esc[d] = code word | length << 24,
 // with bit 31 set and the code word shifted left by 8 for an escape (d >= 16),
 // whose 8 exponent bits follow it.
-struct EncTables {
+struct __align__(16) EncTables {
     uint32_t esc[256];
     uint32_t pcode[256];  // member pair (d0, d1 < 16) at index d0 | d1 << 4: code words back to back
     uint16_t code[256];   // code word of d (the escape code for d >= 16)
     uint8_t len[256];     // coded length of d, escape payload included
     uint8_t plen[256];    // the pair's total length (at most 28)
 };
+static_assert(sizeof(EncTables) % 16 == 0, "copied to LDS in 16-byte words");
+
+// The encoder's tables of table_id 1, evaluated at compile time; each
+// workgroup copies them into LDS with one 16-byte load per thread.
+__host__ __device__ constexpr EncTables make_enc_tables()
+{
+    EncTables t{};
+    for (int i = 0; i < 256; ++i) {
+        const int sym = i < kEsc ? i : kEsc;
+        uint32_t code = kCodeT1[sym], len = kLenT1[sym];
+        t.code[i] = static_cast<uint16_t>(code);
+        if (sym == kEsc) {      // escape: code word, then 8 exponent bits
+            code <<= 8;
+            len += 8;
+        }
+        t.esc[i] = code | (len << 24) | (sym == kEsc ? 0x80000000u : 0u);
+        t.len[i] = static_cast<uint8_t>(len);
+        const int d0 = i & 15, d1 = i >> 4;
+        t.pcode[i] = (kCodeT1[d0] << kLenT1[d1]) | kCodeT1[d1];
+        t.plen[i] = static_cast<uint8_t>(kLenT1[d0] + kLenT1[d1]);
+    }
+    return t;
+}
+__constant__ EncTables c_enc = make_enc_tables();
 
 // A tile is compressed by one workgroup of four waves.  Lane l of every wave
 // works on group l; wave w takes steps 4w..4w+3 of it, which are members
@@ -365,10 +380,10 @@ constexpr int kTileWordsMax = kTile / 4;           // an all-raw tile stream
 constexpr int kEncStage = kTileWordsMax + 8;       // + guard words
 
 struct EncShared {
+    EncTables tb;
     uint32_t stage[kEncStage];
     uint16_t part_max[kEncWaves][kLanes];   // at most 255
     uint16_t part_bits[kEncWaves][kLanes];  // at most 64 * 22
-    EncTables tb;
     uint32_t tile;
     uint32_t spin_limit;
 };
@@ -943,21 +958,10 @@ __device__ __forceinline__ void compress_body(const uint16_t* __restrict__ in,
         if (loaded)
             load_tile<true>(x, v, 0);
     }
+    constexpr uint32_t kTbWords = sizeof(EncTables) / 16;
 #pragma unroll
-    for (uint32_t i = tid; i < 256u; i += kEncBlock) {
-        const uint32_t s = i < static_cast<uint32_t>(kEsc) ? i : static_cast<uint32_t>(kEsc);
-        uint32_t code = code_of(s), len = len_of(s);
-        sh.tb.code[i] = static_cast<uint16_t>(code);
-        if (s == static_cast<uint32_t>(kEsc)) {   // escape: code word, then 8 exponent bits
-            code <<= 8;
-            len += 8;
-        }
-        sh.tb.esc[i] = code | (len << 24) | (s == static_cast<uint32_t>(kEsc) ? 0x80000000u : 0u);
-        sh.tb.len[i] = static_cast<uint8_t>(len);
-        const uint32_t d0 = i & 15, d1 = i >> 4, l1 = len_of(d1);
-        sh.tb.pcode[i] = (code_of(d0) << l1) | code_of(d1);
-        sh.tb.plen[i] = static_cast<uint8_t>(len_of(d0) + l1);
-    }
+    for (uint32_t i = tid; i < kTbWords; i += kEncBlock)
+        reinterpret_cast<uint4*>(&sh.tb)[i] = reinterpret_cast<const uint4*>(&c_enc)[i];
     for (uint32_t i = tid * 4; i < static_cast<uint32_t>(kEncStage); i += kEncBlock * 4)
         *reinterpret_cast<uint4*>(&sh.stage[i]) = make_uint4(0, 0, 0, 0);
     if (tid == 0)
