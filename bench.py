@@ -146,6 +146,48 @@ def cpu_baseline(w, counts, threads, budget_s):
     }
 
 
+def time_pipeline(args, x, counts, dev, evict, ev):
+    """zc_pipeline round trip (compress, device-copy link, decompress) in
+    args.pipeline groups on three streams, against the same call with all
+    stages on one stream; both after the cache flush, 5 runs each."""
+    import numpy as np
+    import torch
+    from lossless_bf16_tensor_sign_amd import zc
+    cap = zc.zc_bound(counts)
+    send = torch.empty(cap, dtype=torch.uint8, device=dev)
+    recv = torch.empty(cap, dtype=torch.uint8, device=dev)
+    sizes = torch.empty(len(counts), dtype=torch.int64, device=dev)
+    ws = torch.empty(zc.zc_workspace_bytes(counts), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    cur = torch.cuda.current_stream()
+    three = tuple(torch.cuda.Stream(device=dev) for _ in range(3))
+    out = {"groups": args.pipeline}
+    for label, streams in (("three_streams", three), ("one_stream", (cur, cur, cur))):
+        times = []
+        for i in range(6):
+            evict(i + 21)
+            for s_ in streams:
+                s_.wait_stream(cur)
+            e0, e1 = ev(), ev()
+            e0.record(streams[0])
+            r = zc.zc_pipeline(x, counts, args.pipeline, send, recv, sizes, y, status, ws,
+                               s_comp=streams[0], s_link=streams[1], s_dec=streams[2])
+            if r != zc.ZC_OK:
+                raise zc.ZcError(r, "zc_pipeline")
+            e1.record(streams[2])
+            cur.wait_stream(streams[2])
+            if i:
+                times.append((e0, e1))
+        torch.cuda.synchronize()
+        if int(status.item()) != 0 or not torch.equal(x, y):
+            log("PIPELINE ROUND TRIP FAILED")
+            sys.exit(1)
+        out[label + "_ms"] = round(float(np.mean([a.elapsed_time(b) for a, b in times])), 4)
+    log("pipeline: %s" % out)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +207,9 @@ def main():
     ap.add_argument("--device-counts", action="store_true",
                     help="time zc_compress_dev / zc_decompress_dev, with the chunk "
                          "counts in device memory (the MoE router's split)")
+    ap.add_argument("--pipeline", type=int, default=0, metavar="G",
+                    help="also time zc_pipeline (compress, device-copy link, decompress) "
+                         "in G chunk groups on three streams and on one")
     ap.add_argument("--reduce", action="store_true",
                     help="decode with zc_decompress_reduce: the chunks are one rank's "
                          "shard as received from each peer, summed in fp32 in chunk "
@@ -400,6 +445,9 @@ def main():
             if st_ == zc.ZC_OK:
                 sw["%s_%d" % (coll, ranks)] = round(res["breakeven_GBps"], 1)
     line["switch_breakeven_link_GBps"] = sw
+
+    if args.pipeline:
+        line["pipeline"] = time_pipeline(args, x, counts, dev, evict, ev)
 
     if not args.no_cpu_baseline:
         threads = max(1, min(args.cpu_threads, os.cpu_count() or 1, len(counts)))

@@ -253,6 +253,40 @@ int zc_decompress_reduce_bf16(const void* d_in, size_t in_bytes,
                               size_t scratch_bytes, void* stream);
 
 /*
+ * Chunk-pipelined exchange (abstract, technique (2): pipelining in the GPU
+ * kernels; pith.science, Figure 5: compress before the collective, decompress
+ * after it; Figure 14 caption: the pipelined Design-2 of the zipped
+ * All-to-All).  The chunks are split into `groups` consecutive groups (group
+ * g holds chunks floor(g C / groups) .. floor((g + 1) C / groups) - 1 of
+ * C = num_chunks).  Each group is compressed on s_comp into d_send, its
+ * streams are carried to d_recv on s_link, and it is decoded from d_recv on
+ * s_dec; an event per stage boundary orders the three stages of one group,
+ * so stage k of group g + 1 can run while stage k + 1 of group g does.  On
+ * one GPU the carrier is a device copy of comp_sizes[c] bytes per slot, the
+ * stand-in for a peer-to-peer send.
+ *   d_in, counts, num_chunks   as zc_compress
+ *   groups         1 .. num_chunks
+ *   d_send, d_recv device, 16-byte aligned, capacity >= zc_bound(...) bytes
+ *                  each, slot layout; d_recv receives only the stream bytes
+ *   d_comp_sizes   device int64[num_chunks], as zc_compress
+ *   d_out          device, sum(counts) bf16 values
+ *   d_status       device int32, 0 on entry; as zc_decompress
+ *   d_ws, ws_bytes as zc_compress; the compress stages run in order on
+ *                  s_comp and share it
+ *   s_comp, s_link, s_dec  hipStream_t (equal streams serialise the stages)
+ * All buffers are caller-owned.  The call creates two events per group and
+ * releases them once their waits are queued.  Returns ZC_OK once everything
+ * is queued (d_out is complete when s_dec reaches this point);
+ * ZC_EINVAL / ZC_ENOSPC before anything is queued for a bad argument;
+ * ZC_EHIP if a launch or event call fails (earlier groups may be queued).
+ */
+int zc_pipeline(const uint16_t* d_in, const int64_t* counts, int32_t num_chunks,
+                int32_t groups, void* d_send, void* d_recv, size_t capacity,
+                int64_t* d_comp_sizes, uint16_t* d_out, int32_t* d_status,
+                void* d_ws, size_t ws_bytes, void* s_comp, void* s_link,
+                void* s_dec);
+
+/*
  * Adaptive switch (abstract, technique (3): compressed or plain collective,
  * chosen from the workload and the system; pith.science, Figure 15 caption:
  * the adaptive switcher).  zc_estimate predicts the compressed size from a

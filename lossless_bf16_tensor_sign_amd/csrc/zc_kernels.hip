@@ -41,6 +41,7 @@
 #include <cstring>
 #include <mutex>
 #include <vector>
+#include <algorithm>
 
 #include "zc.h"
 #include "zc_table.h"
@@ -1555,6 +1556,36 @@ void zc_decompress_dev_kernel(const uint8_t* __restrict__ in, uint16_t* __restri
     decompress_body(in, out, status, *tab);
 }
 
+// ------------------------------------------------------------ pipeline link
+
+// Slots of the chunks of one pipeline group, relative to the group's first.
+struct LinkTable {
+    uint64_t slot[kMaxChunks];     // byte offset of the chunk's slot
+    uint64_t bound[kMaxChunks];    // slot size: nothing past it is read or written
+};
+
+// The stand-in for the link of a pipelined exchange on one GPU: copies each
+// chunk's compressed stream (comp_sizes[c] bytes, read on the device, capped
+// at the slot size) from the sender's slot to the same slot of the receiver.
+// Grid: x = blocks per chunk, y = chunk.
+__global__ __launch_bounds__(kBlock)
+void zc_link_copy_kernel(const uint8_t* __restrict__ send, uint8_t* __restrict__ recv,
+                         const int64_t* __restrict__ comp_sizes, LinkTable tab)
+{
+    const uint32_t c = blockIdx.y;
+    const int64_t sz = comp_sizes[c];
+    const uint64_t bytes = sz < 0 ? 0 : min(static_cast<uint64_t>(sz), tab.bound[c]);
+    const uint8_t* s = send + tab.slot[c];
+    uint8_t* d = recv + tab.slot[c];
+    const uint64_t quads = bytes / 16;
+    const uint64_t step = static_cast<uint64_t>(gridDim.x) * kBlock;
+    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; i < quads; i += step)
+        st_nt4(reinterpret_cast<uint4*>(d) + i, ld_nt4(reinterpret_cast<const uint4*>(s) + i));
+    if (blockIdx.x == 0)
+        for (uint64_t b = quads * 16 + threadIdx.x; b < bytes; b += kBlock)
+            d[b] = s[b];
+}
+
 // ------------------------------------------------------------ reduce
 
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -2076,9 +2107,8 @@ int zc_compress(const uint16_t* d_in, const int64_t* counts, int32_t num_chunks,
         for (int32_t i = 0; i < m && tab.uniform_tiles; ++i)
             if (tab.item_begin[i + 1] - tab.item_begin[i] != tab.uniform_tiles || tab.n[i] == 0)
                 tab.uniform_tiles = 0;
-        // Equal chunks are interleaved and take tiles from per-chunk tickets;
-        // otherwise the grid order is the tile order (a shared ticket would
-        // serialize the workgroups of a large chunk).
+        // Equal chunks are taken round-robin by grid position; otherwise
+        // chunk by chunk (tile_order).
         tab.grid_order = tile_order(tab.uniform_tiles);
         tab.spin_limit = spin_limit;
 
@@ -2274,6 +2304,91 @@ int zc_decompress(const void* d_in, size_t in_bytes, const int64_t* in_offsets,
                            d_out, d_status, tab);
         if (hipGetLastError() != hipSuccess)
             return ZC_EHIP;
+    }
+    return ZC_OK;
+}
+
+int zc_pipeline(const uint16_t* d_in, const int64_t* counts, int32_t num_chunks,
+                int32_t groups, void* d_send, void* d_recv, size_t capacity,
+                int64_t* d_comp_sizes, uint16_t* d_out, int32_t* d_status, void* d_ws,
+                size_t ws_bytes, void* s_comp, void* s_link, void* s_dec)
+{
+    const Counts k = check_counts(counts, num_chunks);
+    if (!k.ok || groups < 1 || (num_chunks > 0 && groups > num_chunks))
+        return ZC_EINVAL;
+    if (num_chunks == 0)
+        return ZC_OK;
+    if (!d_send || !d_recv || !d_comp_sizes || !d_status || !d_ws
+        || (k.total_values && (!d_in || !d_out)))
+        return ZC_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(d_send) & 15) || (reinterpret_cast<uintptr_t>(d_recv) & 15)
+        || (reinterpret_cast<uintptr_t>(d_in) & 1) || (reinterpret_cast<uintptr_t>(d_out) & 1)
+        || (reinterpret_cast<uintptr_t>(d_comp_sizes) & 7))
+        return ZC_EINVAL;
+    if (capacity < zc_bound(counts, num_chunks))
+        return ZC_ENOSPC;
+    if (ws_bytes < zc_workspace_bytes(counts, num_chunks))
+        return ZC_ENOSPC;
+
+    // value offsets and slot offsets of every chunk
+    std::vector<uint64_t> voff(static_cast<size_t>(num_chunks) + 1, 0);
+    std::vector<uint64_t> soff(static_cast<size_t>(num_chunks) + 1, 0);
+    for (int32_t c = 0; c < num_chunks; ++c) {
+        voff[c + 1] = voff[c] + static_cast<uint64_t>(counts[c]);
+        soff[c + 1] = soff[c] + align256(chunk_bound(static_cast<uint64_t>(counts[c])));
+    }
+    hipStream_t sc = static_cast<hipStream_t>(s_comp);
+    hipStream_t sl = static_cast<hipStream_t>(s_link);
+    hipStream_t sd = static_cast<hipStream_t>(s_dec);
+    uint8_t* send = static_cast<uint8_t*>(d_send);
+    uint8_t* recv = static_cast<uint8_t*>(d_recv);
+
+    for (int32_t g = 0; g < groups; ++g) {
+        const int32_t c0 = static_cast<int32_t>(static_cast<int64_t>(g) * num_chunks / groups);
+        const int32_t c1 = static_cast<int32_t>(static_cast<int64_t>(g + 1) * num_chunks / groups);
+        const int32_t m = c1 - c0;
+        const uint64_t gbytes = soff[c1] - soff[c0];
+        // 1. compress the group into the sender's slots (in order on s_comp,
+        //    so every group may use the one workspace)
+        int r = zc_compress(d_in + voff[c0], counts + c0, m, send + soff[c0], gbytes,
+                            d_comp_sizes + c0, d_ws, ws_bytes, sc);
+        if (r != ZC_OK)
+            return r;
+        hipEvent_t compressed, sent;
+        if (hipEventCreateWithFlags(&compressed, hipEventDisableTiming) != hipSuccess)
+            return ZC_EHIP;
+        if (hipEventCreateWithFlags(&sent, hipEventDisableTiming) != hipSuccess) {
+            hipEventDestroy(compressed);
+            return ZC_EHIP;
+        }
+        bool ok = hipEventRecord(compressed, sc) == hipSuccess
+                  && hipStreamWaitEvent(sl, compressed, 0) == hipSuccess;
+        // 2. the link: the group's streams, comp_sizes bytes each
+        for (int32_t b0 = c0; ok && b0 < c1; b0 += kMaxChunks) {
+            const int32_t bm = std::min(c1 - b0, kMaxChunks);
+            LinkTable lt;
+            std::memset(&lt, 0, sizeof lt);
+            for (int32_t i = 0; i < bm; ++i) {
+                lt.slot[i] = soff[b0 + i] - soff[b0];
+                lt.bound[i] = soff[b0 + i + 1] - soff[b0 + i];
+            }
+            const uint32_t bx = std::max(1u, 2048u / static_cast<uint32_t>(bm));
+            hipLaunchKernelGGL(zc_link_copy_kernel, dim3(bx, static_cast<uint32_t>(bm)), dim3(kBlock),
+                               0, sl, send + soff[b0], recv + soff[b0], d_comp_sizes + b0, lt);
+            ok = hipGetLastError() == hipSuccess;
+        }
+        ok = ok && hipEventRecord(sent, sl) == hipSuccess
+             && hipStreamWaitEvent(sd, sent, 0) == hipSuccess;
+        // the waits have been queued: the events are released once they complete
+        hipEventDestroy(compressed);
+        hipEventDestroy(sent);
+        if (!ok)
+            return ZC_EHIP;
+        // 3. decompress the group from the receiver's slots
+        r = zc_decompress(recv + soff[c0], gbytes, nullptr, counts + c0, m, d_out + voff[c0],
+                          d_status, sd);
+        if (r != ZC_OK)
+            return r;
     }
     return ZC_OK;
 }

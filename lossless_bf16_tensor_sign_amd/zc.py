@@ -88,6 +88,11 @@ def lib():
         L.zc_decompress_reduce.restype = ct.c_int
         L.zc_decompress_reduce_bf16.argtypes = L.zc_decompress_reduce.argtypes
         L.zc_decompress_reduce_bf16.restype = ct.c_int
+        L.zc_pipeline.argtypes = [ct.c_void_p, i64p, ct.c_int32, ct.c_int32, ct.c_void_p,
+                                  ct.c_void_p, ct.c_size_t, ct.c_void_p, ct.c_void_p,
+                                  ct.c_void_p, ct.c_void_p, ct.c_size_t, ct.c_void_p,
+                                  ct.c_void_p, ct.c_void_p]
+        L.zc_pipeline.restype = ct.c_int
         L.zc_estimate.argtypes = [ct.c_void_p, ct.c_void_p, ct.c_int32, ct.c_int64,
                                   ct.c_int32, ct.c_void_p, ct.c_void_p]
         L.zc_estimate.restype = ct.c_int
@@ -221,6 +226,19 @@ def zc_decompress_reduce(d_in, n, num_chunks, d_out, d_status, d_scratch, in_off
                   _ptr(d_scratch), sb, _stream(stream)))
 
 
+def zc_pipeline(d_in, counts, groups, d_send, d_recv, d_comp_sizes, d_out, d_status, d_ws,
+                s_comp=None, s_link=None, s_dec=None, capacity=None, ws_bytes=None) -> int:
+    """Queue the chunk-pipelined compress -> link -> decompress exchange."""
+    a, p = _counts(counts)
+    cap = min(d_send.numel() * d_send.element_size(),
+              d_recv.numel() * d_recv.element_size()) if capacity is None else capacity
+    wsb = d_ws.numel() * d_ws.element_size() if ws_bytes is None else ws_bytes
+    return int(lib().zc_pipeline(_ptr(d_in), p, len(a), int(groups), _ptr(d_send),
+                                 _ptr(d_recv), cap, _ptr(d_comp_sizes), _ptr(d_out),
+                                 _ptr(d_status), _ptr(d_ws), wsb, _stream(s_comp),
+                                 _stream(s_link), _stream(s_dec)))
+
+
 def zc_estimate(d_in, d_counts, total_values, samples_per_chunk, d_est, stream=None) -> int:
     """Queue the sampled size estimate of each chunk (int64 device tensors)."""
     return int(lib().zc_estimate(_ptr(d_in), _ptr(d_counts), d_counts.numel(),
@@ -347,3 +365,33 @@ def estimate(x, d_counts, samples_per_chunk=8, stream=None):
     if r != ZC_OK:
         raise ZcError(r, "zc_estimate")
     return est[:d_counts.numel()]
+
+
+def pipeline(x, counts, groups, streams=None, check=True):
+    """Chunk-pipelined exchange of int16/uint16 device tensor x: returns
+    (y, status, send, recv, sizes) with y the decoded values.  streams =
+    (compress, link, decompress) torch streams, default all current."""
+    import torch
+    a = np.asarray(counts, np.int64)
+    cap = zc_bound(a)
+    send = torch.empty(max(cap, 16), dtype=torch.uint8, device=x.device)
+    recv = torch.zeros(max(cap, 16), dtype=torch.uint8, device=x.device)
+    sizes = torch.empty(max(len(a), 1), dtype=torch.int64, device=x.device)
+    ws = torch.empty(max(zc_workspace_bytes(a), 16), dtype=torch.uint8, device=x.device)
+    y = torch.empty(int(a.sum()), dtype=x.dtype, device=x.device)
+    status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    sc, sl, sd = (None, None, None) if streams is None else streams
+    cur = torch.cuda.current_stream()
+    for s_ in (sc, sl, sd):      # the buffers above were written on cur
+        if s_ is not None:
+            s_.wait_stream(cur)
+    r = zc_pipeline(x, a, groups, send, recv, sizes, y, status, ws, s_comp=sc, s_link=sl,
+                    s_dec=sd)
+    if r != ZC_OK:
+        raise ZcError(r, "zc_pipeline")
+    if check:
+        (torch.cuda.current_stream() if sd is None else sd).synchronize()
+        st = int(status.item())
+        if st != 0:
+            raise ZcError(ZC_ECORRUPT, "zc_pipeline: status %#x" % st)
+    return y, status, send, recv, sizes

@@ -178,3 +178,39 @@ def test_estimate_argument_errors_before_any_gpu_work():
     assert lib.zc_estimate(None, V(0x2000), 2, 10, 4, V(0x3000), None) == zc.ZC_EINVAL
     assert lib.zc_estimate(None, None, 0, 5, 4, None, None) == zc.ZC_EINVAL
     assert lib.zc_estimate(None, None, 0, 0, 4, None, None) == zc.ZC_OK
+
+
+def test_pipeline_argument_errors_before_any_gpu_work():
+    lib = zc.lib()
+    import ctypes as ct
+    import numpy as np
+    V = ct.c_void_p
+    big = 1 << 30
+    counts = np.array([100, 9000, 0], np.int64)
+    cp = counts.ctypes.data_as(ct.POINTER(ct.c_int64))
+    ws = zc.zc_workspace_bytes(counts)
+    cap = zc.zc_bound(counts)
+
+    def call(d_in=V(0x1000), groups=2, send=V(0x2000), recv=V(0x3000), capacity=big,
+             sizes=V(0x4000), out=V(0x5000), status=V(0x6000), d_ws=V(0x7000), ws_bytes=big,
+             num_chunks=3):
+        return lib.zc_pipeline(d_in, cp, num_chunks, groups, send, recv, capacity, sizes, out,
+                               status, d_ws, ws_bytes, None, None, None)
+    # groups outside 1..num_chunks
+    assert call(groups=0) == zc.ZC_EINVAL
+    assert call(groups=4) == zc.ZC_EINVAL
+    assert call(groups=-1) == zc.ZC_EINVAL
+    # null buffers
+    for kw in ("send", "recv", "sizes", "status", "d_ws", "d_in", "out"):
+        assert call(**{kw: None}) == zc.ZC_EINVAL, kw
+    # misaligned send / receive slots (16 bytes), values (2 bytes), sizes (8 bytes)
+    assert call(send=V(0x2008)) == zc.ZC_EINVAL
+    assert call(recv=V(0x3004)) == zc.ZC_EINVAL
+    assert call(d_in=V(0x1001)) == zc.ZC_EINVAL
+    assert call(out=V(0x5001)) == zc.ZC_EINVAL
+    assert call(sizes=V(0x4004)) == zc.ZC_EINVAL
+    # capacity and workspace one byte short
+    assert call(capacity=cap - 1) == zc.ZC_ENOSPC
+    assert call(ws_bytes=ws - 1) == zc.ZC_ENOSPC
+    # no chunks: nothing to do
+    assert call(num_chunks=0, groups=1) == zc.ZC_OK
