@@ -19,19 +19,22 @@
 //    Figure 7 caption), which is stored coalesced;
 //  * the byte offset of a tile inside its chunk's exponent section is an
 //    exclusive scan over the tiles of the chunk, done in the same pass with a
-//    decoupled look-back over per-tile status words.  Equal chunks take their
-//    tiles from per-chunk ticket counters, so every tile a workgroup waits on
-//    is already running; uneven chunks take them in grid order (one shared
-//    counter would serialize a large chunk's workgroups).  Every wait is
-//    bounded: past the bound a missing predecessor's size is recomputed from
-//    its input;
+//    decoupled look-back over per-tile status words.  A workgroup's tile
+//    comes from its grid position: round-robin over equal chunks, chunk by
+//    chunk otherwise.  Every wait is bounded: past the bound a missing
+//    predecessor's size is recomputed from its input, so no order of
+//    dispatch can stall it;
 //  * all chunks of a call form one flat list of tiles, so uneven chunk sizes
 //    (the imbalance of Figure 8) still fill the GPU;
-//  * the inner loops are branch-free: the encoder appends one code word per
-//    value to a 64-bit accumulator and ORs each finished word into LDS; the
-//    decoder refills a 64-bit window from LDS every four symbols and takes
-//    one table lookup per symbol (code words longer than the lookup width,
-//    and escapes, take a rare second lookup).
+//  * the inner loops are branch-free: the encoder appends code words (two
+//    members per table entry where no escape occurs) to a 64-bit
+//    accumulator and ORs each finished word into LDS; the decoder refills a
+//    64-bit window from LDS every four or eight symbols and takes one table
+//    lookup per symbol (code words longer than the lookup width, and
+//    escapes, take a rare second lookup);
+//  * no value is carried in a register that a memory load must refill inside
+//    a loop or across the encoder's emission: on this hardware the wait for
+//    such a load also waits for every older store of the wave.
 // No floating point runs on the device.
 #include <hip/hip_runtime.h>
 
@@ -925,10 +928,9 @@ __device__ __forceinline__ void compress_body(const uint16_t* __restrict__ in,
     // The workgroup's chunk comes from its position in the grid: round-robin
     // over the chunks when they all have the same number of tiles, so that
     // few tiles of one chunk are in flight at once; chunk by chunk otherwise.
-    // With equal chunks its tile within the chunk comes from that chunk's
-    // ticket counter (requested first, so that the round trip overlaps the
-    // table set-up), and a tile only waits for lower tickets of its chunk,
-    // held by workgroups that are already running.
+    // The tile within the chunk is the grid position too (tile_order), or,
+    // in the ticket order, the chunk's ticket counter (requested first, so
+    // that the round trip overlaps the table set-up).
     const uint32_t item = blockIdx.x;
     TileCtx x;
     if (ZC_ENC_INTERLEAVE && tab.uniform_tiles)
