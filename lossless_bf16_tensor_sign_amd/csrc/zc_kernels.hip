@@ -2360,7 +2360,7 @@ int zc_pipeline(const uint16_t* d_in, const int64_t* counts, int32_t num_chunks,
         if (hipEventCreateWithFlags(&compressed, hipEventDisableTiming) != hipSuccess)
             return ZC_EHIP;
         if (hipEventCreateWithFlags(&sent, hipEventDisableTiming) != hipSuccess) {
-            hipEventDestroy(compressed);
+            (void)hipEventDestroy(compressed);
             return ZC_EHIP;
         }
         bool ok = hipEventRecord(compressed, sc) == hipSuccess
@@ -2382,8 +2382,8 @@ int zc_pipeline(const uint16_t* d_in, const int64_t* counts, int32_t num_chunks,
         ok = ok && hipEventRecord(sent, sl) == hipSuccess
              && hipStreamWaitEvent(sd, sent, 0) == hipSuccess;
         // the waits have been queued: the events are released once they complete
-        hipEventDestroy(compressed);
-        hipEventDestroy(sent);
+        (void)hipEventDestroy(compressed);
+        (void)hipEventDestroy(sent);
         if (!ok)
             return ZC_EHIP;
         // 3. decompress the group from the receiver's slots
