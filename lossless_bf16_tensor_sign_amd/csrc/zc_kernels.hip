@@ -20,10 +20,10 @@
 //  * the byte offset of a tile inside its chunk's exponent section is an
 //    exclusive scan over the tiles of the chunk, done in the same pass with a
 //    decoupled look-back over per-tile status words.  A workgroup's tile
-//    comes from its grid position: round-robin over equal chunks, chunk by
-//    chunk otherwise.  Every wait is bounded: past the bound a missing
-//    predecessor's size is recomputed from its input, so no order of
-//    dispatch can stall it;
+//    comes from its grid position, chunk by chunk, so neighbouring
+//    workgroups stream neighbouring bytes.  Every wait is bounded: past the
+//    bound a missing predecessor's size is recomputed from its input, so no
+//    order of dispatch can stall it;
 //  * all chunks of a call form one flat list of tiles, so uneven chunk sizes
 //    (the imbalance of Figure 8) still fill the GPU;
 //  * the inner loops are branch-free: the encoder appends code words (two
@@ -55,7 +55,7 @@
 #define ZC_ENC_WAVES 8           // compress occupancy target, waves per SIMD
 #endif
 #ifndef ZC_ENC_INTERLEAVE
-#define ZC_ENC_INTERLEAVE 1      // equal-size chunks: hand out tiles round-robin
+#define ZC_ENC_INTERLEAVE 0      // equal-size chunks: hand out tiles round-robin (else chunk by chunk)
 #endif
 #ifndef ZC_EARLY_LOAD
 #define ZC_EARLY_LOAD 1          // grid-ordered full tiles: loads issued before the table set-up
@@ -925,11 +925,10 @@ __device__ __forceinline__ void compress_body(const uint16_t* __restrict__ in,
     const uint32_t lane = tid & (kLanes - 1);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kLanes);   // uniform: scalar
 
-    // The workgroup's chunk comes from its position in the grid: round-robin
-    // over the chunks when they all have the same number of tiles, so that
-    // few tiles of one chunk are in flight at once; chunk by chunk otherwise.
-    // The tile within the chunk is the grid position too (tile_order), or,
-    // in the ticket order, the chunk's ticket counter (requested first, so
+    // The workgroup's chunk and tile come from its position in the grid
+    // (tile_order): chunk by chunk by default; with ZC_ENC_INTERLEAVE equal
+    // chunks are taken round-robin, and in the ticket order the tile within
+    // the chunk comes from the chunk's ticket counter (requested first, so
     // that the round trip overlaps the table set-up).
     const uint32_t item = blockIdx.x;
     TileCtx x;
