@@ -164,8 +164,6 @@ __device__ inline uint32_t tail_of(uint32_t i)
     return v;
 }
 
-// Chunks of one launch.  Work item = one tile; an empty chunk gets one item
-// that only writes its header.
 // Compress tile orders.  Tickets: workgroups take the chunks round-robin and
 // number their tiles from per-chunk counters.  Chunks: grid position = tile
 // index, chunk by chunk.  RoundRobin: grid position g is tile g / C of chunk
@@ -181,6 +179,8 @@ __host__ __device__ inline uint32_t tile_order(uint32_t uniform_tiles)
     return ZC_ENC_TICKETS ? kOrderTickets : kOrderRoundRobin;
 }
 
+// Chunks of one launch.  Work item = one tile; an empty chunk gets one item
+// that only writes its header.
 struct ChunkTable {
     int32_t nchunks;
     uint32_t nitems;
@@ -2108,8 +2108,7 @@ int zc_compress(const uint16_t* d_in, const int64_t* counts, int32_t num_chunks,
         for (int32_t i = 0; i < m && tab.uniform_tiles; ++i)
             if (tab.item_begin[i + 1] - tab.item_begin[i] != tab.uniform_tiles || tab.n[i] == 0)
                 tab.uniform_tiles = 0;
-        // Equal chunks are taken round-robin by grid position; otherwise
-        // chunk by chunk (tile_order).
+        // Tiles in grid order, chunk by chunk (tile_order).
         tab.grid_order = tile_order(tab.uniform_tiles);
         tab.spin_limit = spin_limit;
 

@@ -203,8 +203,8 @@ def test_workload_full_size(oracle, cfg):
 def test_lookback_recompute_path(oracle, monkeypatch, layout):
     # A spin limit of 0: every tile that finds a predecessor unpublished
     # recomputes that predecessor's size from its input at once.  The
-    # streams must not change, with tiles taken from tickets (equal chunks)
-    # and in grid order (uneven chunks).
+    # streams must not change, for equal chunks and for uneven ones (tiles
+    # taken chunk by chunk in grid order).
     monkeypatch.setenv("ZC_LOOKBACK_SPIN_LIMIT", "0")
     if layout == "equal":
         cnt = np.full(8, 6 * TILE, np.int64)
