@@ -417,15 +417,21 @@ __device__ inline void load_tile(const TileCtx& x, uint4 (&v)[kLoadBatch], int b
         if (FULL) {
             v[k] = ld_nt4(sbase + k * 1024);
         } else {
+            // a segment of 8 values wholly inside the chunk at a 16-byte
+            // aligned address is one load; the ragged end value by value
             const uint32_t i0 = x.base + (k0 + k) * 512 + x.lane * 8;
-            uint32_t w[8];
+            if (i0 + 8 <= x.n && (reinterpret_cast<uintptr_t>(x.src + i0) & 15) == 0) {
+                v[k] = ld_nt4(x.src + i0);
+            } else {
+                uint32_t w[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                w[j] = (i0 + j < x.n) ? x.src[i0 + j] : 0u;
-            v[k].x = w[0] | (w[1] << 16);
-            v[k].y = w[2] | (w[3] << 16);
-            v[k].z = w[4] | (w[5] << 16);
-            v[k].w = w[6] | (w[7] << 16);
+                for (int j = 0; j < 8; ++j)
+                    w[j] = (i0 + j < x.n) ? x.src[i0 + j] : 0u;
+                v[k].x = w[0] | (w[1] << 16);
+                v[k].y = w[2] | (w[3] << 16);
+                v[k].z = w[4] | (w[5] << 16);
+                v[k].w = w[6] | (w[7] << 16);
+            }
         }
     }
 }
@@ -459,11 +465,15 @@ __device__ inline uint32_t split_tile(const TileCtx& x, const uint4 (&v)[kLoadBa
             st_nt2(rbase + kb * 512, make_uint2(raw_a, raw_b));
         } else {
             const uint32_t i0 = x.base + (k0 + kb) * 512 + x.lane * 8;
-            uint8_t* rdst = x.dst + x.G.R + i0;
+            uint8_t* rdst = x.dst + x.G.R + i0;      // 8-byte aligned (R and i0 are)
+            if (i0 + 8 <= x.n) {
+                st_nt2(rdst, make_uint2(raw_a, raw_b));
+            } else {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (i0 + j < x.n)
-                    rdst[j] = static_cast<uint8_t>(((j < 4 ? raw_a : raw_b) >> (8 * (j & 3))) & 0xFF);
+                for (int j = 0; j < 8; ++j)
+                    if (i0 + j < x.n)
+                        rdst[j] = static_cast<uint8_t>(((j < 4 ? raw_a : raw_b) >> (8 * (j & 3))) & 0xFF);
+            }
         }
     }
     return mx >> 7;   // missing members were loaded as 0
@@ -1120,7 +1130,14 @@ __device__ inline void put_values(uint16_t* __restrict__ dst, const uint8_t* __r
                                   uint32_t n, uint32_t i0, uint2 r, const uint32_t (&e8)[8],
                                   bool vec_out)
 {
-    if (FULL && vec_out) {
+    // a partial tile takes the vector form for segments of 8 values wholly
+    // inside the chunk whose output is 16-byte aligned (the raw bytes are
+    // 8-byte aligned: stream slots, R and i0 are)
+    const bool vec = FULL ? vec_out
+                          : (i0 + 8 <= n && (reinterpret_cast<uintptr_t>(dst + i0) & 15) == 0);
+    if (vec) {
+        if (!FULL)
+            r = ld_nt2(rsrc + i0);
         uint4 o;
         o.x = (__builtin_amdgcn_perm(r.x, r.x, 0x01010000u) & 0x807F807Fu) | (e8[0] << 7) | (e8[1] << 23);
         o.y = (__builtin_amdgcn_perm(r.x, r.x, 0x03030202u) & 0x807F807Fu) | (e8[2] << 7) | (e8[3] << 23);
