@@ -91,6 +91,15 @@
 #define ZC_ENC_PAIRS 2           // compress: full tiles emit member pairs from one table entry
                                  // (0 never, 1 in waves with raw groups, 2 always)
 #endif
+#ifndef ZC_RAW_NT
+#define ZC_RAW_NT 0              // compress: raw bytes stored with the nontemporal hint
+#endif
+#ifndef ZC_STREAM_NT
+#define ZC_STREAM_NT 0           // compress: tile streams stored with the nontemporal hint
+#endif
+#ifndef ZC_DEC_OUT_NT
+#define ZC_DEC_OUT_NT 1          // decompress: values stored with the nontemporal hint
+#endif
 #ifndef ZC_ENC_BATCH
 #define ZC_ENC_BATCH 0           // compress: a step's table lookups issued together (1 pairs, 2 escapes)
 #endif
@@ -462,7 +471,10 @@ __device__ inline uint32_t split_tile(const TileCtx& x, const uint4 (&v)[kLoadBa
         mx = max(mx, max(max(q.z & 0x7F80u, (q.z >> 16) & 0x7F80u),
                          max(q.w & 0x7F80u, (q.w >> 16) & 0x7F80u)));
         if (FULL) {
-            st_nt2(rbase + kb * 512, make_uint2(raw_a, raw_b));
+            if (ZC_RAW_NT)
+                st_nt2(rbase + kb * 512, make_uint2(raw_a, raw_b));
+            else
+                *reinterpret_cast<uint2*>(rbase + kb * 512) = make_uint2(raw_a, raw_b);
         } else {
             const uint32_t i0 = x.base + (k0 + kb) * 512 + x.lane * 8;
             uint8_t* rdst = x.dst + x.G.R + i0;      // 8-byte aligned (R and i0 are)
@@ -886,8 +898,12 @@ __device__ __forceinline__ void compress_tile_back(const TileCtx& x, uint32_t (&
                 v[i] = sh.stage[min(r0 + i * kLanes + lane, static_cast<uint32_t>(kEncStage - 1))];
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                if (r0 + i * kLanes + lane < tile_words)
-                    st_nt1(gstream + r0 + i * kLanes + lane, v[i]);
+                if (r0 + i * kLanes + lane < tile_words) {
+                    if (ZC_STREAM_NT)
+                        st_nt1(gstream + r0 + i * kLanes + lane, v[i]);
+                    else
+                        gstream[r0 + i * kLanes + lane] = v[i];
+                }
         }
     }
     write_tile_index(x, toff, tile_bytes, emax, glen, comp_sizes);
@@ -1143,7 +1159,10 @@ __device__ inline void put_values(uint16_t* __restrict__ dst, const uint8_t* __r
         o.y = (__builtin_amdgcn_perm(r.x, r.x, 0x03030202u) & 0x807F807Fu) | (e8[2] << 7) | (e8[3] << 23);
         o.z = (__builtin_amdgcn_perm(r.y, r.y, 0x01010000u) & 0x807F807Fu) | (e8[4] << 7) | (e8[5] << 23);
         o.w = (__builtin_amdgcn_perm(r.y, r.y, 0x03030202u) & 0x807F807Fu) | (e8[6] << 7) | (e8[7] << 23);
-        st_nt4(dst + i0, o);
+        if (ZC_DEC_OUT_NT)
+            st_nt4(dst + i0, o);
+        else
+            *reinterpret_cast<uint4*>(dst + i0) = o;
     } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
