@@ -100,6 +100,12 @@
 #ifndef ZC_DEC_OUT_NT
 #define ZC_DEC_OUT_NT 1          // decompress: values stored with the nontemporal hint
 #endif
+#ifndef ZC_ENC_LOAD_NT
+#define ZC_ENC_LOAD_NT 1         // compress: input loads with the nontemporal hint
+#endif
+#ifndef ZC_DEC_LOAD_NT
+#define ZC_DEC_LOAD_NT 1         // decompress: stream and raw-byte loads with the nontemporal hint
+#endif
 #ifndef ZC_ENC_BATCH
 #define ZC_ENC_BATCH 0           // compress: a step's table lookups issued together (1 pairs, 2 escapes)
 #endif
@@ -424,7 +430,8 @@ __device__ inline void load_tile(const TileCtx& x, uint4 (&v)[kLoadBatch], int b
 #pragma unroll
     for (int k = 0; k < kLoadBatch; ++k) {
         if (FULL) {
-            v[k] = ld_nt4(sbase + k * 1024);
+            v[k] = ZC_ENC_LOAD_NT ? ld_nt4(sbase + k * 1024)
+                                  : *reinterpret_cast<const uint4*>(sbase + k * 1024);
         } else {
             // a segment of 8 values wholly inside the chunk at a 16-byte
             // aligned address is one load; the ragged end value by value
@@ -1212,7 +1219,7 @@ __device__ __forceinline__ void decode_group(const Win& win, const uint8_t* __re
     uint2 ring[kRing];
 #pragma unroll
     for (int j = 0; j < kRing; ++j)
-        ring[j] = FULL ? ld_nt2(rsrc2 + j * 64) : make_uint2(0, 0);
+        ring[j] = FULL ? (ZC_DEC_LOAD_NT ? ld_nt2(rsrc2 + j * 64) : rsrc2[j * 64]) : make_uint2(0, 0);
 #pragma unroll 1
     for (int k0 = 0; k0 < kSteps; k0 += kRing)
 #pragma unroll
@@ -1284,7 +1291,8 @@ __device__ __forceinline__ void decode_group(const Win& win, const uint8_t* __re
         }
         put_values<FULL>(dst, rsrc, n, base + k * 512 + lane * 8, ring[kj], e8, vec_out);
         if (FULL)   // the last round reloads the last row (in bounds, unused)
-            ring[kj] = ld_nt2(rsrc2 + min(k + kRing, kSteps - 1) * 64);
+            ring[kj] = ZC_DEC_LOAD_NT ? ld_nt2(rsrc2 + min(k + kRing, kSteps - 1) * 64)
+                                      : rsrc2[min(k + kRing, kSteps - 1) * 64];
     }
 }
 
@@ -1300,7 +1308,8 @@ __device__ inline void stage_words(uint32_t* __restrict__ s, const uint32_t* __r
 #pragma unroll
     for (int i = 0; i < kRows; ++i)
         if (static_cast<uint32_t>(i * kLanes) < words)
-            v[i] = ld_nt1(g + min(lane + i * kLanes, words - 1));
+            v[i] = ZC_DEC_LOAD_NT ? ld_nt1(g + min(lane + i * kLanes, words - 1))
+                                  : g[min(lane + i * kLanes, words - 1)];
 #pragma unroll
     for (int i = 0; i < kRows; ++i)
         if (lane + i * kLanes < words)
