@@ -115,6 +115,9 @@
 #ifndef ZC_DEC_WAVES
 #define ZC_DEC_WAVES 8           // decompress occupancy target, waves per SIMD
 #endif
+#ifndef ZC_ESC_PAIRS
+#define ZC_ESC_PAIRS 1           // compress: escape steps of coded-only waves emit two members per OR
+#endif
 
 namespace {
 
@@ -737,24 +740,50 @@ __device__ __forceinline__ void emit_quarter(uint32_t* __restrict__ s, const Enc
                 for (int j = 0; j < 8; ++j)
                     es[j] = tb.esc[(d4[j >> 2] >> (8 * (j & 3))) & 0xFF];
             }
+            // Each member's word is its code, or the escape code and the
+            // exponent's 8 bits (at most 22 bits).  With ZC_ESC_PAIRS, in a
+            // wave without raw groups, two members go out with one LDS OR
+            // when their words fit in 32 bits on every lane (an escape
+            // beside a code of up to 10 bits).  Waves with raw groups keep
+            // one member per OR: the pairs there cost register spills.
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t d = (d4[j >> 2] >> (8 * (j & 3))) & 0xFF;
-                uint32_t ent = ((ZC_ENC_BATCH & 2) != 0) ? es[j] : tb.esc[d];
-                if (MIXED && raw_mode)
-                    ent = ((emax - d) & 0xFF) | (8u << 24);
-                const bool valid = FULL || first + static_cast<uint32_t>(k * 8 + j) < ng;
-                ent = valid ? ent : 0u;
-                const uint32_t L = (ent >> 24) & 31;
-                const uint32_t esc = static_cast<uint32_t>(static_cast<int32_t>(ent) >> 31);
-                acc <<= L;
-                acc |= (ent & 0x3FFFFFu) | ((emax - d) & esc & 0xFFu);
-                nacc += L;
-                const uint32_t w = __builtin_amdgcn_alignbit(hi32(acc), lo32(acc), nacc);
-                const uint32_t f = nacc >> 5;
-                atomicOr(&s[wi], f ? w : 0u);
-                wi += f;
-                nacc &= 31;
+            for (int j = 0; j < 8; j += ((ZC_ESC_PAIRS && !MIXED) ? 2 : 1)) {
+                constexpr int kU = (ZC_ESC_PAIRS && !MIXED) ? 2 : 1;
+                uint32_t cw[kU], L[kU];
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    const int jj = j + u;
+                    const uint32_t d = (d4[jj >> 2] >> (8 * (jj & 3))) & 0xFF;
+                    uint32_t ent = ((ZC_ENC_BATCH & 2) != 0) ? es[jj] : tb.esc[d];
+                    if (MIXED && raw_mode)
+                        ent = ((emax - d) & 0xFF) | (8u << 24);
+                    const bool valid = FULL || first + static_cast<uint32_t>(k * 8 + jj) < ng;
+                    ent = valid ? ent : 0u;
+                    L[u] = (ent >> 24) & 31;
+                    const uint32_t esc = static_cast<uint32_t>(static_cast<int32_t>(ent) >> 31);
+                    cw[u] = (ent & 0x3FFFFFu) | ((emax - d) & esc & 0xFFu);
+                }
+                if (kU == 2 && __ballot(L[0] + L[kU - 1] > 32u) == 0) {
+                    const uint32_t pl = L[0] + L[kU - 1];
+                    acc = (acc << pl) | ((cw[0] << L[kU - 1]) | cw[kU - 1]);
+                    nacc += pl;
+                    const uint32_t w = __builtin_amdgcn_alignbit(hi32(acc), lo32(acc), nacc);
+                    const uint32_t f = nacc >> 5;
+                    atomicOr(&s[wi], f ? w : 0u);
+                    wi += f;
+                    nacc &= 31;
+                } else {
+#pragma unroll
+                    for (int u = 0; u < kU; ++u) {
+                        acc = (acc << L[u]) | cw[u];
+                        nacc += L[u];
+                        const uint32_t w = __builtin_amdgcn_alignbit(hi32(acc), lo32(acc), nacc);
+                        const uint32_t f = nacc >> 5;
+                        atomicOr(&s[wi], f ? w : 0u);
+                        wi += f;
+                        nacc &= 31;
+                    }
+                }
             }
         }
     }
