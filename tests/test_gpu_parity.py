@@ -400,12 +400,32 @@ def _stress_tiles(kind, tiles, seed):
                 e = 110 + rng.integers(0, 4, size=6)
                 grid[t, pos // 8, lane, pos % 8] = (e << 7).astype(np.uint16)
             grid[t, 0, :, 0] = 125 << 7
+    elif kind == "escape_single":
+        # one zero per lane and step, its pair partner a short code: every
+        # escape pair fits in 32 bits (escape words are 22 bits)
+        for t in range(tiles):
+            for k in range(16):
+                j = 2 * rng.integers(0, 4, size=64) + rng.integers(0, 2, size=64)
+                grid[t, k, np.arange(64), j] = 0
+    elif kind == "escape_long":
+        # zeros whose pair partner is 11-14 binades below the group maximum
+        # (long code words): such a pair exceeds 32 bits, the others fit
+        for t in range(tiles):
+            grid[t, 0, :, 0] = 125 << 7
+            for lane in range(64):
+                for q in rng.choice(63, size=4, replace=False):
+                    m = 2 * (int(q) + 1)
+                    k, j = divmod(m, 8)
+                    grid[t, k, lane, j] = 0
+                    grid[t, k, lane, j + 1] = (111 + int(rng.integers(0, 4))) << 7
     return grid.reshape(-1)
 
 
-@pytest.mark.parametrize("kind", ["raw_heavy", "escape_runs", "long_codes"])
+@pytest.mark.parametrize("kind", ["raw_heavy", "escape_runs", "long_codes", "escape_single",
+                                  "escape_long"])
 def test_stress_layouts(oracle, kind):
-    seed = {"raw_heavy": 11, "escape_runs": 12, "long_codes": 13}[kind]
+    seed = {"raw_heavy": 11, "escape_runs": 12, "long_codes": 13, "escape_single": 14,
+            "escape_long": 15}[kind]
     w = _stress_tiles(kind, 5, seed=seed)
     n = w.size
     # full tiles, then the same data with a ragged tail and an unaligned start
@@ -422,3 +442,7 @@ def test_stress_paths_are_taken(oracle):
     assert toffs[1] - toffs[0] > 4096            # tile stream beyond the LDS buffer
     glen = s[32 + 68 * T:32 + 68 * T + 2 * NG].view(np.uint16)
     assert 0 < int((glen == 1024).sum()) < NG     # raw and coded groups mixed
+    for kind in ("escape_single", "escape_long"):
+        s = oracle.compress_chunk(_stress_tiles(kind, 2, seed=1))
+        glen = s[32 + 68 * T:32 + 68 * T + 2 * NG].view(np.uint16)
+        assert int(glen.max()) < 1024, kind       # every group coded
