@@ -92,6 +92,38 @@ def read_traffic(workload_name):
     return out
 
 
+def host_cpu():
+    """CPU model name and core counts of this host (from /proc/cpuinfo and the
+    scheduler's affinity mask)."""
+    model, sockets, cores_per = None, set(), {}
+    try:
+        with open("/proc/cpuinfo") as f:
+            phys = None
+            for ln in f:
+                k, _, v = ln.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "model name" and model is None:
+                    model = v
+                elif k == "physical id":
+                    phys = v
+                    sockets.add(v)
+                elif k == "cpu cores" and phys is not None:
+                    cores_per[phys] = int(v)
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {
+        "cpu_model": model,
+        "logical_cpus": os.cpu_count(),
+        "physical_cores": sum(cores_per.values()) if cores_per else None,
+        "sockets": len(sockets) if sockets else None,
+        "usable_cpus": usable,
+    }
+
+
 def cpu_baseline(w, counts, threads, budget_s):
     """The oracle on the host: one thread over the first chunk (per-core
     rate), then the first k chunks spread over `threads` threads, k chosen so
@@ -143,6 +175,7 @@ def cpu_baseline(w, counts, threads, budget_s):
         "wall_s": round(wall, 3),
         "comp_bytes_sample": int(sum(r[2] for r in res)),
         "roundtrip_ok": bool(ok),
+        "host": host_cpu(),
     }
 
 

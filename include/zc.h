@@ -60,22 +60,31 @@ typedef enum {
 /* Largest count per chunk (values). */
 #define ZC_MAX_CHUNK_VALUES 2147483647LL
 
+/* Largest num_chunks of any call: a decoder failure names its chunk in the
+ * low 24 bits of the status word, so every chunk index must fit there. */
+#define ZC_MAX_CHUNKS (1 << 24)
+
 /*
  * Worst-case bytes of the ZCB1 stream of one chunk of n values (every group
- * in raw mode): X + n + 4T.  Host only; returns 0 for n < 0.
+ * in raw mode): X + n + 4T, with X and T as in the layout above.  A function
+ * of the ZCB1 container of this file, not of the pages.  Host only; returns 0
+ * for n < 0.
  */
 size_t zc_chunk_bound(int64_t n);
 
 /*
  * Bytes of a slot-layout buffer for num_chunks chunks: the sum of
- * align256(zc_chunk_bound(counts[c])).  counts is a host array.  Returns 0
- * if an argument is invalid.
+ * align256(zc_chunk_bound(counts[c])) (the slot layout above).  counts is a
+ * host array.  Returns 0 if an argument is invalid (a count outside
+ * 0 .. ZC_MAX_CHUNK_VALUES, or num_chunks outside 0 .. ZC_MAX_CHUNKS).
  */
 size_t zc_bound(const int64_t* counts, int32_t num_chunks);
 
 /*
- * Device workspace bytes that zc_compress needs for these counts (look-back
- * status words and work counters).  Host only.
+ * Device workspace bytes that zc_compress needs for these counts: one
+ * look-back status word per tile of the largest launch (a launch takes up
+ * to 64 chunks), after a fixed header.  Sizing only, no passage of the pages
+ * behind it.  Host only; 0 if an argument is invalid.
  */
 size_t zc_workspace_bytes(const int64_t* counts, int32_t num_chunks);
 
@@ -90,7 +99,8 @@ size_t zc_workspace_bytes(const int64_t* counts, int32_t num_chunks);
  *                 stream's end inside its slot are left unwritten
  *   d_comp_sizes  device int64[num_chunks]: comp_bytes of each stream
  *   d_ws          device workspace of ws_bytes >= zc_workspace_bytes(...),
- *                 4-byte aligned; its contents need not be initialised
+ *                 8-byte aligned (its status words are 64-bit atomics); its
+ *                 contents need not be initialised
  *   stream        hipStream_t the work is queued on
  * Returns ZC_OK once the work is queued, or an error before anything is
  * queued (ZC_EINVAL, ZC_ENOSPC) or when a launch fails (ZC_EHIP).  Calls that
@@ -98,8 +108,8 @@ size_t zc_workspace_bytes(const int64_t* counts, int32_t num_chunks);
  * Every wait inside the kernel is bounded: a tile whose look-back finds a
  * predecessor unpublished after a fixed number of polls recomputes that
  * predecessor's size from the input, which gives the same stream.  The
- * environment variable ZC_LOOKBACK_SPIN_LIMIT (a decimal poll count, read at
- * each call) overrides that bound; tests set it to 0 to run that path.
+ * environment variable ZC_LOOKBACK_SPIN_LIMIT (a decimal poll count, read
+ * once per process, at the first compress call) overrides that bound.
  */
 int zc_compress(const uint16_t* d_in, const int64_t* counts,
                 int32_t num_chunks, void* d_out, size_t out_capacity,
@@ -107,8 +117,13 @@ int zc_compress(const uint16_t* d_in, const int64_t* counts,
                 void* stream);
 
 /*
- * Decompress num_chunks ZCB1 streams back to bf16 (strict: a stream is
- * accepted only if it is the exact output of zc_compress for its values).
+ * Decompress num_chunks ZCB1 streams back to bf16: the inverse of
+ * zc_compress, run after the collective has delivered the streams (ZipCCL
+ * abstract, technique (2): the GPU decompression kernels; shd-paper.top
+ * summary, technical framework: decompress after communication).  The codec
+ * is lossless (abstract), so the output is bit-identical to the compressed
+ * input.  Strict: a stream is accepted only if it is the exact output of
+ * zc_compress for its values.
  *   d_in        device, in_bytes readable bytes holding the streams
  *   in_offsets  host int64[num_chunks]: byte offset of stream c in d_in, each
  *               a multiple of 16; NULL means the slot layout
@@ -116,13 +131,17 @@ int zc_compress(const uint16_t* d_in, const int64_t* counts,
  *   d_out       device, sum(counts) bf16 values written back to back
  *   d_status    device int32, must be 0 on entry.  After the stream has run
  *               it is 0 if every stream was valid; otherwise it holds
- *               (reason << 24) | chunk for one failed check, reason >= 1
+ *               (reason << 24) | chunk for one failed check, reason >= 1,
+ *               chunk = the failing chunk's index in this call (0-based)
  *               (see zc_strerror of ZC_ECORRUPT; the reasons are listed with
  *               ZC_REASON_*).  Output values of a corrupt chunk are undefined,
- *               but nothing is read outside [offset, offset + comp_bytes) of
- *               a stream (nor past in_bytes) and nothing is written outside
- *               that chunk's part of d_out.
+ *               but nothing is written outside that chunk's part of d_out,
+ *               and nothing is read outside [offset, offset + max(comp_bytes,
+ *               X)) of a stream (X = the stream's fixed part, see the layout
+ *               above; the header and index are read before comp_bytes is
+ *               checked) nor past in_bytes.
  *   stream      hipStream_t
+ * No workspace: every tile's offset is read from the stream's tile index.
  * Returns ZC_OK once queued; ZC_EINVAL / ZC_EHIP as for zc_compress.
  */
 int zc_decompress(const void* d_in, size_t in_bytes,

@@ -201,6 +201,7 @@ __host__ __device__ inline uint32_t tile_order(uint32_t uniform_tiles)
 // that only writes its header.
 struct ChunkTable {
     int32_t nchunks;
+    int32_t chunk_base;            // index of the launch's first chunk in the call (status reports)
     uint32_t nitems;
     uint32_t uniform_tiles;        // > 0: every chunk has this many tiles
     uint32_t grid_order;           // compress tile order: kOrderTickets, kOrderChunks or kOrderRoundRobin
@@ -1596,22 +1597,23 @@ __device__ __forceinline__ void decompress_body(const uint8_t* __restrict__ in,
 
     if (!live)
         return;
+    const int cid = tab.chunk_base + c;     // the chunk's index in the call, for reports
     if (n == 0) {
         // a header-only stream
         const uint8_t* src = in + tab.boff[c];
         const uint32_t hw = lane < 8 ? reinterpret_cast<const uint32_t*>(src)[lane] : 0u;
         if (__ballot(lane < 8 && hw != header_word(lane, 0, 32)) && lane == 0)
-            report(status, ZC_REASON_HEADER, c);
+            report(status, ZC_REASON_HEADER, cid);
         return;
     }
     const uint8_t* src = in + tab.boff[c];
     uint16_t* dst = out + tab.voff[c];
     const uint32_t rem = min(n - t * kTile, static_cast<uint32_t>(kTile));
     if (rem == kTile && (reinterpret_cast<uintptr_t>(dst) & 15) == 0)
-        decompress_tile<true>(src, dst, status, c, n, t, tab.bavail[c], lane, s_stage[wave],
+        decompress_tile<true>(src, dst, status, cid, n, t, tab.bavail[c], lane, s_stage[wave],
                               s_lut8, s_tail, s_len, meta);
     else
-        decompress_tile_partial(src, dst, status, c, n, t, tab.bavail[c], lane, s_stage[wave],
+        decompress_tile_partial(src, dst, status, cid, n, t, tab.bavail[c], lane, s_stage[wave],
                                 s_lut8, s_tail, s_len, meta);
 }
 
@@ -1851,6 +1853,7 @@ void zc_plan_kernel(const int64_t* __restrict__ counts, int32_t num_chunks, int3
     if (lane == 0) {
         tab->item_begin[m] = items;
         tab->nchunks = m;
+        tab->chunk_base = c0;
         tab->nitems = bad ? 0u : items;
         tab->uniform_tiles = uniform;
         tab->grid_order = tile_order(uniform);
@@ -1997,7 +2000,7 @@ struct Counts {
 Counts check_counts(const int64_t* counts, int32_t num_chunks)
 {
     Counts r{false, 0, 0};
-    if (num_chunks < 0 || (num_chunks > 0 && !counts))
+    if (num_chunks < 0 || num_chunks > ZC_MAX_CHUNKS || (num_chunks > 0 && !counts))
         return r;
     for (int32_t c = 0; c < num_chunks; ++c) {
         if (counts[c] < 0 || counts[c] > ZC_MAX_CHUNK_VALUES)
@@ -2012,16 +2015,20 @@ Counts check_counts(const int64_t* counts, int32_t num_chunks)
 
 
 // Look-back polls a tile makes before it recomputes a missing predecessor's
-// size from the input.  The environment variable ZC_LOOKBACK_SPIN_LIMIT
-// overrides the default (tests set 0 to run the recomputation path).
+// size from the input.  The environment variable ZC_LOOKBACK_SPIN_LIMIT, read
+// once per process at the first compress call, overrides the default (tests
+// set 0 in a child process to run the recomputation path).
 uint32_t lookback_spin_limit()
 {
-    const char* e = std::getenv("ZC_LOOKBACK_SPIN_LIMIT");
-    if (!e || !*e)
-        return kSpinLimit;
-    char* end = nullptr;
-    const unsigned long v = std::strtoul(e, &end, 10);
-    return (end && *end == 0 && v <= 0xFFFFFFFFul) ? static_cast<uint32_t>(v) : kSpinLimit;
+    static const uint32_t limit = [] {
+        const char* e = std::getenv("ZC_LOOKBACK_SPIN_LIMIT");
+        if (!e || !*e)
+            return kSpinLimit;
+        char* end = nullptr;
+        const unsigned long v = std::strtoul(e, &end, 10);
+        return (end && *end == 0 && v <= 0xFFFFFFFFul) ? static_cast<uint32_t>(v) : kSpinLimit;
+    }();
+    return limit;
 }
 
 constexpr size_t kWsHeader = kMaxChunks * kTicketStride * 4;   // per-chunk ticket counters
@@ -2042,7 +2049,8 @@ uint64_t dev_max_items(int64_t total, int32_t m)
 
 bool dev_args_ok(int64_t total, int32_t num_chunks)
 {
-    return num_chunks >= 0 && total >= 0 && (num_chunks > 0 || total == 0) &&
+    return num_chunks >= 0 && num_chunks <= ZC_MAX_CHUNKS && total >= 0 &&
+           (num_chunks > 0 || total == 0) &&
            dev_max_items(total, num_chunks < kMaxChunks ? num_chunks : kMaxChunks) < (1ull << 31);
 }
 
@@ -2058,13 +2066,65 @@ uint64_t dev_tables_offset(int64_t total, int32_t num_chunks)
 
 namespace {
 
+// zc_decompress; reported chunk indices start at chunk_base (zc_pipeline
+// decodes group by group and reports indices of the whole call).
+int decompress_chunks(const void* d_in, size_t in_bytes, const int64_t* in_offsets,
+                      const int64_t* counts, int32_t num_chunks, uint16_t* d_out,
+                      int32_t* d_status, void* stream, int32_t chunk_base)
+{
+    const Counts k = check_counts(counts, num_chunks);
+    if (!k.ok)
+        return ZC_EINVAL;
+    if (num_chunks == 0)
+        return ZC_OK;
+    if (!d_in || !d_status || (k.total_values && !d_out))
+        return ZC_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(d_in) & 15) || (reinterpret_cast<uintptr_t>(d_out) & 1)
+        || (reinterpret_cast<uintptr_t>(d_status) & 3))
+        return ZC_EINVAL;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint8_t* in = static_cast<const uint8_t*>(d_in);
+    uint64_t voff = 0, slot = 0;
+    for (int32_t c0 = 0; c0 < num_chunks; c0 += kMaxChunks) {
+        ChunkTable tab;
+        std::memset(&tab, 0, sizeof tab);
+        uint32_t items = 0;
+        int32_t m = 0;
+        for (int32_t c = c0; c < num_chunks && c < c0 + kMaxChunks; ++c, ++m) {
+            const uint64_t n = static_cast<uint64_t>(counts[c]);
+            const uint64_t T = (n + kTile - 1) / kTile;
+            const int64_t off = in_offsets ? in_offsets[c] : static_cast<int64_t>(slot);
+            if (off < 0 || (off & 15) || static_cast<uint64_t>(off) + 32 > in_bytes)
+                return ZC_EINVAL;
+            tab.item_begin[m] = items;
+            tab.n[m] = static_cast<uint32_t>(n);
+            tab.voff[m] = voff;
+            tab.boff[m] = static_cast<uint64_t>(off);
+            tab.bavail[m] = in_bytes - static_cast<uint64_t>(off);
+            items += static_cast<uint32_t>(T ? T : 1);
+            voff += n;
+            slot += align256(chunk_bound(n));
+        }
+        tab.nchunks = m;
+        tab.chunk_base = chunk_base + c0;
+        tab.nitems = items;
+        tab.item_begin[m] = items;
+        hipLaunchKernelGGL(zc_decompress_kernel, dim3((items + kWaves - 1) / kWaves), dim3(kBlock), 0, s, in,
+                           d_out, d_status, tab);
+        if (hipGetLastError() != hipSuccess)
+            return ZC_EHIP;
+    }
+    return ZC_OK;
+}
+
 // Decode num_chunks streams of n values into the staging buffer, then sum
 // them (fp32 output, or bf16 when `bf16`).
 int decompress_reduce(const void* d_in, size_t in_bytes, const int64_t* in_offsets, int64_t n,
                       int32_t num_chunks, void* d_out, bool bf16, int32_t* d_status,
                       void* d_scratch, size_t scratch_bytes, void* stream)
 {
-    if (n < 0 || n > ZC_MAX_CHUNK_VALUES || num_chunks < 0)
+    if (n < 0 || n > ZC_MAX_CHUNK_VALUES || num_chunks < 0 || num_chunks > ZC_MAX_CHUNKS)
         return ZC_EINVAL;
     if (n == 0)
         return ZC_OK;
@@ -2077,8 +2137,8 @@ int decompress_reduce(const void* d_in, size_t in_bytes, const int64_t* in_offse
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (num_chunks > 0) {
         std::vector<int64_t> counts(static_cast<size_t>(num_chunks), n);
-        const int r = zc_decompress(d_in, in_bytes, in_offsets, counts.data(), num_chunks,
-                                    static_cast<uint16_t*>(d_scratch), d_status, stream);
+        const int r = decompress_chunks(d_in, in_bytes, in_offsets, counts.data(), num_chunks,
+                                        static_cast<uint16_t*>(d_scratch), d_status, stream, 0);
         if (r != ZC_OK)
             return r;
     }
@@ -2304,8 +2364,8 @@ int zc_decompress_dev(const void* d_in, size_t in_bytes, const int64_t* d_in_off
 int zc_estimate(const uint16_t* d_in, const int64_t* d_counts, int32_t num_chunks,
                 int64_t total_values, int32_t samples_per_chunk, int64_t* d_est, void* stream)
 {
-    if (num_chunks < 0 || total_values < 0 || samples_per_chunk < 1 ||
-        (num_chunks == 0 && total_values != 0))
+    if (num_chunks < 0 || num_chunks > ZC_MAX_CHUNKS || total_values < 0 ||
+        samples_per_chunk < 1 || (num_chunks == 0 && total_values != 0))
         return ZC_EINVAL;
     if (num_chunks == 0)
         return ZC_OK;
@@ -2337,49 +2397,8 @@ int zc_decompress(const void* d_in, size_t in_bytes, const int64_t* in_offsets,
                   const int64_t* counts, int32_t num_chunks, uint16_t* d_out,
                   int32_t* d_status, void* stream)
 {
-    const Counts k = check_counts(counts, num_chunks);
-    if (!k.ok)
-        return ZC_EINVAL;
-    if (num_chunks == 0)
-        return ZC_OK;
-    if (!d_in || !d_status || (k.total_values && !d_out))
-        return ZC_EINVAL;
-    if ((reinterpret_cast<uintptr_t>(d_in) & 15) || (reinterpret_cast<uintptr_t>(d_out) & 1)
-        || (reinterpret_cast<uintptr_t>(d_status) & 3))
-        return ZC_EINVAL;
-
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const uint8_t* in = static_cast<const uint8_t*>(d_in);
-    uint64_t voff = 0, slot = 0;
-    for (int32_t c0 = 0; c0 < num_chunks; c0 += kMaxChunks) {
-        ChunkTable tab;
-        std::memset(&tab, 0, sizeof tab);
-        uint32_t items = 0;
-        int32_t m = 0;
-        for (int32_t c = c0; c < num_chunks && c < c0 + kMaxChunks; ++c, ++m) {
-            const uint64_t n = static_cast<uint64_t>(counts[c]);
-            const uint64_t T = (n + kTile - 1) / kTile;
-            const int64_t off = in_offsets ? in_offsets[c] : static_cast<int64_t>(slot);
-            if (off < 0 || (off & 15) || static_cast<uint64_t>(off) + 32 > in_bytes)
-                return ZC_EINVAL;
-            tab.item_begin[m] = items;
-            tab.n[m] = static_cast<uint32_t>(n);
-            tab.voff[m] = voff;
-            tab.boff[m] = static_cast<uint64_t>(off);
-            tab.bavail[m] = in_bytes - static_cast<uint64_t>(off);
-            items += static_cast<uint32_t>(T ? T : 1);
-            voff += n;
-            slot += align256(chunk_bound(n));
-        }
-        tab.nchunks = m;
-        tab.nitems = items;
-        tab.item_begin[m] = items;
-        hipLaunchKernelGGL(zc_decompress_kernel, dim3((items + kWaves - 1) / kWaves), dim3(kBlock), 0, s, in,
-                           d_out, d_status, tab);
-        if (hipGetLastError() != hipSuccess)
-            return ZC_EHIP;
-    }
-    return ZC_OK;
+    return decompress_chunks(d_in, in_bytes, in_offsets, counts, num_chunks, d_out, d_status,
+                             stream, 0);
 }
 
 int zc_pipeline(const uint16_t* d_in, const int64_t* counts, int32_t num_chunks,
@@ -2459,8 +2478,8 @@ int zc_pipeline(const uint16_t* d_in, const int64_t* counts, int32_t num_chunks,
         if (!ok)
             return ZC_EHIP;
         // 3. decompress the group from the receiver's slots
-        r = zc_decompress(recv + soff[c0], gbytes, nullptr, counts + c0, m, d_out + voff[c0],
-                          d_status, sd);
+        r = decompress_chunks(recv + soff[c0], gbytes, nullptr, counts + c0, m, d_out + voff[c0],
+                              d_status, sd, c0);
         if (r != ZC_OK)
             return r;
     }

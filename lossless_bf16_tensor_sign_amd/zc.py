@@ -125,6 +125,27 @@ def _stream(stream):
     return ct.c_void_p(stream.cuda_stream)
 
 
+def _on(stream):
+    """Context that makes `stream` current (None: the current stream).
+
+    The allocating wrappers below allocate their buffers and read the status
+    word inside it, so the caching allocator ties every buffer to the stream
+    the kernels run on (a buffer freed on return is reused only by work
+    ordered after them) and the status read is ordered after the decode."""
+    import contextlib
+    import torch
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
+def _offsets(in_offsets, num_chunks):
+    if in_offsets is None:
+        return None, None
+    off, op = _counts(in_offsets)
+    if len(off) < int(num_chunks):
+        raise ValueError("in_offsets has %d entries for %d chunks" % (len(off), num_chunks))
+    return off, op
+
+
 # ----------------------------------------------------------- C entry points
 
 def zc_chunk_bound(n: int) -> int:
@@ -181,10 +202,7 @@ def zc_decompress(d_in, counts, d_out, d_status, in_offsets=None,
     """Queue decompression; d_status (int32 device) must hold 0."""
     a, p = _counts(counts)
     nb = d_in.numel() * d_in.element_size() if in_bytes is None else in_bytes
-    if in_offsets is not None:
-        off, op = _counts(in_offsets)
-    else:
-        off, op = None, None
+    off, op = _offsets(in_offsets, len(a))
     return int(lib().zc_decompress(_ptr(d_in), nb, op, p, len(a), _ptr(d_out),
                                    _ptr(d_status), _stream(stream)))
 
@@ -202,6 +220,8 @@ def zc_compress_dev(d_in, d_counts, total_values, d_out, d_comp_sizes, d_slot_of
 def zc_decompress_dev(d_in, d_counts, total_values, d_out, d_status, d_ws, d_in_offsets=None,
                       stream=None, in_bytes=None, ws_bytes=None) -> int:
     """Queue decompression with the counts (and offsets) in device tensors."""
+    if d_in_offsets is not None and d_in_offsets.numel() < d_counts.numel():
+        raise ValueError("d_in_offsets has fewer entries than d_counts")
     nb = d_in.numel() * d_in.element_size() if in_bytes is None else in_bytes
     wsb = d_ws.numel() * d_ws.element_size() if ws_bytes is None else ws_bytes
     return int(lib().zc_decompress_dev(_ptr(d_in), nb, _ptr(d_in_offsets), _ptr(d_counts),
@@ -215,12 +235,7 @@ def zc_decompress_reduce(d_in, n, num_chunks, d_out, d_status, d_scratch, in_off
     (rounded once to bf16 into a 16-bit d_out when bf16=True)."""
     nb = d_in.numel() * d_in.element_size() if in_bytes is None else in_bytes
     sb = d_scratch.numel() * d_scratch.element_size() if scratch_bytes is None else scratch_bytes
-    if in_offsets is not None:
-        off, op = _counts(in_offsets)
-        if len(off) < int(num_chunks):
-            raise ValueError("in_offsets has fewer entries than num_chunks")
-    else:
-        off, op = None, None
+    off, op = _offsets(in_offsets, num_chunks)
     fn = lib().zc_decompress_reduce_bf16 if bf16 else lib().zc_decompress_reduce
     return int(fn(_ptr(d_in), nb, op, int(n), int(num_chunks), _ptr(d_out), _ptr(d_status),
                   _ptr(d_scratch), sb, _stream(stream)))
@@ -261,6 +276,13 @@ def zc_switch_decide(collective, ranks, nbytes, comp_bytes, link_GBps, step_late
 
 # ------------------------------------------------ allocating conveniences
 
+def _raise_on_status(what, status):
+    st = int(status.item())
+    if st != 0:
+        raise ZcError(ZC_ECORRUPT, "%s: %s in chunk %d"
+                      % (what, REASONS.get(st >> 24, st >> 24), st & 0xFFFFFF))
+
+
 def compress(x, counts, stream=None):
     """Compress a device tensor of bf16 (or its uint16/int16 bits).
 
@@ -268,10 +290,11 @@ def compress(x, counts, stream=None):
     import torch
     a, _ = _counts(counts)
     dev = x.device
-    out = torch.empty(max(zc_bound(a), 16), dtype=torch.uint8, device=dev)
-    sizes = torch.empty(max(len(a), 1), dtype=torch.int64, device=dev)
-    ws = torch.empty(max(zc_workspace_bytes(a), 8), dtype=torch.uint8, device=dev)
-    r = zc_compress(x, a, out, sizes, ws, stream=stream)
+    with _on(stream):
+        out = torch.empty(max(zc_bound(a), 16), dtype=torch.uint8, device=dev)
+        sizes = torch.empty(max(len(a), 1), dtype=torch.int64, device=dev)
+        ws = torch.empty(max(zc_workspace_bytes(a), 8), dtype=torch.uint8, device=dev)
+        r = zc_compress(x, a, out, sizes, ws, stream=stream)
     if r != ZC_OK:
         raise ZcError(r, "zc_compress")
     return out, sizes[:len(a)]
@@ -281,17 +304,15 @@ def decompress(buf, counts, in_offsets=None, stream=None, check=True):
     """Decode streams back to a uint16 device tensor of sum(counts) values."""
     import torch
     a, _ = _counts(counts)
-    out = torch.empty(max(int(a.sum()), 1), dtype=torch.int16, device=buf.device)
-    status = torch.zeros(1, dtype=torch.int32, device=buf.device)
-    r = zc_decompress(buf, a, out, status, in_offsets=in_offsets, stream=stream)
-    if r != ZC_OK:
-        raise ZcError(r, "zc_decompress")
-    out = out[:int(a.sum())]
-    if check:
-        st = int(status.item())
-        if st != 0:
-            raise ZcError(ZC_ECORRUPT, "zc_decompress: %s in chunk %d"
-                          % (REASONS.get(st >> 24, st >> 24), st & 0xFFFFFF))
+    with _on(stream):
+        out = torch.empty(max(int(a.sum()), 1), dtype=torch.int16, device=buf.device)
+        status = torch.zeros(1, dtype=torch.int32, device=buf.device)
+        r = zc_decompress(buf, a, out, status, in_offsets=in_offsets, stream=stream)
+        if r != ZC_OK:
+            raise ZcError(r, "zc_decompress")
+        out = out[:int(a.sum())]
+        if check:
+            _raise_on_status("zc_decompress", status)
     return out, status
 
 
@@ -302,11 +323,13 @@ def compress_dev(x, d_counts, stream=None):
     import torch
     dev = x.device
     total, nc = x.numel(), d_counts.numel()
-    out = torch.empty(max(zc_bound_max(total, nc), 16), dtype=torch.uint8, device=dev)
-    sizes = torch.empty(max(nc, 1), dtype=torch.int64, device=dev)
-    slots = torch.empty(max(nc, 1), dtype=torch.int64, device=dev)
-    ws = torch.empty(max(zc_workspace_bytes_max(total, nc), 256), dtype=torch.uint8, device=dev)
-    r = zc_compress_dev(x, d_counts, total, out, sizes, slots, ws, stream=stream)
+    with _on(stream):
+        out = torch.empty(max(zc_bound_max(total, nc), 16), dtype=torch.uint8, device=dev)
+        sizes = torch.empty(max(nc, 1), dtype=torch.int64, device=dev)
+        slots = torch.empty(max(nc, 1), dtype=torch.int64, device=dev)
+        ws = torch.empty(max(zc_workspace_bytes_max(total, nc), 256), dtype=torch.uint8,
+                         device=dev)
+        r = zc_compress_dev(x, d_counts, total, out, sizes, slots, ws, stream=stream)
     if r != ZC_OK:
         raise ZcError(r, "zc_compress_dev")
     return out, sizes[:nc], slots[:nc]
@@ -317,20 +340,18 @@ def decompress_dev(buf, d_counts, total_values, d_in_offsets=None, stream=None, 
     import torch
     dev = buf.device
     nc = d_counts.numel()
-    out = torch.empty(max(int(total_values), 1), dtype=torch.int16, device=dev)
-    status = torch.zeros(1, dtype=torch.int32, device=dev)
-    ws = torch.empty(max(zc_workspace_bytes_max(total_values, nc), 256), dtype=torch.uint8,
-                     device=dev)
-    r = zc_decompress_dev(buf, d_counts, total_values, out, status, ws, d_in_offsets=d_in_offsets,
-                          stream=stream)
-    if r != ZC_OK:
-        raise ZcError(r, "zc_decompress_dev")
-    out = out[:int(total_values)]
-    if check:
-        st = int(status.item())
-        if st != 0:
-            raise ZcError(ZC_ECORRUPT, "zc_decompress_dev: %s in chunk %d"
-                          % (REASONS.get(st >> 24, st >> 24), st & 0xFFFFFF))
+    with _on(stream):
+        out = torch.empty(max(int(total_values), 1), dtype=torch.int16, device=dev)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        ws = torch.empty(max(zc_workspace_bytes_max(total_values, nc), 256), dtype=torch.uint8,
+                         device=dev)
+        r = zc_decompress_dev(buf, d_counts, total_values, out, status, ws,
+                              d_in_offsets=d_in_offsets, stream=stream)
+        if r != ZC_OK:
+            raise ZcError(r, "zc_decompress_dev")
+        out = out[:int(total_values)]
+        if check:
+            _raise_on_status("zc_decompress_dev", status)
     return out, status
 
 
@@ -341,27 +362,28 @@ def decompress_reduce(buf, n, num_chunks, in_offsets=None, stream=None, check=Tr
     when bf16=True; int32 device status)."""
     import torch
     dev = buf.device
-    out = torch.empty(max(int(n), 8), dtype=torch.int16 if bf16 else torch.float32, device=dev)
-    status = torch.zeros(1, dtype=torch.int32, device=dev)
-    scratch = torch.empty(max(2 * int(n) * int(num_chunks), 16), dtype=torch.uint8, device=dev)
-    r = zc_decompress_reduce(buf, n, num_chunks, out, status, scratch, in_offsets=in_offsets,
-                             stream=stream, bf16=bf16)
-    if r != ZC_OK:
-        raise ZcError(r, "zc_decompress_reduce")
-    out = out[:int(n)]
-    if check:
-        st = int(status.item())
-        if st != 0:
-            raise ZcError(ZC_ECORRUPT, "zc_decompress_reduce: %s in chunk %d"
-                          % (REASONS.get(st >> 24, st >> 24), st & 0xFFFFFF))
+    with _on(stream):
+        out = torch.empty(max(int(n), 8), dtype=torch.int16 if bf16 else torch.float32,
+                          device=dev)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        scratch = torch.empty(max(2 * int(n) * int(num_chunks), 16), dtype=torch.uint8,
+                              device=dev)
+        r = zc_decompress_reduce(buf, n, num_chunks, out, status, scratch,
+                                 in_offsets=in_offsets, stream=stream, bf16=bf16)
+        if r != ZC_OK:
+            raise ZcError(r, "zc_decompress_reduce")
+        out = out[:int(n)]
+        if check:
+            _raise_on_status("zc_decompress_reduce", status)
     return out, status
 
 
 def estimate(x, d_counts, samples_per_chunk=8, stream=None):
     """Estimated stream bytes per chunk (int64 device tensor)."""
     import torch
-    est = torch.empty(max(d_counts.numel(), 1), dtype=torch.int64, device=x.device)
-    r = zc_estimate(x, d_counts, x.numel(), samples_per_chunk, est, stream=stream)
+    with _on(stream):
+        est = torch.empty(max(d_counts.numel(), 1), dtype=torch.int64, device=x.device)
+        r = zc_estimate(x, d_counts, x.numel(), samples_per_chunk, est, stream=stream)
     if r != ZC_OK:
         raise ZcError(r, "zc_estimate")
     return est[:d_counts.numel()]
@@ -387,10 +409,18 @@ def pipeline(x, counts, groups, streams=None, check=True):
             s_.wait_stream(cur)
     r = zc_pipeline(x, a, groups, send, recv, sizes, y, status, ws, s_comp=sc, s_link=sl,
                     s_dec=sd)
+    # the buffers were allocated on cur but are used on the three streams:
+    # keep the allocator from reusing them (ws in particular, which is freed
+    # on return) before the work queued there has run
+    for s_, bufs in ((sc, (x, send, sizes, ws)), (sl, (send, recv, sizes)),
+                     (sd, (recv, y, status))):
+        if s_ is not None:
+            for b in bufs:
+                b.record_stream(s_)
     if r != ZC_OK:
         raise ZcError(r, "zc_pipeline")
     if check:
-        (torch.cuda.current_stream() if sd is None else sd).synchronize()
+        cur.wait_stream(cur if sd is None else sd)
         st = int(status.item())
         if st != 0:
             raise ZcError(ZC_ECORRUPT, "zc_pipeline: status %#x" % st)

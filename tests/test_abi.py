@@ -214,3 +214,28 @@ def test_pipeline_argument_errors_before_any_gpu_work():
     assert call(ws_bytes=ws - 1) == zc.ZC_ENOSPC
     # no chunks: nothing to do
     assert call(num_chunks=0, groups=1) == zc.ZC_OK
+
+
+def test_chunk_count_limit():
+    # a decoder failure names its chunk in 24 bits: more chunks are refused
+    lib = zc.lib()
+    import ctypes as ct
+    cnt = np.zeros(4, np.int64)
+    p = cnt.ctypes.data_as(ct.POINTER(ct.c_int64))
+    assert lib.zc_bound(p, (1 << 24) + 1) == 0          # rejected before counts are read
+    assert lib.zc_workspace_bytes(p, (1 << 24) + 1) == 0
+    assert lib.zc_compress(None, p, (1 << 24) + 1, None, 0, None, None, 0, None) == zc.ZC_EINVAL
+    assert lib.zc_decompress(None, 0, None, p, (1 << 24) + 1, None, None, None) == zc.ZC_EINVAL
+    assert zc.zc_bound_max(10, (1 << 24) + 1) == 0
+    assert zc.zc_bound(cnt) > 0
+
+
+def test_binding_checks_offsets_length():
+    # the binding refuses an offsets array shorter than the counts before
+    # calling the library (which would read past it)
+    import torch
+    d = torch.zeros(64, dtype=torch.uint8)
+    out = torch.zeros(8, dtype=torch.int16)
+    st = torch.zeros(1, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        zc.zc_decompress(d, [1, 1, 1], out, st, in_offsets=[0, 16])

@@ -13,6 +13,7 @@ import pytest
 import torch
 
 from lossless_bf16_tensor_sign_amd import synth, zc
+from tests import oracle_pool
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -113,17 +114,30 @@ def test_invalid_split_gives_minus_one():
 
 
 def test_estimate_full_moe_workload(oracle):
-    # The MoE all-to-all workload at full size (64 Zipf-sized chunks), 8
-    # samples per chunk: three chunks against the oracle, and the total
-    # within a few percent of the real compressed size.
+    # The MoE all-to-all workload at full size (64 Zipf-sized chunks): with 8
+    # samples per chunk every chunk's estimate equals the oracle-derived one,
+    # and the total is within a few percent of the real compressed size; with
+    # samples >= T every estimate is the exact size.
     w, cnt = synth.make(4, workers=8)
     say("estimate MoE layout: %d values" % w.size)
+    vo = oracle_pool.value_offsets(cnt)
+    per_chunk = oracle_pool.map_chunks(
+        lambda c: oracle_tile_bytes(oracle, w[vo[c]:vo[c + 1]]), len(cnt))
+
+    def expect(samples):
+        out = []
+        for X, tb in per_chunk:
+            T = tb.size
+            k = min(samples, T)
+            s = int(sum(int(tb[(i * T) // k]) for i in range(k))) if k else 0
+            out.append(X + ((s * T + k // 2) // k if k else 0))
+        return np.array(out, np.int64)
+
     got = gpu_estimate(w, cnt, 8)
-    order = np.argsort(cnt)
-    vo = np.concatenate([[0], np.cumsum(cnt)])
-    for c in sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])}):
-        want = expected(oracle, w[vo[c]:vo[c + 1]], [cnt[c]], 8)
-        assert got[c] == want[0], c
+    assert np.array_equal(got, expect(8))
+    exact = gpu_estimate(w, cnt, 1 << 20)
+    assert np.array_equal(exact, expect(1 << 20))
     _, sizes = zc.compress(torch.from_numpy(w.view(np.int16)).to(DEV), cnt)
-    real = int(sizes.sum().item())
-    assert abs(int(got.sum()) - real) / real < 0.02
+    real = sizes.cpu().numpy()
+    assert np.array_equal(exact, real)
+    assert abs(int(got.sum()) - int(real.sum())) / int(real.sum()) < 0.02

@@ -15,6 +15,7 @@ import pytest
 import torch
 
 from lossless_bf16_tensor_sign_amd import synth, zc
+from tests import oracle_pool
 
 pytestmark = pytest.mark.gpu
 
@@ -74,9 +75,10 @@ def test_many_chunks_one_group_each(oracle):
     check(oracle, w, counts, 65, three_streams())
 
 
-def test_full_fsdp_shape_sampled(oracle):
+def test_full_fsdp_shape(oracle):
     # the FSDP all-gather shard (64 x 4 Mi) in 8 groups: every value is
-    # checked by the round trip, 4 chunks' streams against the oracle
+    # checked by the round trip, and every chunk's stream in the send and in
+    # the receive buffer against the oracle
     w, counts = synth.make(2, workers=8)
     counts = np.asarray(counts, np.int64)
     x = torch.from_numpy(w.view(np.int16)).to(DEV)
@@ -87,9 +89,6 @@ def test_full_fsdp_shape_sampled(oracle):
     assert torch.equal(y, x)
     off, _ = oracle.slot_offsets(counts)
     g_sizes = sizes.cpu().numpy()
-    vo = np.concatenate([[0], np.cumsum(counts)])
-    for c in (0, 17, 40, 63):
-        ref = oracle.compress_chunk(w[vo[c]:vo[c + 1]])
-        assert g_sizes[c] == ref.size
-        got = recv[off[c]:off[c] + ref.size].cpu().numpy()
-        assert np.array_equal(got, ref), c
+    say("oracle comparison of both buffers")
+    oracle_pool.compare_chunks(oracle, w, counts, send.cpu().numpy(), g_sizes, off, label="send")
+    oracle_pool.compare_chunks(oracle, w, counts, recv.cpu().numpy(), g_sizes, off, label="recv")
