@@ -116,6 +116,32 @@ int zc_compress(const uint16_t* d_in, const int64_t* counts,
                 int64_t* d_comp_sizes, void* d_ws, size_t ws_bytes,
                 void* stream);
 
+/* Size of the library-owned workspace of zc_compress_noalloc (per GPU). */
+#define ZC_NOALLOC_WORKSPACE_BYTES ((size_t)4 << 20)
+
+/*
+ * zc_compress for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It takes no workspace: the look-back status words live in a library-owned
+ * device array of ZC_NOALLOC_WORKSPACE_BYTES, one per GPU, held from the first
+ * call on that GPU until the process ends.  The call itself allocates
+ * nothing (no hipMalloc, no allocating library routine); the caller still
+ * owns d_in, d_out and d_comp_sizes.
+ *   arguments     as zc_compress, without d_ws / ws_bytes; the current device
+ *                 must be the one the buffers and the stream belong to
+ * Limit: zc_workspace_bytes(counts, num_chunks) <= ZC_NOALLOC_WORKSPACE_BYTES
+ * (about 65 000 tiles of 8192 values per launch of up to 64 chunks, i.e.
+ * about 535 M values), else ZC_ENOSPC before anything is queued.
+ * Every call on one GPU shares that GPU's array and starts by clearing the
+ * part it uses, so calls on one GPU must not overlap in time: calls on
+ * different streams of one GPU race unless the caller orders them.
+ * Returns as zc_compress; ZC_EHIP also if the array's device address cannot
+ * be found.  The output is byte-identical to zc_compress's.
+ */
+int zc_compress_noalloc(const uint16_t* d_in, const int64_t* counts,
+                        int32_t num_chunks, void* d_out, size_t out_capacity,
+                        int64_t* d_comp_sizes, void* stream);
+
 /*
  * Decompress num_chunks ZCB1 streams back to bf16: the inverse of
  * zc_compress, run after the collective has delivered the streams (ZipCCL

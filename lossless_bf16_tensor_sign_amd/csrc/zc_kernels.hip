@@ -2038,6 +2038,31 @@ constexpr size_t kWsHeader = kMaxChunks * kTicketStride * 4;   // per-chunk tick
 
 namespace {
 
+// ---- compress without a caller workspace
+
+// The workspace of zc_compress_noalloc: one copy per GPU, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not device
+// memory: kernels and copies get the per-device address that
+// hipGetSymbolAddress returns (noalloc_scratch below), never the name.
+constexpr size_t kNoallocBytes = ZC_NOALLOC_WORKSPACE_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoallocBytes];
+
+constexpr int kMaxDevices = 64;
+
+// The device address of this GPU's scratch array, looked up once per device
+// with that device current; nullptr if the lookup failed.
+void* noalloc_scratch(int device)
+{
+    static std::once_flag once[kMaxDevices];
+    static void* ptr[kMaxDevices];
+    std::call_once(once[device], [device] {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess)
+            ptr[device] = p;
+    });
+    return ptr[device];
+}
+
 // ---- device-resident split: bounds and workspace layout
 
 // Tiles of one launch of m chunks holding at most `total` values:
@@ -2258,6 +2283,29 @@ int zc_compress(const uint16_t* d_in, const int64_t* counts, int32_t num_chunks,
             return ZC_EHIP;
     }
     return ZC_OK;
+}
+
+int zc_compress_noalloc(const uint16_t* d_in, const int64_t* counts, int32_t num_chunks,
+                        void* d_out, size_t out_capacity, int64_t* d_comp_sizes, void* stream)
+{
+    const Counts k = check_counts(counts, num_chunks);
+    if (!k.ok)
+        return ZC_EINVAL;
+    if (num_chunks == 0)
+        return ZC_OK;
+    const size_t need = zc_workspace_bytes(counts, num_chunks);
+    if (need > kNoallocBytes)
+        return ZC_ENOSPC;
+    int device = -1;
+    if (hipGetDevice(&device) != hipSuccess || device < 0 || device >= kMaxDevices)
+        return ZC_EHIP;
+    void* ws = noalloc_scratch(device);     // this device's array, current device set
+    if (!ws)
+        return ZC_EHIP;
+    // the same launches as zc_compress; its clear kernel zeroes the status
+    // words this call uses (they hold the previous call's values)
+    return zc_compress(d_in, counts, num_chunks, d_out, out_capacity, d_comp_sizes, ws,
+                       kNoallocBytes, stream);
 }
 
 size_t zc_bound_max(int64_t total_values, int32_t num_chunks)

@@ -66,6 +66,9 @@ def lib():
                                   ct.c_size_t, ct.c_void_p, ct.c_void_p,
                                   ct.c_size_t, ct.c_void_p]
         L.zc_compress.restype = ct.c_int
+        L.zc_compress_noalloc.argtypes = [ct.c_void_p, i64p, ct.c_int32, ct.c_void_p,
+                                          ct.c_size_t, ct.c_void_p, ct.c_void_p]
+        L.zc_compress_noalloc.restype = ct.c_int
         L.zc_decompress.argtypes = [ct.c_void_p, ct.c_size_t, i64p, i64p,
                                     ct.c_int32, ct.c_void_p, ct.c_void_p,
                                     ct.c_void_p]
@@ -195,6 +198,16 @@ def zc_compress(d_in, counts, d_out, d_comp_sizes, d_ws, stream=None,
     return int(lib().zc_compress(_ptr(d_in), p, len(a), _ptr(d_out), cap,
                                  _ptr(d_comp_sizes), _ptr(d_ws), wsb,
                                  _stream(stream)))
+
+
+def zc_compress_noalloc(d_in, counts, d_out, d_comp_sizes, stream=None,
+                        out_capacity=None) -> int:
+    """Queue compression with the library's own per-GPU workspace (no
+    workspace argument; nothing is allocated)."""
+    a, p = _counts(counts)
+    cap = d_out.numel() * d_out.element_size() if out_capacity is None else out_capacity
+    return int(lib().zc_compress_noalloc(_ptr(d_in), p, len(a), _ptr(d_out), cap,
+                                         _ptr(d_comp_sizes), _stream(stream)))
 
 
 def zc_decompress(d_in, counts, d_out, d_status, in_offsets=None,
