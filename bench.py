@@ -190,7 +190,7 @@ def time_pipeline(args, x, counts, dev, evict, ev):
     send = torch.empty(cap, dtype=torch.uint8, device=dev)
     recv = torch.empty(cap, dtype=torch.uint8, device=dev)
     sizes = torch.empty(len(counts), dtype=torch.int64, device=dev)
-    ws = torch.empty(zc.zc_workspace_bytes(counts), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(zc.zc_workspace_bytes(counts), dtype=torch.uint8, device=dev)
     y = torch.empty_like(x)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     cur = torch.cuda.current_stream()
@@ -280,7 +280,7 @@ def main():
     sizes = torch.empty(len(counts), dtype=torch.int64, device=dev)
     slots = torch.empty(len(counts), dtype=torch.int64, device=dev)
     dcounts = torch.from_numpy(np.asarray(counts, np.int64)).to(dev)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
     y = torch.empty(n, dtype=torch.int16, device=dev)
     red = torch.empty(shard if args.reduce else 4, dtype=torch.float32, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)

@@ -81,10 +81,20 @@ size_t zc_chunk_bound(int64_t n);
 size_t zc_bound(const int64_t* counts, int32_t num_chunks);
 
 /*
- * Device workspace bytes that zc_compress needs for these counts: one
- * look-back status word per tile of the largest launch (a launch takes up
- * to 64 chunks), after a fixed header.  Sizing only, no passage of the pages
- * behind it.  Host only; 0 if an argument is invalid.
+ * Device workspace bytes that zc_compress needs for these counts: a fixed
+ * header (the last launch's tag and 64 counters of finished workgroups) and
+ * one look-back status word per tile of the largest launch (a launch takes
+ * up to 64 chunks).  Sizing only, no passage of the pages behind it.  Host
+ * only; 0 if an argument is invalid.
+ *
+ * A workspace must hold zeros before the first call that uses it (a
+ * one-time initialisation, e.g. at allocation); every call leaves it ready
+ * for the next.  Each launch tags the status words it writes with a number
+ * one above the tag stored in the header, and its last workgroup stores that
+ * tag once every other workgroup has finished, so no call has to clear the
+ * words of an earlier one (graph replays included).  When the tag wraps
+ * (after 2^32 - 1 launches on one workspace) that launch clears every status
+ * word first.
  */
 size_t zc_workspace_bytes(const int64_t* counts, int32_t num_chunks);
 
@@ -99,8 +109,8 @@ size_t zc_workspace_bytes(const int64_t* counts, int32_t num_chunks);
  *                 stream's end inside its slot are left unwritten
  *   d_comp_sizes  device int64[num_chunks]: comp_bytes of each stream
  *   d_ws          device workspace of ws_bytes >= zc_workspace_bytes(...),
- *                 8-byte aligned (its status words are 64-bit atomics); its
- *                 contents need not be initialised
+ *                 8-byte aligned (its status words are 64-bit atomics),
+ *                 zero-filled before its first use (see zc_workspace_bytes)
  *   stream        hipStream_t the work is queued on
  * Returns ZC_OK once the work is queued, or an error before anything is
  * queued (ZC_EINVAL, ZC_ENOSPC) or when a launch fails (ZC_EHIP).  Calls that
@@ -223,7 +233,7 @@ size_t zc_workspace_bytes_max(int64_t total_values, int32_t num_chunks);
  *                 c's stream in d_out (the slot layout of those counts)
  *   d_out         out_capacity >= zc_bound_max(total_values, num_chunks)
  *   d_ws          256-byte aligned, ws_bytes >= zc_workspace_bytes_max(...),
- *                 contents need not be initialised
+ *                 zero-filled before its first use, as for zc_compress
  *   other arguments as zc_compress.
  * The counts are checked on the device.  If they are out of range or do not
  * sum to total_values, nothing is compressed and every d_comp_sizes and

@@ -50,75 +50,6 @@
 #include "zc_table.h"
 #include "zc_table_v1.inc"
 
-// Tuning knobs (compile-time; the defaults are the measured best).
-#ifndef ZC_ENC_WAVES
-#define ZC_ENC_WAVES 8           // compress occupancy target, waves per SIMD
-#endif
-#ifndef ZC_ENC_INTERLEAVE
-#define ZC_ENC_INTERLEAVE 0      // equal-size chunks: hand out tiles round-robin (else chunk by chunk)
-#endif
-#ifndef ZC_EARLY_LOAD
-#define ZC_EARLY_LOAD 1          // grid-ordered full tiles: loads issued before the table set-up
-#endif
-#ifndef ZC_ENC_TICKETS
-#define ZC_ENC_TICKETS 0         // round-robin tiles numbered by per-chunk tickets (else by grid position)
-#endif
-#ifndef ZC_STATUS_STRIDE
-#define ZC_STATUS_STRIDE 8       // 8-byte look-back status words, one per this many
-#endif
-#ifndef ZC_POLL_LANES
-#define ZC_POLL_LANES 16         // predecessors read per look-back poll
-#endif
-#ifndef ZC_EARLY_POLL
-#define ZC_EARLY_POLL 0          // first look-back poll issued before emission
-#endif
-#ifndef ZC_STORE_X4
-#define ZC_STORE_X4 0            // tile streams stored with 16-byte stores
-#endif
-#ifndef ZC_MIXED_PAIR
-#define ZC_MIXED_PAIR 1          // waves with raw groups may also emit pairs
-#endif
-#ifndef ZC_ENC_TILE_WAVES
-#define ZC_ENC_TILE_WAVES 4      // compress: waves that share one tile (2 or 4)
-#endif
-#ifndef ZC_ENC_REEXTRACT
-#define ZC_ENC_REEXTRACT 0       // compress: emission extracts d from the packed words again
-#endif
-#ifndef ZC_LATE_PUBLISH
-#define ZC_LATE_PUBLISH 1        // compress: inclusive prefix published after the tile's stores
-#endif
-#ifndef ZC_ENC_PAIRS
-#define ZC_ENC_PAIRS 2           // compress: full tiles emit member pairs from one table entry
-                                 // (0 never, 1 in waves with raw groups, 2 always)
-#endif
-#ifndef ZC_RAW_NT
-#define ZC_RAW_NT 0              // compress: raw bytes stored with the nontemporal hint
-#endif
-#ifndef ZC_STREAM_NT
-#define ZC_STREAM_NT 0           // compress: tile streams stored with the nontemporal hint
-#endif
-#ifndef ZC_DEC_OUT_NT
-#define ZC_DEC_OUT_NT 1          // decompress: values stored with the nontemporal hint
-#endif
-#ifndef ZC_ENC_LOAD_NT
-#define ZC_ENC_LOAD_NT 1         // compress: input loads with the nontemporal hint
-#endif
-#ifndef ZC_DEC_LOAD_NT
-#define ZC_DEC_LOAD_NT 1         // decompress: stream and raw-byte loads with the nontemporal hint
-#endif
-#ifndef ZC_ENC_BATCH
-#define ZC_ENC_BATCH 0           // compress: a step's table lookups issued together (1 pairs, 2 escapes)
-#endif
-#ifndef ZC_DEC_RING
-#define ZC_DEC_RING 1            // decompress: steps of sign+mantissa bytes prefetched ahead
-#endif
-#ifndef ZC_DEC_WAVES
-#define ZC_DEC_WAVES 8           // decompress occupancy target, waves per SIMD
-#endif
-#ifndef ZC_ESC_PAIRS
-#define ZC_ESC_PAIRS 1           // compress: escape steps of coded-only waves emit two members per OR
-#endif
-
 namespace {
 
 constexpr int kLanes = 64;
@@ -128,8 +59,8 @@ constexpr int kSteps = 16;
 constexpr int kTile = 8192;
 constexpr int kStageWords = 1024;                 // LDS tile-stream buffer per wave (4 KiB)
 constexpr int kStageAlloc = kStageWords + 8;      // + guard and carry words
-constexpr int kMinWavesEnc = ZC_ENC_WAVES;        // occupancy targets, waves per SIMD
-constexpr int kMinWavesDec = ZC_DEC_WAVES;
+constexpr int kMinWavesEnc = 8;                   // occupancy targets, waves per SIMD
+constexpr int kMinWavesDec = 8;
 constexpr int kMaxChunks = 64;                     // chunks per launch
 constexpr uint32_t kMagic = 0x3142435Au;
 constexpr uint32_t kVerTable = 0x00010001u;        // version 1, table_id 1
@@ -138,14 +69,27 @@ constexpr int kEscLen = ZC_T1_ESC_LEN;
 constexpr int kLutBits = ZC_T1_LUT_BITS;          // first decode level (byte entries)
 constexpr int kTailBits = ZC_T1_TAIL_BITS;        // second level
 constexpr int kLutRaw = 1 << kLutBits;            // raw-mode byte entries follow
-constexpr uint32_t kTicketStride = 32;             // one 128-byte line per chunk counter
 constexpr uint32_t kSpinLimit = 1u << 14;          // look-back polls before recomputing
-// Look-back status words sit one per 64-byte line: a tile's status is
-// written through to device-coherent memory, and tiles sharing a line would
-// serialize those writes.
-constexpr uint32_t kStatusStride = ZC_STATUS_STRIDE;
-constexpr uint64_t kFlagAgg = 1ull << 62;
-constexpr uint64_t kFlagInc = 2ull << 62;
+constexpr uint32_t kPollLanes = 16;                // predecessors read per look-back poll
+
+// Compress workspace: a header, then one 8-byte look-back status word per
+// tile, one per 64-byte line (a tile's status is written through to
+// device-coherent memory, and tiles sharing a line would serialize those
+// writes).  Header: the last launch's tag (epoch, u32) at byte 0, then 64
+// counters of finished workgroups, one u32 per 128-byte line from byte 128.
+constexpr uint32_t kCounters = 64;
+constexpr uint32_t kCounterStride = 32;            // u32 index step between counters
+constexpr uint32_t kHdrEpoch = 0;                  // u32 index
+constexpr uint32_t kHdrCounters = 32;              // u32 index (byte 128)
+constexpr size_t kWsHeader = 128 + kCounters * 128 + 128;   // 8448 bytes
+constexpr uint32_t kDoneSpinLimit = 1u << 22;      // polls of the last workgroup
+constexpr uint32_t kStatusStride = 8;              // u64 index step between status words
+// A status word: the launch's tag (epoch) in bits 32-63, the flag in bits
+// 30-31 (1 = the tile's own size is known, 2 = its inclusive prefix is),
+// the value in 32-bit words in bits 0-29.  Words with another launch's tag
+// read as "not yet published", so no launch has to clear them first.
+constexpr uint32_t kFlagAgg = 1;
+constexpr uint32_t kFlagInc = 2;
 
 static_assert(ZC_T1_NSYM == 17, "table_id 1 has 17 symbols");
 static_assert(ZC_T1_TAIL_OK == 1, "long code words must share the all-ones prefix");
@@ -182,29 +126,12 @@ __device__ inline uint32_t tail_of(uint32_t i)
     return v;
 }
 
-// Compress tile orders.  Tickets: workgroups take the chunks round-robin and
-// number their tiles from per-chunk counters.  Chunks: grid position = tile
-// index, chunk by chunk.  RoundRobin: grid position g is tile g / C of chunk
-// g mod C (every chunk has the same number of tiles).
-constexpr uint32_t kOrderTickets = 0;
-constexpr uint32_t kOrderChunks = 1;
-constexpr uint32_t kOrderRoundRobin = 2;
-
-__host__ __device__ inline uint32_t tile_order(uint32_t uniform_tiles)
-{
-    if (!ZC_ENC_INTERLEAVE || !uniform_tiles)
-        return kOrderChunks;
-    return ZC_ENC_TICKETS ? kOrderTickets : kOrderRoundRobin;
-}
-
 // Chunks of one launch.  Work item = one tile; an empty chunk gets one item
 // that only writes its header.
 struct ChunkTable {
     int32_t nchunks;
     int32_t chunk_base;            // index of the launch's first chunk in the call (status reports)
     uint32_t nitems;
-    uint32_t uniform_tiles;        // > 0: every chunk has this many tiles
-    uint32_t grid_order;           // compress tile order: kOrderTickets, kOrderChunks or kOrderRoundRobin
     uint32_t spin_limit;           // compress: look-back polls before recomputing
     uint32_t item_begin[kMaxChunks + 1];
     uint32_t n[kMaxChunks];
@@ -257,6 +184,24 @@ __device__ inline uint32_t wave_excl_scan(uint32_t x, uint32_t lane, uint32_t* t
     }
     *total = __shfl(incl, kLanes - 1);
     return incl - x;
+}
+
+// Inclusive prefix sum over the wave with DPP row operations (no LDS round
+// trip, no per-lane address): shifts by 1, 2, 4 and 8 lanes inside each row
+// of 16 (out-of-row sources read 0), then row 0's last lane is added to row 1
+// and row 2's to row 3, then lane 31 to rows 2 and 3.  Returns the exclusive
+// prefix; *total is lane 63's sum, read into a scalar register.
+__device__ inline uint32_t wave_excl_scan_dpp(uint32_t x, uint32_t* total)
+{
+    int v = static_cast<int>(x);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    *total = static_cast<uint32_t>(__builtin_amdgcn_readlane(v, kLanes - 1));
+    return static_cast<uint32_t>(v) - x;
 }
 
 __device__ inline uint32_t wave_sum(uint32_t x)
@@ -339,20 +284,6 @@ __device__ inline void st_nt1(uint32_t* p, uint32_t v) { __builtin_nontemporal_s
 
 // ------------------------------------------------------------ compress
 
-// Zeroes the ticket counters and the first word of each status slot.
-__global__ void zc_clear_kernel(uint32_t* __restrict__ tickets, uint32_t ticket_words,
-                                uint64_t* __restrict__ status, uint32_t items)
-{
-    for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < ticket_words + items;
-         i += gridDim.x * blockDim.x) {
-        if (i < ticket_words)
-            tickets[i] = 0;
-        else
-            status[static_cast<size_t>(i - ticket_words) * kStatusStride] = 0;
-    }
-}
-
-
 // Indexed by d = E_max - e (0..255).  esc[d] = code word | length << 24,
 // with bit 31 set and the code word shifted left by 8 for an escape (d >= 16),
 // whose 8 exponent bits follow it.
@@ -388,15 +319,14 @@ __host__ __device__ constexpr EncTables make_enc_tables()
 }
 __constant__ EncTables c_enc = make_enc_tables();
 
-// A tile is compressed by one workgroup of four waves.  Lane l of every wave
-// works on group l; wave w takes steps 4w..4w+3 of it, which are members
+// A tile is compressed by the four waves of a workgroup.  Lane l of every
+// wave works on group l; wave w takes steps 4w..4w+3 of it, which are members
 // 32w..32w+31 in the group's order.  The four partial maxima and partial code
 // lengths of a group meet in LDS, so each thread knows where its quarter of
 // the group's stream starts; the four waves then write their code words into
 // one LDS copy of the tile stream, and wave 0 places it in the chunk.
-constexpr int kEncWaves = ZC_ENC_TILE_WAVES;       // waves per compress workgroup (one tile)
+constexpr int kEncWaves = 4;                       // waves per compress workgroup
 constexpr int kEncBlock = kLanes * kEncWaves;
-static_assert(kEncWaves == 2 || kEncWaves == 4, "a tile is shared by 2 or 4 waves");
 constexpr int kQSteps = kSteps / kEncWaves;        // steps per wave
 constexpr int kQMembers = kQSteps * 8;             // members per wave and group
 constexpr int kTileWordsMax = kTile / 4;           // an all-raw tile stream
@@ -404,13 +334,12 @@ constexpr int kEncStage = kTileWordsMax + 8;       // + guard words
 
 struct EncShared {
     EncTables tb;
-    uint32_t stage[kEncStage];
+    uint32_t stage[kEncStage];              // the tile stream being built (zero between tiles)
     uint16_t part_max[kEncWaves][kLanes];   // at most 255
     uint16_t part_bits[kEncWaves][kLanes];  // at most 64 * 22
-    uint32_t tile;
-    uint32_t spin_limit;
 };
 
+// One tile of a launch: its chunk, place and geometry (all uniform).
 struct TileCtx {
     const uint16_t* src;
     uint8_t* dst;
@@ -419,23 +348,45 @@ struct TileCtx {
     int c;
 };
 
-// A wave loads its steps of the tile in batches of at most four (16 bytes
-// per lane each), which bounds the registers that hold loaded values.
-constexpr int kLoadBatch = kQSteps < 4 ? kQSteps : 4;
-constexpr int kBatches = kQSteps / kLoadBatch;
-
-// Loads batch `b` of this wave's steps (FULL = 8192 values at a 16-byte
-// aligned address; otherwise missing members read as 0).
-template <bool FULL>
-__device__ inline void load_tile(const TileCtx& x, uint4 (&v)[kLoadBatch], int b)
+__device__ inline TileCtx tile_ctx(const ChunkTable& tab, uint32_t item,
+                                   const uint16_t* __restrict__ in, uint8_t* __restrict__ out,
+                                   uint32_t lane, uint32_t wave)
 {
-    const uint32_t k0 = x.wave * kQSteps + b * kLoadBatch;
+    TileCtx x;
+    x.c = find_chunk(tab, item);
+    x.n = tab.n[x.c];
+    x.first = tab.item_begin[x.c];
+    x.item = item;
+    x.t = item - x.first;
+    x.base = x.t * kTile;
+    x.rem = x.n ? min(x.n - x.base, static_cast<uint32_t>(kTile)) : 0u;
+    x.src = in + tab.voff[x.c];
+    x.dst = out + tab.boff[x.c];
+    x.G = geometry(x.n);
+    x.lane = lane;
+    x.wave = wave;
+    return x;
+}
+
+// A whole tile of 8192 values at a 16-byte aligned address takes the vector
+// path (tile starts are 16 KiB apart inside a chunk).
+__device__ inline bool tile_full(const TileCtx& x)
+{
+    return x.rem == kTile && (reinterpret_cast<uintptr_t>(x.src) & 15) == 0;
+}
+
+// Loads this wave's four steps of the tile (16 bytes per lane each; FULL =
+// 8192 values at a 16-byte aligned address; otherwise missing members read
+// as 0).
+template <bool FULL>
+__device__ inline void load_tile(const TileCtx& x, uint4 (&v)[kQSteps])
+{
+    const uint32_t k0 = x.wave * kQSteps;
     const char* sbase = reinterpret_cast<const char*>(x.src + x.base) + k0 * 1024 + x.lane * 16;
 #pragma unroll
-    for (int k = 0; k < kLoadBatch; ++k) {
+    for (int k = 0; k < kQSteps; ++k) {
         if (FULL) {
-            v[k] = ZC_ENC_LOAD_NT ? ld_nt4(sbase + k * 1024)
-                                  : *reinterpret_cast<const uint4*>(sbase + k * 1024);
+            v[k] = ld_nt4(sbase + k * 1024);
         } else {
             // a segment of 8 values wholly inside the chunk at a 16-byte
             // aligned address is one load; the ragged end value by value
@@ -456,19 +407,18 @@ __device__ inline void load_tile(const TileCtx& x, uint4 (&v)[kLoadBatch], int b
     }
 }
 
-// Splits loaded batch `b`: raw bytes are stored at once, exponents stay
+// Splits the loaded steps: raw bytes are stored at once, exponents stay
 // packed 4 per word, the maximum exponent is returned.
 template <bool FULL>
-__device__ inline uint32_t split_tile(const TileCtx& x, const uint4 (&v)[kLoadBatch],
-                                      uint32_t (&ex)[kQSteps][2], int b)
+__device__ inline uint32_t split_tile(const TileCtx& x, const uint4 (&v)[kQSteps],
+                                      uint32_t (&ex)[kQSteps][2])
 {
-    const uint32_t k0 = x.wave * kQSteps + b * kLoadBatch;
+    const uint32_t k0 = x.wave * kQSteps;
     char* rbase = reinterpret_cast<char*>(x.dst + x.G.R + x.base) + k0 * 512 + x.lane * 8;
     uint32_t mx = 0;
 #pragma unroll
-    for (int kb = 0; kb < kLoadBatch; ++kb) {
-        const int k = b * kLoadBatch + kb;
-        const uint4 q = v[kb];
+    for (int k = 0; k < kQSteps; ++k) {
+        const uint4 q = v[k];
         const uint32_t lo_a = __builtin_amdgcn_perm(q.y, q.x, 0x06040200u);
         const uint32_t hi_a = __builtin_amdgcn_perm(q.y, q.x, 0x07050301u);
         const uint32_t lo_b = __builtin_amdgcn_perm(q.w, q.z, 0x06040200u);
@@ -482,12 +432,9 @@ __device__ inline uint32_t split_tile(const TileCtx& x, const uint4 (&v)[kLoadBa
         mx = max(mx, max(max(q.z & 0x7F80u, (q.z >> 16) & 0x7F80u),
                          max(q.w & 0x7F80u, (q.w >> 16) & 0x7F80u)));
         if (FULL) {
-            if (ZC_RAW_NT)
-                st_nt2(rbase + kb * 512, make_uint2(raw_a, raw_b));
-            else
-                *reinterpret_cast<uint2*>(rbase + kb * 512) = make_uint2(raw_a, raw_b);
+            *reinterpret_cast<uint2*>(rbase + k * 512) = make_uint2(raw_a, raw_b);
         } else {
-            const uint32_t i0 = x.base + (k0 + kb) * 512 + x.lane * 8;
+            const uint32_t i0 = x.base + (k0 + k) * 512 + x.lane * 8;
             uint8_t* rdst = x.dst + x.G.R + i0;      // 8-byte aligned (R and i0 are)
             if (i0 + 8 <= x.n) {
                 st_nt2(rdst, make_uint2(raw_a, raw_b));
@@ -502,50 +449,54 @@ __device__ inline uint32_t split_tile(const TileCtx& x, const uint4 (&v)[kLoadBa
     return mx >> 7;   // missing members were loaded as 0
 }
 
-template <bool FULL>
-__device__ inline uint32_t load_split(const TileCtx& x, uint32_t (&ex)[kQSteps][2])
+// Decoupled look-back over per-tile status words (see kFlagAgg / kFlagInc).
+// Publishing comes first; the exclusive offset is resolved later, so the
+// caller can do other work while predecessors finish.  Sizes and prefixes
+// are in 32-bit words (tile streams are whole words).
+
+__device__ inline uint64_t status_word(uint32_t epoch, uint32_t flag, uint32_t words)
 {
-    uint32_t mx = 0;
-#pragma unroll
-    for (int b = 0; b < kBatches; ++b) {
-        uint4 v[kLoadBatch];
-        load_tile<FULL>(x, v, b);
-        mx = max(mx, split_tile<FULL>(x, v, ex, b));
-    }
-    return mx;
+    return (static_cast<uint64_t>(epoch) << 32) | (flag << 30) | words;
 }
 
-// Decoupled look-back over per-tile status words (flag in bits 62-63:
-// 1 = the tile's own byte count is known, 2 = its inclusive prefix is).
-// Publishing comes first; the exclusive offset is resolved later, so the
-// caller can do other work while predecessors finish.
+// A polled status word as (flag << 62) | words, or 0 if it does not carry
+// this launch's tag (written by an earlier launch, or never).
+__device__ inline uint64_t status_norm(uint64_t s, uint32_t epoch)
+{
+    return hi32(s) == epoch
+               ? (static_cast<uint64_t>(lo32(s) >> 30) << 62) | (lo32(s) & 0x3FFFFFFFu)
+               : 0ull;
+}
+
 __device__ inline void look_back_publish(uint64_t* __restrict__ status, uint32_t item, uint32_t t,
-                                         uint32_t tile_bytes, uint32_t lane)
+                                         uint32_t tile_words, uint32_t lane, uint32_t epoch)
 {
     if (lane == 0)
-        __hip_atomic_store(&status[item * kStatusStride], (t == 0 ? kFlagInc : kFlagAgg) | tile_bytes,
+        __hip_atomic_store(&status[item * kStatusStride],
+                           status_word(epoch, t == 0 ? kFlagInc : kFlagAgg, tile_words),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One poll of the look-back window: the status words of the 64 tiles below
+// One poll of the look-back window: the status words of the 16 tiles below
 // `top` (lane l reads tile top - l), zero where they belong to no
 // predecessor.
 __device__ inline uint64_t look_back_poll(const uint64_t* __restrict__ status, int64_t top,
-                                          uint32_t first, uint32_t lane)
+                                          uint32_t first, uint32_t lane, uint32_t epoch)
 {
     const int64_t idx = top - static_cast<int64_t>(lane);
     uint64_t s = 0;
-    if (lane < ZC_POLL_LANES && idx >= static_cast<int64_t>(first))
-        s = __hip_atomic_load(&status[idx * kStatusStride], __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_AGENT);
+    if (lane < kPollLanes && idx >= static_cast<int64_t>(first))
+        s = status_norm(__hip_atomic_load(&status[idx * kStatusStride], __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT), epoch);
     return s;
 }
 
-// The byte count of tile `t` of a chunk (`src`, `n` values) recomputed from
-// its input: the encoder's group maxima, code lengths and mode, one group
-// per lane.  The look-back falls back on it for a predecessor that has not
-// published within the spin limit, so that no wait is unbounded.
-__device__ inline uint32_t tile_bytes_from_input(
+// The size in words of tile `t`'s stream for a chunk (`src`, `n` values),
+// recomputed from its input: the encoder's group maxima, code lengths and
+// mode, one group per lane.  The look-back falls back on it for a
+// predecessor that has not published within the spin limit, so that no wait
+// is unbounded.
+__device__ inline uint32_t tile_words_from_input(
     const uint16_t* __restrict__ src, uint32_t n, uint32_t t, uint32_t lane,
     const uint8_t* __restrict__ len)
 {
@@ -568,31 +519,30 @@ __device__ inline uint32_t tile_bytes_from_input(
                 bits += len[emax - ((static_cast<uint32_t>(src[i]) >> 7) & 0xFF)];
         }
     const uint32_t glen = (ng > 0 && bits >= 8 * ng) ? 8 * ng : bits;
-    return ((wave_sum(glen) + 31) >> 5) * 4;
+    return (wave_sum(glen) + 31) >> 5;
 }
 
-// The exclusive byte offset of tile `t`: sums predecessors' sizes down to
-// the nearest one whose inclusive prefix is known, then publishes this
-// tile's inclusive prefix.  `s` is the first poll (of the window below the
-// tile), issued earlier by the caller so that its latency overlaps work.
-// After `spin_limit` polls that still miss a predecessor, the missing sizes
-// are recomputed from the input instead (the chunk is `src`, `n` values).
-__device__ inline uint32_t look_back_resolve(uint64_t* __restrict__ status, uint32_t item,
-                                             uint32_t t, uint32_t first, uint32_t tile_bytes,
-                                             uint32_t lane, uint64_t s,
-                                             const uint16_t* __restrict__ src, uint32_t n,
-                                             const uint8_t* __restrict__ len, uint32_t spin_limit)
+// The exclusive word offset of tile `t`: sums predecessors' sizes down to
+// the nearest one whose inclusive prefix is known.  After `spin_limit` polls
+// that still miss a predecessor, the missing sizes are recomputed from the
+// input instead (the chunk is `src`, `n` values).
+__device__ inline uint32_t look_back_resolve(const uint64_t* __restrict__ status, uint32_t item,
+                                             uint32_t t, uint32_t first, uint32_t lane,
+                                             uint32_t epoch, const uint16_t* __restrict__ src,
+                                             uint32_t n, const uint8_t* __restrict__ len,
+                                             uint32_t spin_limit)
 {
     if (t == 0)
         return 0;
     int64_t top = static_cast<int64_t>(item) - 1;
+    uint64_t s = look_back_poll(status, top, first, lane, epoch);
     uint32_t acc = 0;
     uint32_t spins = 0;
     while (true) {
-        const bool in_range = lane < ZC_POLL_LANES &&
+        const bool in_range = lane < kPollLanes &&
                               top - static_cast<int64_t>(lane) >= static_cast<int64_t>(first);
         const uint32_t flag = static_cast<uint32_t>(s >> 62);
-        const uint64_t inc_mask = __ballot(in_range && flag == 2);
+        const uint64_t inc_mask = __ballot(in_range && flag == kFlagInc);
         const uint64_t zero_mask = __ballot(in_range && flag == 0);
         if (inc_mask) {
             const int p = __ffsll(static_cast<unsigned long long>(inc_mask)) - 1;
@@ -603,15 +553,15 @@ __device__ inline uint32_t look_back_resolve(uint64_t* __restrict__ status, uint
             }
         } else if (zero_mask == 0) {
             acc += wave_sum(static_cast<uint32_t>(s));
-            top -= ZC_POLL_LANES;
-            s = look_back_poll(status, top, first, lane);
+            top -= kPollLanes;
+            s = look_back_poll(status, top, first, lane, epoch);
             continue;
         }
         if (spins < spin_limit) {
             // a predecessor has not published yet: poll the same window again
             ++spins;
             __builtin_amdgcn_s_sleep(1);
-            s = look_back_poll(status, top, first, lane);
+            s = look_back_poll(status, top, first, lane, epoch);
             continue;
         }
         // waited too long: recompute the missing sizes (the chunk's first
@@ -619,27 +569,47 @@ __device__ inline uint32_t look_back_resolve(uint64_t* __restrict__ status, uint
         for (uint64_t miss = zero_mask; miss; miss &= miss - 1) {
             const int i = __ffsll(static_cast<unsigned long long>(miss)) - 1;
             const uint32_t p = static_cast<uint32_t>(top - i);
-            const uint32_t bytes = tile_bytes_from_input(src, n, p - first, lane, len);
+            const uint32_t words = tile_words_from_input(src, n, p - first, lane, len);
             if (lane == static_cast<uint32_t>(i))
-                s = (p == first ? kFlagInc : kFlagAgg) | bytes;
+                s = (static_cast<uint64_t>(p == first ? kFlagInc : kFlagAgg) << 62) | words;
         }
     }
-    if (!ZC_LATE_PUBLISH && lane == 0)
-        __hip_atomic_store(&status[item * kStatusStride], kFlagInc | (acc + tile_bytes),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return acc;
+}
+
+// Appends code words to a thread's stream accumulator: `acc` holds the
+// stream's pending bits (nacc of them, fewer than 32, at the bottom), and
+// each whole 32-bit word is ORed into the LDS tile stream at word wi.  One
+// call appends `len` <= 32 bits of `code`.
+__device__ __forceinline__ void emit_bits(uint32_t* __restrict__ s, uint64_t& acc, uint32_t& nacc,
+                                          uint32_t& wi, uint32_t code, uint32_t len)
+{
+    acc = (acc << len) | code;
+    nacc += len;
+    const uint32_t wv = __builtin_amdgcn_alignbit(hi32(acc), lo32(acc), nacc);
+    const uint32_t f = nacc >> 5;
+    atomicOr(&s[wi], f ? wv : 0u);
+    wi += f;
+    nacc &= 31;
 }
 
 // Appends this thread's members of its group to the LDS tile stream from bit
 // `off`: one code word per value, or for a raw group (MIXED waves only) the
-// exponents as 8-bit words.  `first` is the group member index of the
-// thread's first value; members at or past `ng` are not written.  A step in
-// which no lane of the wave has an escape appends its code words two at a
-// time (at most 28 bits per pair).
+// exponents as 8-bit words.  Only the thread's first `nv` members are
+// written (all 32 in a full tile; in a partial one the members present are a
+// prefix of the group's member order).
+//  * A step in which no coded lane of the wave has an escape takes two
+//    members per lookup of the member-pair table (full tiles) and four
+//    members per LDS OR when their words fit in 32 bits on every lane.
+//  * A step with an escape looks each member up in the escape table (code
+//    word, or escape code and the exponent's 8 bits: at most 22 bits) and
+//    appends four members per OR when their words fit in 32 bits on every
+//    lane (an escape beside three short codes; a raw lane's four exponents
+//    are exactly 32 bits), else two per OR when every pair fits, else one.
 template <bool FULL, bool MIXED>
 __device__ __forceinline__ void emit_quarter(uint32_t* __restrict__ s, const EncTables& tb,
                                     const uint32_t (&dd)[kQSteps][2], uint32_t emax,
-                                    uint32_t ng, uint32_t first, bool raw_mode, uint32_t off)
+                                    uint32_t nv, bool raw_mode, uint32_t off)
 {
     uint64_t acc = 0;
     uint32_t nacc = off & 31;
@@ -649,12 +619,10 @@ __device__ __forceinline__ void emit_quarter(uint32_t* __restrict__ s, const Enc
     for (int k = 0; k < kQSteps; ++k) {
         const uint32_t d4[2] = {dd[k][0], dd[k][1]};
         const bool esc_here = coded && (((d4[0] | d4[1]) & 0xF0F0F0F0u) != 0);
-        if (FULL && (ZC_ENC_PAIRS == 2 || (ZC_ENC_PAIRS == 1 && MIXED)) &&
-            __ballot(esc_here) == 0) {
-            // Every d of the step's coded lanes is below 16, so two members
+        if (FULL && __ballot(esc_here) == 0) {
+            // every d of the step's coded lanes is below 16, so two members
             // index one pair entry: d0 | d1 << 4 is read off the packed
-            // bytes as (w | w >> 4).  Four members go out with one LDS OR
-            // when their code words fit in 32 bits on every lane.
+            // bytes as (w | w >> 4)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const uint32_t w = d4[h];
@@ -670,119 +638,52 @@ __device__ __forceinline__ void emit_quarter(uint32_t* __restrict__ s, const Enc
                     l23 = 16;
                 }
                 if (__ballot(l01 + l23 > 32u) == 0) {
-                    const uint32_t pl = l01 + l23;
-                    acc = (acc << pl) | ((c01 << l23) | c23);
-                    nacc += pl;
-                    const uint32_t wv = __builtin_amdgcn_alignbit(hi32(acc), lo32(acc), nacc);
-                    const uint32_t f = nacc >> 5;
-                    atomicOr(&s[wi], f ? wv : 0u);
-                    wi += f;
-                    nacc &= 31;
+                    emit_bits(s, acc, nacc, wi, (c01 << l23) | c23, l01 + l23);
                 } else {
-                    const uint32_t cc[2] = {c01, c23}, ll[2] = {l01, l23};
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        acc = (acc << ll[u]) | cc[u];
-                        nacc += ll[u];
-                        const uint32_t wv = __builtin_amdgcn_alignbit(hi32(acc), lo32(acc), nacc);
-                        const uint32_t f = nacc >> 5;
-                        atomicOr(&s[wi], f ? wv : 0u);
-                        wi += f;
-                        nacc &= 31;
-                    }
+                    emit_bits(s, acc, nacc, wi, c01, l01);
+                    emit_bits(s, acc, nacc, wi, c23, l23);
                 }
-            }
-        } else if ((!MIXED || ZC_MIXED_PAIR) && __ballot(esc_here) == 0) {
-            // the step's table lookups are all issued before its first LDS
-            // OR, so that they cost one LDS round trip, not one per pair
-            // (no escape here: each entry is code | length << 24)
-            uint32_t es[8];
-            if constexpr ((ZC_ENC_BATCH & 1) != 0) {
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj)
-                    es[jj] = tb.esc[(d4[jj >> 2] >> (8 * (jj & 3))) & 0xFF];
-            }
-#pragma unroll
-            for (int j = 0; j < 8; j += 2) {
-                uint32_t c2[2], l2[2];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int jj = j + u;
-                    const uint32_t d = (d4[jj >> 2] >> (8 * (jj & 3))) & 0xFF;
-                    uint32_t c, l;
-                    if constexpr ((ZC_ENC_BATCH & 1) != 0) {
-                        c = es[jj] & 0x3FFFFFu;
-                        l = es[jj] >> 24;
-                    } else {
-                        c = tb.code[d];
-                        l = tb.len[d];
-                    }
-                    if (MIXED) {
-                        c = raw_mode ? ((emax - d) & 0xFF) : c;
-                        l = raw_mode ? 8u : l;
-                    }
-                    const bool valid = FULL || first + static_cast<uint32_t>(k * 8 + jj) < ng;
-                    c2[u] = valid ? c : 0u;
-                    l2[u] = valid ? l : 0u;
-                }
-                const uint32_t pl = l2[0] + l2[1];
-                acc = (acc << pl) | ((c2[0] << l2[1]) | c2[1]);
-                nacc += pl;
-                const uint32_t w = __builtin_amdgcn_alignbit(hi32(acc), lo32(acc), nacc);
-                const uint32_t f = nacc >> 5;
-                atomicOr(&s[wi], f ? w : 0u);
-                wi += f;
-                nacc &= 31;
             }
         } else {
-            uint32_t es[8];
-            if constexpr ((ZC_ENC_BATCH & 2) != 0) {
+            // escape step: each member's word from the escape table; the
+            // quad's words are combined in 32 bits, which is exact when they
+            // fit; otherwise they are looked up again, pair by pair
+            auto member = [&](int u, uint32_t w, int jj, uint32_t& c, uint32_t& L) {
+                const uint32_t d = (w >> (8 * u)) & 0xFF;
+                uint32_t ent = tb.esc[d];
+                if (MIXED && raw_mode)
+                    ent = ((emax - d) & 0xFF) | (8u << 24);
+                const bool valid = FULL || static_cast<uint32_t>(k * 8 + jj) < nv;
+                ent = valid ? ent : 0u;
+                L = (ent >> 24) & 31;
+                const uint32_t esc = static_cast<uint32_t>(static_cast<int32_t>(ent) >> 31);
+                c = (ent & 0x3FFFFFu) | ((emax - d) & esc & 0xFFu);
+            };
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    es[j] = tb.esc[(d4[j >> 2] >> (8 * (j & 3))) & 0xFF];
-            }
-            // Each member's word is its code, or the escape code and the
-            // exponent's 8 bits (at most 22 bits).  With ZC_ESC_PAIRS, in a
-            // wave without raw groups, two members go out with one LDS OR
-            // when their words fit in 32 bits on every lane (an escape
-            // beside a code of up to 10 bits).  Waves with raw groups keep
-            // one member per OR: the pairs there cost register spills.
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t w = d4[h];
+                uint32_t cq = 0, lq = 0;
 #pragma unroll
-            for (int j = 0; j < 8; j += ((ZC_ESC_PAIRS && !MIXED) ? 2 : 1)) {
-                constexpr int kU = (ZC_ESC_PAIRS && !MIXED) ? 2 : 1;
-                uint32_t cw[kU], L[kU];
-#pragma unroll
-                for (int u = 0; u < kU; ++u) {
-                    const int jj = j + u;
-                    const uint32_t d = (d4[jj >> 2] >> (8 * (jj & 3))) & 0xFF;
-                    uint32_t ent = ((ZC_ENC_BATCH & 2) != 0) ? es[jj] : tb.esc[d];
-                    if (MIXED && raw_mode)
-                        ent = ((emax - d) & 0xFF) | (8u << 24);
-                    const bool valid = FULL || first + static_cast<uint32_t>(k * 8 + jj) < ng;
-                    ent = valid ? ent : 0u;
-                    L[u] = (ent >> 24) & 31;
-                    const uint32_t esc = static_cast<uint32_t>(static_cast<int32_t>(ent) >> 31);
-                    cw[u] = (ent & 0x3FFFFFu) | ((emax - d) & esc & 0xFFu);
+                for (int u = 0; u < 4; ++u) {
+                    uint32_t c, L;
+                    member(u, w, 4 * h + u, c, L);
+                    cq = (cq << L) | c;
+                    lq += L;
                 }
-                if (kU == 2 && __ballot(L[0] + L[kU - 1] > 32u) == 0) {
-                    const uint32_t pl = L[0] + L[kU - 1];
-                    acc = (acc << pl) | ((cw[0] << L[kU - 1]) | cw[kU - 1]);
-                    nacc += pl;
-                    const uint32_t w = __builtin_amdgcn_alignbit(hi32(acc), lo32(acc), nacc);
-                    const uint32_t f = nacc >> 5;
-                    atomicOr(&s[wi], f ? w : 0u);
-                    wi += f;
-                    nacc &= 31;
+                if (__ballot(lq > 32u) == 0) {
+                    emit_bits(s, acc, nacc, wi, cq, lq);
                 } else {
 #pragma unroll
-                    for (int u = 0; u < kU; ++u) {
-                        acc = (acc << L[u]) | cw[u];
-                        nacc += L[u];
-                        const uint32_t w = __builtin_amdgcn_alignbit(hi32(acc), lo32(acc), nacc);
-                        const uint32_t f = nacc >> 5;
-                        atomicOr(&s[wi], f ? w : 0u);
-                        wi += f;
-                        nacc &= 31;
+                    for (int u = 0; u < 4; u += 2) {
+                        uint32_t c0, l0, c1, l1;
+                        member(u, w, 4 * h + u, c0, l0);
+                        member(u + 1, w, 4 * h + u + 1, c1, l1);
+                        if (__ballot(l0 + l1 > 32u) == 0) {
+                            emit_bits(s, acc, nacc, wi, (c0 << l1) | c1, l0 + l1);
+                        } else {
+                            emit_bits(s, acc, nacc, wi, c0, l0);
+                            emit_bits(s, acc, nacc, wi, c1, l1);
+                        }
                     }
                 }
             }
@@ -790,26 +691,6 @@ __device__ __forceinline__ void emit_quarter(uint32_t* __restrict__ s, const Enc
     }
     if (nacc)
         atomicOr(&s[wi], lo32(acc) << (32 - nacc));
-}
-
-// Stores a tile stream from LDS to its 4-byte aligned place: single words
-// up to the first 16-byte boundary, 16-byte stores after it, single words
-// for the rest.
-__device__ inline void store_stream(uint8_t* gdst, const uint32_t* __restrict__ s,
-                                    uint32_t words, uint32_t lane)
-{
-    uint32_t* g = reinterpret_cast<uint32_t*>(gdst);
-    const uint32_t head = min(words, (4u - ((reinterpret_cast<uintptr_t>(g) >> 2) & 3u)) & 3u);
-    if (lane < head)
-        st_nt1(g + lane, s[lane]);
-    const uint32_t quads = (words - head) >> 2;
-    for (uint32_t q = lane; q < quads; q += kLanes) {
-        const uint32_t w = head + 4 * q;
-        st_nt4(g + w, make_uint4(s[w], s[w + 1], s[w + 2], s[w + 3]));
-    }
-    const uint32_t done = head + 4 * quads;
-    if (done + lane < words)
-        st_nt1(g + done + lane, s[done + lane]);
 }
 
 // Wave 0 of a tile: the tile's index entries; the last tile of a chunk also
@@ -839,15 +720,21 @@ __device__ inline void write_tile_index(const TileCtx& x, uint32_t toff, uint32_
 }
 
 // Everything after the loads: the partial maxima of the four waves are in
-// sh.part_max (written before the barrier that precedes this call).
+// sh.part_max (written before the barrier that precedes this call).  Waves
+// 1-3 return after the emission; wave 0 resolves the tile's offset, stores
+// the stream and the index entries, then publishes.
 template <bool FULL>
 __device__ __forceinline__ void compress_tile_back(const TileCtx& x, uint32_t (&dd)[kQSteps][2],
                                    int64_t* __restrict__ comp_sizes,
-                                   uint64_t* __restrict__ status, EncShared& sh)
+                                   uint64_t* __restrict__ status, EncShared& sh,
+                                   uint32_t epoch, uint32_t spin_limit)
 {
     const uint32_t lane = x.lane, wave = x.wave;
     const uint32_t ng = FULL ? 128u : group_members(x.rem, lane);
     const uint32_t first = wave * kQMembers;     // group index of this thread's first member
+    // members of this thread present in the tile (a prefix of its 32)
+    const uint32_t nv = FULL ? static_cast<uint32_t>(kQMembers)
+                             : min(ng > first ? ng - first : 0u, static_cast<uint32_t>(kQMembers));
 
     // 1. the group maximum from the waves' partial ones
     uint32_t emax = sh.part_max[0][lane];
@@ -862,6 +749,10 @@ __device__ __forceinline__ void compress_tile_back(const TileCtx& x, uint32_t (&
     for (int k = 0; k < kQSteps; ++k) {
         dd[k][0] = em4 - dd[k][0];
         dd[k][1] = em4 - dd[k][1];
+        // opaque from here on: the emission recomputes a raw group's
+        // exponents as E_max - d instead of keeping the exponent words alive
+        // beside the distances (which spilled registers)
+        asm volatile("" : "+v"(dd[k][0]), "+v"(dd[k][1]));
     }
     uint32_t bits = 0;
 #pragma unroll
@@ -870,17 +761,9 @@ __device__ __forceinline__ void compress_tile_back(const TileCtx& x, uint32_t (&
         for (int j = 0; j < 8; ++j) {
             const uint32_t d = (dd[k][j >> 2] >> (8 * (j & 3))) & 0xFF;
             const uint32_t L = sh.tb.len[d];
-            bits += (FULL || first + static_cast<uint32_t>(k * 8 + j) < ng) ? L : 0u;
+            bits += (FULL || static_cast<uint32_t>(k * 8 + j) < nv) ? L : 0u;
         }
     }
-    // The emission extracts each d again: an empty register constraint
-    // keeps the compiler from carrying the extracted bytes (two per value)
-    // across the barrier instead of the packed words.
-#if ZC_ENC_REEXTRACT
-#pragma unroll
-    for (int k = 0; k < kQSteps; ++k)
-        asm volatile("" : "+v"(dd[k][0]), "+v"(dd[k][1]));
-#endif
     sh.part_bits[wave][lane] = static_cast<uint16_t>(bits);
     __syncthreads();
 
@@ -900,195 +783,189 @@ __device__ __forceinline__ void compress_tile_back(const TileCtx& x, uint32_t (&
     uint32_t tile_bits;
     const uint32_t off = wave_excl_scan(glen, lane, &tile_bits);
     tile_bits = __builtin_amdgcn_readfirstlane(tile_bits);
-    const uint32_t tile_words = (tile_bits + 31) >> 5;
-    const uint32_t tile_bytes = tile_words * 4;
-    uint64_t poll = 0;
-    if (wave == 0) {
-        look_back_publish(status, x.item, x.t, tile_bytes, lane);
-        if (ZC_EARLY_POLL && x.t != 0)
-            poll = look_back_poll(status, static_cast<int64_t>(x.item) - 1, x.first, lane);
-    }
+    // at most 64 groups of 1024 bits: the bound keeps the stores of step 5
+    // inside the tile's share of the chunk bound whatever the scan gives
+    const uint32_t tile_words = min((tile_bits + 31) >> 5, static_cast<uint32_t>(kTileWordsMax));
+    if (wave == 0)
+        look_back_publish(status, x.item, x.t, tile_words, lane, epoch);
 
     // 4. code words into the LDS tile stream (zeroed at the kernel's start)
     if (__ballot(raw_mode) == 0)
-        emit_quarter<FULL, false>(sh.stage, sh.tb, dd, emax, ng, first, raw_mode, off + pre);
+        emit_quarter<FULL, false>(sh.stage, sh.tb, dd, emax, nv, raw_mode, off + pre);
     else
-        emit_quarter<FULL, true>(sh.stage, sh.tb, dd, emax, ng, first, raw_mode, off + pre);
+        emit_quarter<FULL, true>(sh.stage, sh.tb, dd, emax, nv, raw_mode, off + pre);
     __syncthreads();
     if (wave != 0)
         return;
 
     // 5. wave 0: the tile's offset, the stream, the index arrays
-    if (!ZC_EARLY_POLL && x.t != 0)
-        poll = look_back_poll(status, static_cast<int64_t>(x.item) - 1, x.first, lane);
-    const uint32_t toff = look_back_resolve(status, x.item, x.t, x.first, tile_bytes, lane, poll,
-                                            x.src, x.n, sh.tb.len, sh.spin_limit);
-    if (ZC_STORE_X4) {
-        store_stream(x.dst + x.G.X + toff, sh.stage, tile_words, lane);
-    } else {
-        // eight rows of LDS reads ahead of their stores
-        uint32_t* gstream = reinterpret_cast<uint32_t*>(x.dst + x.G.X + toff);
-        for (uint32_t r0 = 0; r0 < tile_words; r0 += 8 * kLanes) {
-            uint32_t v[8];
+    const uint32_t toff_w = look_back_resolve(status, x.item, x.t, x.first, lane, epoch, x.src,
+                                              x.n, sh.tb.len, spin_limit);
+    const uint32_t toff = toff_w * 4, tile_bytes = tile_words * 4;
+    // stores never leave the chunk's bound, whatever the offsets say (a
+    // correct stream always fits; this only keeps a fault impossible)
+    const bool fits = static_cast<uint64_t>(x.G.X) + toff + tile_bytes <= chunk_bound(x.n);
+    // eight rows of LDS read ahead of their stores
+    uint32_t* gstream = reinterpret_cast<uint32_t*>(x.dst + x.G.X + toff);
+    for (uint32_t r0 = 0; r0 < tile_words; r0 += 8 * kLanes) {
+        uint32_t v[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                v[i] = sh.stage[min(r0 + i * kLanes + lane, static_cast<uint32_t>(kEncStage - 1))];
+        for (int i = 0; i < 8; ++i)
+            v[i] = sh.stage[min(r0 + i * kLanes + lane, static_cast<uint32_t>(kEncStage - 1))];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                if (r0 + i * kLanes + lane < tile_words) {
-                    if (ZC_STREAM_NT)
-                        st_nt1(gstream + r0 + i * kLanes + lane, v[i]);
-                    else
-                        gstream[r0 + i * kLanes + lane] = v[i];
-                }
-        }
+        for (int i = 0; i < 8; ++i)
+            if (fits && r0 + i * kLanes + lane < tile_words)
+                gstream[r0 + i * kLanes + lane] = v[i];
     }
     write_tile_index(x, toff, tile_bytes, emax, glen, comp_sizes);
-    if (ZC_LATE_PUBLISH && x.t != 0 && lane == 0)
-        __hip_atomic_store(&status[x.item * kStatusStride], kFlagInc | (toff + tile_bytes),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the inclusive prefix is published after the stores: published earlier,
+    // the store loop waited for that device-coherent write to complete
+    if (x.t != 0 && lane == 0)
+        __hip_atomic_store(&status[x.item * kStatusStride],
+                           status_word(epoch, kFlagInc, toff_w + tile_words), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Tiles that are partial (a chunk's last tile) or unaligned: kept out of
 // line so that their register needs do not constrain the full-tile path.
 __device__ __attribute__((noinline)) void compress_tile_partial(
-    const uint16_t* src, uint8_t* dst, uint32_t n, uint32_t t, uint32_t item, uint32_t first,
-    uint32_t lane, uint32_t wave, int c, int64_t* __restrict__ comp_sizes,
-    uint64_t* __restrict__ status, EncShared* sh)
+    TileCtx x, int64_t* __restrict__ comp_sizes, uint64_t* __restrict__ status,
+    EncShared* sh, uint32_t epoch, uint32_t spin_limit)
 {
-    TileCtx x;
-    x.src = src;
-    x.dst = dst;
-    x.n = n;
-    x.t = t;
-    x.item = item;
-    x.first = first;
-    x.lane = lane;
-    x.wave = wave;
-    x.c = c;
-    x.G = geometry(n);
-    x.base = t * kTile;
-    x.rem = min(n - x.base, static_cast<uint32_t>(kTile));
     uint32_t dd[kQSteps][2];
-    sh->part_max[wave][lane] = static_cast<uint16_t>(load_split<false>(x, dd));
+    uint4 u[kQSteps];
+    load_tile<false>(x, u);
+    sh->part_max[x.wave][x.lane] = static_cast<uint16_t>(split_tile<false>(x, u, dd));
     __syncthreads();
-    compress_tile_back<false>(x, dd, comp_sizes, status, *sh);
+    compress_tile_back<false>(x, dd, comp_sizes, status, *sh, epoch, spin_limit);
 }
 
-__device__ __forceinline__ void compress_body(const uint16_t* __restrict__ in,
+// The end of a launch for wave 0 of each workgroup.  Every workgroup but the
+// last in grid order adds itself to one of 64 counters (spread over separate
+// lines) and leaves; the last one waits, bounded, until the others have all
+// counted (each counts after its last status access), then stores this
+// launch's tag for the next launch and resets the counters.  No workgroup
+// waits on the last one, so its wait ends.  When the tag wraps, or if the
+// wait ran out, every status slot is cleared first (a slot cleared under a
+// still-running look-back only sends it to the recomputation path).
+__device__ inline void finish_launch(uint32_t* __restrict__ hdr, uint64_t* __restrict__ status,
+                                     uint32_t status_slots, uint32_t epoch, uint32_t lane)
+{
+    uint32_t* counters = hdr + kHdrCounters;
+    if (blockIdx.x != gridDim.x - 1) {
+        if (lane == 0)
+            __hip_atomic_fetch_add(&counters[(blockIdx.x % kCounters) * kCounterStride], 1u,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    bool done = false;
+    for (uint32_t spin = 0; spin < kDoneSpinLimit && !done; ++spin) {
+        const uint32_t c = __hip_atomic_load(&counters[lane * kCounterStride], __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        done = wave_sum(c) >= gridDim.x - 1;
+        if (!done)
+            __builtin_amdgcn_s_sleep(2);
+    }
+    if (epoch == 0xFFFFFFFFu || !done) {
+        for (uint32_t i = lane; i < status_slots; i += kLanes)
+            __hip_atomic_store(&status[static_cast<size_t>(i) * kStatusStride], 0ull,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __hip_atomic_store(&counters[lane * kCounterStride], 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0)
+        __hip_atomic_store(&hdr[kHdrEpoch], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// This launch's tag: one more than the last launch's, stored in the
+// workspace (0 is never a tag, so a zeroed workspace holds no valid word).
+// It is read with a scalar load through the constant address space: the
+// scalar cache is invalidated at every kernel dispatch, and the word changes
+// only at the very end of a launch, after every workgroup has read it.  (A
+// device-coherent vector load of this one word by every workgroup cost
+// about 15 % of the kernel's time.)
+typedef const __attribute__((address_space(4))) uint32_t* ConstU32;
+
+__device__ inline uint32_t launch_epoch(const uint32_t* __restrict__ hdr)
+{
+    const uint32_t e = ((ConstU32)hdr)[kHdrEpoch] + 1u;
+    return e == 0 ? 1u : e;
+}
+
+// One tile per workgroup, in grid order (chunk by chunk, so neighbouring
+// workgroups stream neighbouring bytes).  The look-back never waits without
+// bound, so the order needs no assumption about dispatch order.  The
+// launch's tag (epoch) is one more than the one stored in the workspace.
+template <class Tab>
+__device__ __forceinline__ void compress_body(const Tab& tab, const uint16_t* __restrict__ in,
                                               uint8_t* __restrict__ out,
                                               int64_t* __restrict__ comp_sizes,
-                                              uint64_t* __restrict__ status,
-                                              uint32_t* __restrict__ tickets,
-                                              const ChunkTable& tab)
+                                              uint8_t* __restrict__ ws, uint32_t status_slots)
 {
     __shared__ __align__(16) EncShared sh;
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & (kLanes - 1);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kLanes);   // uniform: scalar
-
-    // The workgroup's chunk and tile come from its position in the grid
-    // (tile_order): chunk by chunk by default; with ZC_ENC_INTERLEAVE equal
-    // chunks are taken round-robin, and in the ticket order the tile within
-    // the chunk comes from the chunk's ticket counter (requested first, so
-    // that the round trip overlaps the table set-up).
+    uint32_t* hdr = reinterpret_cast<uint32_t*>(ws);
+    uint64_t* status = reinterpret_cast<uint64_t*>(ws + kWsHeader);
     const uint32_t item = blockIdx.x;
-    TileCtx x;
-    if (ZC_ENC_INTERLEAVE && tab.uniform_tiles)
-        x.c = static_cast<int>(item % static_cast<uint32_t>(tab.nchunks));
-    else
-        x.c = find_chunk(tab, item);
-    uint32_t ticket = 0;
-    if (tab.grid_order == kOrderTickets && tid == 0)
-        ticket = atomicAdd(&tickets[x.c * kTicketStride], 1u);
-    x.n = tab.n[x.c];
-    x.first = tab.item_begin[x.c];
-    x.lane = lane;
-    x.wave = wave;
-    x.src = in + tab.voff[x.c];
-    x.dst = out + tab.boff[x.c];
-    x.G = geometry(x.n);
-    const bool aligned = (reinterpret_cast<uintptr_t>(x.src) & 15) == 0;
-
-    // A grid-ordered tile is known at once: a full one issues its loads now,
-    // so that their latency covers the table set-up below.
-    uint4 v[kLoadBatch];
-    bool loaded = false;
-    if (tab.grid_order != kOrderTickets) {
-        x.t = tab.grid_order == kOrderRoundRobin ? item / static_cast<uint32_t>(tab.nchunks)
-                                                 : item - x.first;
-        x.base = x.t * kTile;
-        loaded = ZC_EARLY_LOAD && x.n != 0 && aligned && x.n - x.base >= static_cast<uint32_t>(kTile);
-        if (loaded)
-            load_tile<true>(x, v, 0);
+    if (item >= tab.nitems) {      // device-split grids are sized for the bound
+        if (wave == 0)
+            finish_launch(hdr, status, status_slots, launch_epoch(hdr), lane);
+        return;
     }
+    const TileCtx x = tile_ctx(tab, item, in, out, lane, wave);
+
+    // a full tile issues its loads first, so that their latency covers the
+    // table set-up below; the launch's tag is read after them and first
+    // needed when the tile publishes its size
+    const bool full = tile_full(x);
+    uint4 v[kQSteps];
+    if (full)
+        load_tile<true>(x, v);
+    const uint32_t epoch = launch_epoch(hdr);
     constexpr uint32_t kTbWords = sizeof(EncTables) / 16;
 #pragma unroll
     for (uint32_t i = tid; i < kTbWords; i += kEncBlock)
         reinterpret_cast<uint4*>(&sh.tb)[i] = reinterpret_cast<const uint4*>(&c_enc)[i];
     for (uint32_t i = tid * 4; i < static_cast<uint32_t>(kEncStage); i += kEncBlock * 4)
         *reinterpret_cast<uint4*>(&sh.stage[i]) = make_uint4(0, 0, 0, 0);
-    if (tid == 0)
-        sh.spin_limit = tab.spin_limit;
-    if (tab.grid_order == kOrderTickets) {
-        if (tid == 0)
-            sh.tile = ticket;
-        __syncthreads();
-        x.t = __builtin_amdgcn_readfirstlane(sh.tile);
-    }
-    x.item = x.first + x.t;
 
     if (x.n == 0) {
         if (tid < 8)
             reinterpret_cast<uint32_t*>(x.dst)[tid] = header_word(tid, 0, 32);
         if (tid == 0)
             comp_sizes[x.c] = 32;
-        return;
-    }
-    x.base = x.t * kTile;
-    x.rem = min(x.n - x.base, static_cast<uint32_t>(kTile));
-    const bool full = x.rem == kTile && aligned;
-    if (full) {
-        if (!loaded)
-            load_tile<true>(x, v, 0);
+    } else if (full) {
         uint32_t dd[kQSteps][2];
-        uint32_t mx = split_tile<true>(x, v, dd, 0);
-#pragma unroll
-        for (int b = 1; b < kBatches; ++b) {
-            load_tile<true>(x, v, b);
-            mx = max(mx, split_tile<true>(x, v, dd, b));
-        }
-        sh.part_max[wave][lane] = static_cast<uint16_t>(mx);
+        sh.part_max[wave][lane] = static_cast<uint16_t>(split_tile<true>(x, v, dd));
         __syncthreads();
-        compress_tile_back<true>(x, dd, comp_sizes, status, sh);
+        compress_tile_back<true>(x, dd, comp_sizes, status, sh, epoch, tab.spin_limit);
     } else {
-        compress_tile_partial(x.src, x.dst, x.n, x.t, x.item, x.first, lane, wave, x.c,
-                              comp_sizes, status, &sh);
+        compress_tile_partial(x, comp_sizes, status, &sh, epoch, tab.spin_limit);
     }
+    if (wave == 0)
+        finish_launch(hdr, status, status_slots, epoch, lane);
 }
 
 __global__ __launch_bounds__(kEncBlock, kMinWavesEnc)
 void zc_compress_kernel(const uint16_t* __restrict__ in, uint8_t* __restrict__ out,
-                        int64_t* __restrict__ comp_sizes,
-                        uint64_t* __restrict__ status, uint32_t* __restrict__ tickets,
-                        ChunkTable tab)
+                        int64_t* __restrict__ comp_sizes, uint8_t* __restrict__ ws,
+                        uint32_t status_slots, ChunkTable tab)
 {
-    compress_body(in, out, comp_sizes, status, tickets, tab);
+    compress_body(tab, in, out, comp_sizes, ws, status_slots);
 }
 
 // The same with the chunk table in device memory (built on the device from
 // device-resident counts); the grid is an upper bound on the tile count and
-// workgroups past the table's tiles return at once.
+// workgroups past the table's tiles only take part in the launch's end.
 __global__ __launch_bounds__(kEncBlock, kMinWavesEnc)
 void zc_compress_dev_kernel(const uint16_t* __restrict__ in, uint8_t* __restrict__ out,
-                            int64_t* __restrict__ comp_sizes,
-                            uint64_t* __restrict__ status, uint32_t* __restrict__ tickets,
-                            const ChunkTable* __restrict__ tab)
+                            int64_t* __restrict__ comp_sizes, uint8_t* __restrict__ ws,
+                            uint32_t status_slots, const ChunkTable* __restrict__ tab)
 {
-    if (blockIdx.x >= tab->nitems)
-        return;
-    compress_body(in, out, comp_sizes, status, tickets, *tab);
+    compress_body(*tab, in, out, comp_sizes, ws, status_slots);
 }
 
 // ------------------------------------------------------------ decompress
@@ -1196,10 +1073,7 @@ __device__ inline void put_values(uint16_t* __restrict__ dst, const uint8_t* __r
         o.y = (__builtin_amdgcn_perm(r.x, r.x, 0x03030202u) & 0x807F807Fu) | (e8[2] << 7) | (e8[3] << 23);
         o.z = (__builtin_amdgcn_perm(r.y, r.y, 0x01010000u) & 0x807F807Fu) | (e8[4] << 7) | (e8[5] << 23);
         o.w = (__builtin_amdgcn_perm(r.y, r.y, 0x03030202u) & 0x807F807Fu) | (e8[6] << 7) | (e8[7] << 23);
-        if (ZC_DEC_OUT_NT)
-            st_nt4(dst + i0, o);
-        else
-            *reinterpret_cast<uint4*>(dst + i0) = o;
+        st_nt4(dst + i0, o);
     } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -1243,13 +1117,13 @@ __device__ __forceinline__ void decode_group(const Win& win, const uint8_t* __re
     // unrolled inner loop indexes statically: each slot is reloaded right
     // after its last use, so no register is copied while its load is in
     // flight and each wait leaves the younger loads and stores outstanding.
-    constexpr int kRing = ZC_DEC_RING;
+    constexpr int kRing = 1;
     static_assert(kSteps % kRing == 0, "whole rounds of the prefetch ring");
     const uint2* rsrc2 = reinterpret_cast<const uint2*>(rsrc + base) + lane;
     uint2 ring[kRing];
 #pragma unroll
     for (int j = 0; j < kRing; ++j)
-        ring[j] = FULL ? (ZC_DEC_LOAD_NT ? ld_nt2(rsrc2 + j * 64) : rsrc2[j * 64]) : make_uint2(0, 0);
+        ring[j] = FULL ? ld_nt2(rsrc2 + j * 64) : make_uint2(0, 0);
 #pragma unroll 1
     for (int k0 = 0; k0 < kSteps; k0 += kRing)
 #pragma unroll
@@ -1321,8 +1195,7 @@ __device__ __forceinline__ void decode_group(const Win& win, const uint8_t* __re
         }
         put_values<FULL>(dst, rsrc, n, base + k * 512 + lane * 8, ring[kj], e8, vec_out);
         if (FULL)   // the last round reloads the last row (in bounds, unused)
-            ring[kj] = ZC_DEC_LOAD_NT ? ld_nt2(rsrc2 + min(k + kRing, kSteps - 1) * 64)
-                                      : rsrc2[min(k + kRing, kSteps - 1) * 64];
+            ring[kj] = ld_nt2(rsrc2 + min(k + kRing, kSteps - 1) * 64);
     }
 }
 
@@ -1338,8 +1211,7 @@ __device__ inline void stage_words(uint32_t* __restrict__ s, const uint32_t* __r
 #pragma unroll
     for (int i = 0; i < kRows; ++i)
         if (static_cast<uint32_t>(i * kLanes) < words)
-            v[i] = ZC_DEC_LOAD_NT ? ld_nt1(g + min(lane + i * kLanes, words - 1))
-                                  : g[min(lane + i * kLanes, words - 1)];
+            v[i] = ld_nt1(g + min(lane + i * kLanes, words - 1));
 #pragma unroll
     for (int i = 0; i < kRows; ++i)
         if (lane + i * kLanes < words)
@@ -1834,10 +1706,6 @@ void zc_plan_kernel(const int64_t* __restrict__ counts, int32_t num_chunks, int3
     }
     bad = __ballot(bad) != 0 || items > max_items;
 
-    // equal chunks (all non-empty with the same tile count) are interleaved
-    const uint32_t first_items = __shfl(items_c, 0);
-    const bool same = !mine || (items_c == first_items && n > 0);
-    const uint32_t uniform = (__ballot(!same) == 0 && m > 0) ? first_items : 0u;
     if (mine) {
         tab->item_begin[lane] = ibegin;
         tab->n[lane] = static_cast<uint32_t>(n);
@@ -1855,8 +1723,6 @@ void zc_plan_kernel(const int64_t* __restrict__ counts, int32_t num_chunks, int3
         tab->nchunks = m;
         tab->chunk_base = c0;
         tab->nitems = bad ? 0u : items;
-        tab->uniform_tiles = uniform;
-        tab->grid_order = tile_order(uniform);
         tab->spin_limit = spin_limit;
         if (decode && bad && status)
             atomicCAS(status, 0, (ZC_REASON_SIZE << 24) | (c0 & 0xFFFFFF));
@@ -2031,7 +1897,13 @@ uint32_t lookback_spin_limit()
     return limit;
 }
 
-constexpr size_t kWsHeader = kMaxChunks * kTicketStride * 4;   // per-chunk ticket counters
+// Zeroes `words` 32-bit words (a workspace that must start at zero).
+__global__ void zc_zero_kernel(uint32_t* __restrict__ p, uint64_t words)
+{
+    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < words;
+         i += static_cast<uint64_t>(gridDim.x) * blockDim.x)
+        p[i] = 0;
+}
 
 
 }  // namespace
@@ -2050,14 +1922,21 @@ static __device__ __align__(256) uint8_t scratch[kNoallocBytes];
 constexpr int kMaxDevices = 64;
 
 // The device address of this GPU's scratch array, looked up once per device
-// with that device current; nullptr if the lookup failed.
-void* noalloc_scratch(int device)
+// with that device current; nullptr if the lookup or its clearing failed.
+// The array must start at zero (a compress workspace does), so the first call
+// on a device clears it with a fill kernel on that call's stream, ahead of
+// the call's own launches.
+void* noalloc_scratch(int device, hipStream_t stream)
 {
     static std::once_flag once[kMaxDevices];
     static void* ptr[kMaxDevices];
-    std::call_once(once[device], [device] {
+    std::call_once(once[device], [device, stream] {
         void* p = nullptr;
-        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess)
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return;
+        hipLaunchKernelGGL(zc_zero_kernel, dim3(256), dim3(256), 0, stream,
+                           static_cast<uint32_t*>(p), static_cast<uint64_t>(kNoallocBytes / 4));
+        if (hipGetLastError() == hipSuccess)
             ptr[device] = p;
     });
     return ptr[device];
@@ -2079,7 +1958,7 @@ bool dev_args_ok(int64_t total, int32_t num_chunks)
            dev_max_items(total, num_chunks < kMaxChunks ? num_chunks : kMaxChunks) < (1ull << 31);
 }
 
-// Workspace layout of the device-split calls: ticket counters, look-back
+// Workspace layout of the device-split calls: header, look-back
 // status words for the largest launch, then one chunk table per launch.
 uint64_t dev_tables_offset(int64_t total, int32_t num_chunks)
 {
@@ -2238,9 +2117,10 @@ int zc_compress(const uint16_t* d_in, const int64_t* counts, int32_t num_chunks,
         return ZC_ENOSPC;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    uint32_t* ticket = static_cast<uint32_t*>(d_ws);
     const uint32_t spin_limit = lookback_spin_limit();
-    uint64_t* status = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(d_ws) + kWsHeader);
+    uint8_t* ws = static_cast<uint8_t*>(d_ws);
+    const uint64_t slots64 = (ws_bytes - kWsHeader) / (8ull * kStatusStride);
+    const uint32_t slots = static_cast<uint32_t>(slots64 < 0xFFFFFFFFull ? slots64 : 0xFFFFFFFFull);
     uint8_t* out = static_cast<uint8_t*>(d_out);
 
     uint64_t voff = 0, boff = 0;
@@ -2261,24 +2141,14 @@ int zc_compress(const uint16_t* d_in, const int64_t* counts, int32_t num_chunks,
             boff += align256(chunk_bound(n));
         }
         tab.nchunks = m;
+        tab.chunk_base = c0;
         tab.nitems = items;
         tab.item_begin[m] = items;
-        tab.uniform_tiles = tab.n[0] ? (items / static_cast<uint32_t>(m)) : 0u;
-        for (int32_t i = 0; i < m && tab.uniform_tiles; ++i)
-            if (tab.item_begin[i + 1] - tab.item_begin[i] != tab.uniform_tiles || tab.n[i] == 0)
-                tab.uniform_tiles = 0;
-        // Tiles in grid order, chunk by chunk (tile_order).
-        tab.grid_order = tile_order(tab.uniform_tiles);
         tab.spin_limit = spin_limit;
-
-        // the ticket word and the look-back status words start at zero
-        const uint32_t twords = static_cast<uint32_t>(kWsHeader / 4);
-        const uint32_t words = items + twords;
-        const uint32_t cblocks = (words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024;
-        hipLaunchKernelGGL(zc_clear_kernel, dim3(cblocks), dim3(256), 0, s, ticket, twords,
-                           status, items);
-        hipLaunchKernelGGL(zc_compress_kernel, dim3(items), dim3(kEncBlock), 0, s, d_in,
-                           out, d_comp_sizes + c0, status, ticket, tab);
+        // one workgroup per tile; the status words need no clearing (each
+        // launch tags its own)
+        hipLaunchKernelGGL(zc_compress_kernel, dim3(items), dim3(kEncBlock), 0, s, d_in, out,
+                           d_comp_sizes + c0, ws, slots, tab);
         if (hipGetLastError() != hipSuccess)
             return ZC_EHIP;
     }
@@ -2299,11 +2169,11 @@ int zc_compress_noalloc(const uint16_t* d_in, const int64_t* counts, int32_t num
     int device = -1;
     if (hipGetDevice(&device) != hipSuccess || device < 0 || device >= kMaxDevices)
         return ZC_EHIP;
-    void* ws = noalloc_scratch(device);     // this device's array, current device set
+    void* ws = noalloc_scratch(device, static_cast<hipStream_t>(stream));   // current device's
     if (!ws)
         return ZC_EHIP;
-    // the same launches as zc_compress; its clear kernel zeroes the status
-    // words this call uses (they hold the previous call's values)
+    // the same launch as zc_compress: the array is this device's workspace,
+    // which every call leaves ready for the next
     return zc_compress(d_in, counts, num_chunks, d_out, out_capacity, d_comp_sizes, ws,
                        kNoallocBytes, stream);
 }
@@ -2349,24 +2219,19 @@ int zc_compress_dev(const uint16_t* d_in, const int64_t* d_counts, int32_t num_c
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* ws = static_cast<uint8_t*>(d_ws);
-    uint32_t* ticket = reinterpret_cast<uint32_t*>(ws);
-    uint64_t* status = reinterpret_cast<uint64_t*>(ws + kWsHeader);
-    uint8_t* tables = ws + dev_tables_offset(total_values, num_chunks);
+    const uint64_t tables_at = dev_tables_offset(total_values, num_chunks);
+    uint8_t* tables = ws + tables_at;
+    const uint32_t slots = static_cast<uint32_t>((tables_at - kWsHeader) / (8ull * kStatusStride));
     const uint32_t spin_limit = lookback_spin_limit();
     for (int32_t c0 = 0, g = 0; c0 < num_chunks; c0 += kMaxChunks, ++g) {
         const int32_t m = num_chunks - c0 < kMaxChunks ? num_chunks - c0 : kMaxChunks;
         const uint32_t items = static_cast<uint32_t>(dev_max_items(total_values, m));
         ChunkTable* tab = reinterpret_cast<ChunkTable*>(tables + g * align256(sizeof(ChunkTable)));
-        const uint32_t twords = static_cast<uint32_t>(kWsHeader / 4);
-        const uint32_t words = items + twords;
-        const uint32_t cblocks = (words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024;
-        hipLaunchKernelGGL(zc_clear_kernel, dim3(cblocks), dim3(256), 0, s, ticket, twords,
-                           status, items);
         hipLaunchKernelGGL(zc_plan_kernel, dim3(1), dim3(kLanes), 0, s, d_counts, num_chunks, c0, m,
                            total_values, static_cast<const int64_t*>(nullptr), uint64_t(0), items,
                            spin_limit, 0, tab, d_slot_off, d_comp_sizes, static_cast<int32_t*>(nullptr));
         hipLaunchKernelGGL(zc_compress_dev_kernel, dim3(items), dim3(kEncBlock), 0, s, d_in,
-                           static_cast<uint8_t*>(d_out), d_comp_sizes + c0, status, ticket,
+                           static_cast<uint8_t*>(d_out), d_comp_sizes + c0, ws, slots,
                            static_cast<const ChunkTable*>(tab));
         if (hipGetLastError() != hipSuccess)
             return ZC_EHIP;

@@ -306,7 +306,7 @@ def compress(x, counts, stream=None):
     with _on(stream):
         out = torch.empty(max(zc_bound(a), 16), dtype=torch.uint8, device=dev)
         sizes = torch.empty(max(len(a), 1), dtype=torch.int64, device=dev)
-        ws = torch.empty(max(zc_workspace_bytes(a), 8), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(max(zc_workspace_bytes(a), 8), dtype=torch.uint8, device=dev)
         r = zc_compress(x, a, out, sizes, ws, stream=stream)
     if r != ZC_OK:
         raise ZcError(r, "zc_compress")
@@ -340,7 +340,7 @@ def compress_dev(x, d_counts, stream=None):
         out = torch.empty(max(zc_bound_max(total, nc), 16), dtype=torch.uint8, device=dev)
         sizes = torch.empty(max(nc, 1), dtype=torch.int64, device=dev)
         slots = torch.empty(max(nc, 1), dtype=torch.int64, device=dev)
-        ws = torch.empty(max(zc_workspace_bytes_max(total, nc), 256), dtype=torch.uint8,
+        ws = torch.zeros(max(zc_workspace_bytes_max(total, nc), 256), dtype=torch.uint8,
                          device=dev)
         r = zc_compress_dev(x, d_counts, total, out, sizes, slots, ws, stream=stream)
     if r != ZC_OK:
@@ -412,7 +412,7 @@ def pipeline(x, counts, groups, streams=None, check=True):
     send = torch.empty(max(cap, 16), dtype=torch.uint8, device=x.device)
     recv = torch.zeros(max(cap, 16), dtype=torch.uint8, device=x.device)
     sizes = torch.empty(max(len(a), 1), dtype=torch.int64, device=x.device)
-    ws = torch.empty(max(zc_workspace_bytes(a), 16), dtype=torch.uint8, device=x.device)
+    ws = torch.zeros(max(zc_workspace_bytes(a), 16), dtype=torch.uint8, device=x.device)
     y = torch.empty(int(a.sum()), dtype=x.dtype, device=x.device)
     status = torch.zeros(1, dtype=torch.int32, device=x.device)
     sc, sl, sd = (None, None, None) if streams is None else streams

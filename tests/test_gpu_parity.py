@@ -288,7 +288,7 @@ def test_device_split_rejects_bad_counts():
         out = torch.zeros(zc.zc_bound_max(total, 3), dtype=torch.uint8, device=DEV)
         sizes = torch.zeros(3, dtype=torch.int64, device=DEV)
         slots = torch.zeros(3, dtype=torch.int64, device=DEV)
-        ws = torch.empty(zc.zc_workspace_bytes_max(total, 3), dtype=torch.uint8, device=DEV)
+        ws = torch.zeros(zc.zc_workspace_bytes_max(total, 3), dtype=torch.uint8, device=DEV)
         assert zc.zc_compress_dev(x, dc, total, out, sizes, slots, ws) == zc.ZC_OK
         torch.cuda.synchronize()
         assert sizes.cpu().tolist() == [-1, -1, -1]
@@ -309,7 +309,7 @@ def test_capacity_and_argument_errors():
     x = to_dev(synth.gaussian_bits(10000, 0.02, seed=1))
     out = torch.empty(zc.zc_bound(cnt) - 1, dtype=torch.uint8, device=DEV)
     sizes = torch.empty(1, dtype=torch.int64, device=DEV)
-    ws = torch.empty(zc.zc_workspace_bytes(cnt), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(zc.zc_workspace_bytes(cnt), dtype=torch.uint8, device=DEV)
     assert zc.zc_compress(x, cnt, out, sizes, ws) == zc.ZC_ENOSPC
     out = torch.empty(zc.zc_bound(cnt), dtype=torch.uint8, device=DEV)
     assert zc.zc_compress(x, cnt, out, sizes, ws[:16]) == zc.ZC_ENOSPC
@@ -535,3 +535,62 @@ def test_decoder_writes_stay_in_the_chunk(oracle):
     # the oracle rejects about 30 of each 50 in the index and exponent
     # sections, none in the sign+mantissa bytes
     assert 40 <= rejected <= 110, rejected
+
+
+# ------------------------------------------- workspace launch tags ---
+
+WS_HEADER = 8448         # header bytes: u32 tag of the last launch at 0, then 64 u32
+WS_COUNTERS = 64         # counters of finished workgroups, one per 128-byte line from 128
+WS_SLOT = 64             # one 8-byte status word per 64-byte line after the header
+
+
+def _compress_into(x, cnt, ws):
+    cnt = np.asarray(cnt, np.int64)
+    out = torch.zeros(zc.zc_bound(cnt), dtype=torch.uint8, device=DEV)
+    sizes = torch.zeros(len(cnt), dtype=torch.int64, device=DEV)
+    assert zc.zc_compress(x, cnt, out, sizes, ws) == zc.ZC_OK
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), sizes.cpu().numpy()
+
+
+def test_workspace_reused_across_calls(oracle):
+    # One workspace for a run of calls with different data and layouts: the
+    # status words of earlier calls carry older tags and are never taken for
+    # this call's; every call's streams equal the oracle's, and the header
+    # holds the number of calls made, its counter back at zero.
+    layouts = [np.full(6, 5 * TILE, np.int64), np.array([3, 9 * TILE + 1, 0, TILE], np.int64),
+               np.full(3, 11 * TILE, np.int64), np.array([70 * TILE + 9], np.int64)]
+    ws = torch.zeros(max(zc.zc_workspace_bytes(c) for c in layouts), dtype=torch.uint8,
+                     device=DEV)
+    for i, cnt in enumerate(layouts * 2):
+        w = synth.gaussian_bits(int(cnt.sum()), 0.001 * (i + 1), seed=300 + i)
+        w[::(101 + i)] = 0
+        say("reused workspace, call %d: %s" % (i, cnt.tolist()))
+        b, sz = _compress_into(to_dev(w), cnt, ws)
+        off, _ = oracle.slot_offsets(cnt)
+        oracle_pool.compare_chunks(oracle, w, cnt, b, sz, off, label="call %d" % i)
+        hdr = ws[:WS_HEADER].cpu().numpy().view(np.uint32)
+        counters = hdr[32:32 + 32 * WS_COUNTERS:32]
+        assert hdr[0] == i + 1 and not counters.any(), (i, hdr[0], counters)
+
+
+def test_workspace_tag_wraps(oracle):
+    # The launch tag wraps after 2^32 - 1 launches: the launch that takes the
+    # last tag clears every status slot of the workspace before it stores the
+    # tag, and the next launch starts again at 1.  Forced here by writing the
+    # header; both calls must still equal the oracle.
+    cnt = np.full(4, 7 * TILE, np.int64)
+    ws = torch.zeros(zc.zc_workspace_bytes(cnt), dtype=torch.uint8, device=DEV)
+    ws[:4].view(torch.int32)[0] = -2           # stored tag 0xFFFFFFFE
+    for i, tag in enumerate((0xFFFFFFFF, 1)):
+        w = synth.gaussian_bits(int(cnt.sum()), 0.02, seed=400 + i)
+        b, sz = _compress_into(to_dev(w), cnt, ws)
+        off, _ = oracle.slot_offsets(cnt)
+        oracle_pool.compare_chunks(oracle, w, cnt, b, sz, off, label="wrap call %d" % i)
+        h = ws.cpu().numpy()
+        assert int(h[:4].view(np.uint32)[0]) == tag
+        slots = h[WS_HEADER:].reshape(-1, WS_SLOT)[:, :8].copy().view(np.uint64).ravel()
+        if tag == 0xFFFFFFFF:
+            assert not slots.any()                 # cleared after the last use of the tag
+        else:
+            assert np.all((slots >> np.uint64(32)) == 1)    # every tile published with tag 1
