@@ -17,6 +17,9 @@ roofline.traffic is read from the committed counter summary of this workload
 (profiles/zc_kernels_<workload>_traffic.txt) when the kernel sources hash to
 the value recorded there; otherwise it is null.
 
+With the default workload, workloads 1, 3, 4 and 5 are then timed the same
+way (compress and decompress only) and reported under per_config.
+
 The oracle (plain C, test infrastructure) is timed on the host cores over the
 same workload for the cpu_baseline field.
 
@@ -221,6 +224,67 @@ def time_pipeline(args, x, counts, dev, evict, ev):
     return out
 
 
+def measure_workload(wl, steps, warmup, dev, stream, evict, ev):
+    """Compress and decompress timings of workload wl with host chunk counts,
+    measured the way the headline workload is (cache flush before each call,
+    HIP events on the library's stream), and its round trip checked."""
+    import numpy as np
+    import torch
+    from lossless_bf16_tensor_sign_amd import synth, zc
+    w, counts = synth.make(wl, seed=synth.default_seed(wl), workers=8)
+    n = int(counts.sum())
+    x = torch.from_numpy(w.view(np.int16)).to(dev)
+    del w
+    buf = torch.empty(zc.zc_bound(counts), dtype=torch.uint8, device=dev)
+    sizes = torch.empty(len(counts), dtype=torch.int64, device=dev)
+    ws = torch.zeros(zc.zc_workspace_bytes(counts), dtype=torch.uint8, device=dev)
+    y = torch.empty(n, dtype=torch.int16, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    tc, td = [], []
+    for i in range(warmup + steps):
+        evict(i + 31)
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        r = zc.zc_compress(x, counts, buf, sizes, ws, stream=stream)
+        e1.record(stream)
+        if r != zc.ZC_OK:
+            raise zc.ZcError(r, "zc_compress")
+        evict(i + 32)
+        e2, e3 = ev(), ev()
+        e2.record(stream)
+        r = zc.zc_decompress(buf, counts, y, status, stream=stream)
+        e3.record(stream)
+        if r != zc.ZC_OK:
+            raise zc.ZcError(r, "zc_decompress")
+        if i >= warmup:
+            tc.append((e0, e1))
+            td.append((e2, e3))
+    torch.cuda.synchronize()
+    if int(status.item()) != 0 or not torch.equal(x, y):
+        log("ROUND TRIP FAILED on workload %d" % wl)
+        sys.exit(1)
+    comp = int(sizes.sum().item())
+    c_s = float(np.mean([a.elapsed_time(b) for a, b in tc])) * 1e-3
+    d_s = float(np.mean([a.elapsed_time(b) for a, b in td])) * 1e-3
+    alg = 2 * n + comp
+    out = {
+        "values": n,
+        "chunks": int(len(counts)),
+        "steps": steps,
+        "compress_ms": round(c_s * 1e3, 4),
+        "decompress_ms": round(d_s * 1e3, 4),
+        "compress_GBps": round(2 * n / c_s / 1e9, 2),
+        "decompress_GBps": round(2 * n / d_s / 1e9, 2),
+        "ratio": round(2 * n / comp, 5),
+        "pct_hbm_peak_algorithmic": {
+            "compress": round(100 * alg / c_s / 1e9 / HBM_PEAK_GBPS, 2),
+            "decompress": round(100 * alg / d_s / 1e9 / HBM_PEAK_GBPS, 2),
+        },
+    }
+    log("workload %d: %s" % (wl, out))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,7 +311,18 @@ def main():
                     help="decode with zc_decompress_reduce: the chunks are one rank's "
                          "shard as received from each peer, summed in fp32 in chunk "
                          "order (equal chunks only)")
+    ap.add_argument("--per-config", default=None, metavar="LIST",
+                    help="comma-separated other workloads to time after the headline "
+                         "one (compress and decompress only), reported under per_config; "
+                         "default 1,3,4,5 for workload 2 and none otherwise; '' for none")
+    ap.add_argument("--per-config-steps", type=int, default=10)
     args = ap.parse_args()
+    if args.per_config is None:
+        args.per_config = "1,3,4,5" if args.workload == 2 else ""
+    others = [int(v) for v in args.per_config.split(",") if v.strip()]
+    if any(v not in (1, 2, 3, 4, 5) or v == args.workload for v in others):
+        print("--per-config takes workloads 1..5 other than --workload", file=sys.stderr)
+        sys.exit(2)
 
     if args.gpus != 1:
         print("bench.py measures one GPU only: this codec runs per GPU and no "
@@ -481,6 +556,16 @@ def main():
 
     if args.pipeline:
         line["pipeline"] = time_pipeline(args, x, counts, dev, evict, ev)
+
+    if others:
+        # free the headline workload's buffers before the next ones are made
+        del x, buf, y, sizes, slots, dcounts, ws, red, est
+        torch.cuda.empty_cache()
+        line["per_config"] = {}
+        for wl in others:
+            log("per-config workload %d (%s)" % (wl, synth.NAMES[wl]))
+            line["per_config"][synth.NAMES[wl]] = measure_workload(
+                wl, args.per_config_steps, 2, dev, stream, evict, ev)
 
     if not args.no_cpu_baseline:
         threads = max(1, min(args.cpu_threads, os.cpu_count() or 1, len(counts)))

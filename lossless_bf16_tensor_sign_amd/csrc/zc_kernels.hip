@@ -70,7 +70,7 @@ constexpr int kLutBits = ZC_T1_LUT_BITS;          // first decode level (byte en
 constexpr int kTailBits = ZC_T1_TAIL_BITS;        // second level
 constexpr int kLutRaw = 1 << kLutBits;            // raw-mode byte entries follow
 constexpr uint32_t kSpinLimit = 1u << 14;          // look-back polls before recomputing
-constexpr uint32_t kPollLanes = 16;                // predecessors read per look-back poll
+constexpr uint32_t kPollLanes = 12;                // predecessors read per look-back poll
 
 // Compress workspace: a header, then one 8-byte look-back status word per
 // tile, one per 64-byte line (a tile's status is written through to
@@ -383,26 +383,35 @@ __device__ inline void load_tile(const TileCtx& x, uint4 (&v)[kQSteps])
 {
     const uint32_t k0 = x.wave * kQSteps;
     const char* sbase = reinterpret_cast<const char*>(x.src + x.base) + k0 * 1024 + x.lane * 16;
+    if (FULL) {
+#pragma unroll
+        for (int k = 0; k < kQSteps; ++k)
+            v[k] = ld_nt4(sbase + k * 1024);
+        return;
+    }
+    // every segment of 8 values wholly inside the chunk is one load when
+    // the chunk is 16-byte aligned; these are all issued before the ragged
+    // end (or an unaligned chunk) is read value by value
+    const bool aligned = (reinterpret_cast<uintptr_t>(x.src) & 15) == 0;
 #pragma unroll
     for (int k = 0; k < kQSteps; ++k) {
-        if (FULL) {
+        const uint32_t i0 = x.base + (k0 + k) * 512 + x.lane * 8;
+        v[k] = make_uint4(0, 0, 0, 0);
+        if (aligned && i0 + 8 <= x.n)
             v[k] = ld_nt4(sbase + k * 1024);
-        } else {
-            // a segment of 8 values wholly inside the chunk at a 16-byte
-            // aligned address is one load; the ragged end value by value
-            const uint32_t i0 = x.base + (k0 + k) * 512 + x.lane * 8;
-            if (i0 + 8 <= x.n && (reinterpret_cast<uintptr_t>(x.src + i0) & 15) == 0) {
-                v[k] = ld_nt4(x.src + i0);
-            } else {
-                uint32_t w[8];
+    }
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    w[j] = (i0 + j < x.n) ? x.src[i0 + j] : 0u;
-                v[k].x = w[0] | (w[1] << 16);
-                v[k].y = w[2] | (w[3] << 16);
-                v[k].z = w[4] | (w[5] << 16);
-                v[k].w = w[6] | (w[7] << 16);
-            }
+    for (int k = 0; k < kQSteps; ++k) {
+        const uint32_t i0 = x.base + (k0 + k) * 512 + x.lane * 8;
+        if (!(aligned && i0 + 8 <= x.n) && i0 < x.n) {
+            uint32_t w[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                w[j] = (i0 + j < x.n) ? x.src[i0 + j] : 0u;
+            v[k].x = w[0] | (w[1] << 16);
+            v[k].y = w[2] | (w[3] << 16);
+            v[k].z = w[4] | (w[5] << 16);
+            v[k].w = w[6] | (w[7] << 16);
         }
     }
 }
@@ -477,8 +486,8 @@ __device__ inline void look_back_publish(uint64_t* __restrict__ status, uint32_t
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One poll of the look-back window: the status words of the 16 tiles below
-// `top` (lane l reads tile top - l), zero where they belong to no
+// One poll of the look-back window: the status words of the kPollLanes
+// tiles below `top` (lane l reads tile top - l), zero where they belong to no
 // predecessor.
 __device__ inline uint64_t look_back_poll(const uint64_t* __restrict__ status, int64_t top,
                                           uint32_t first, uint32_t lane, uint32_t epoch)
@@ -619,7 +628,11 @@ __device__ __forceinline__ void emit_quarter(uint32_t* __restrict__ s, const Enc
     for (int k = 0; k < kQSteps; ++k) {
         const uint32_t d4[2] = {dd[k][0], dd[k][1]};
         const bool esc_here = coded && (((d4[0] | d4[1]) & 0xF0F0F0F0u) != 0);
-        if (FULL && __ballot(esc_here) == 0) {
+        // in a partial tile a thread's step is whole, absent (no member in
+        // the tile: it emits nothing) or, at the ragged end, in between
+        const bool absent = !FULL && static_cast<uint32_t>(k * 8) >= nv;
+        const bool ragged = !FULL && !absent && static_cast<uint32_t>(k * 8 + 8) > nv;
+        if (__ballot((esc_here && !absent) || ragged) == 0) {
             // every d of the step's coded lanes is below 16, so two members
             // index one pair entry: d0 | d1 << 4 is read off the packed
             // bytes as (w | w >> 4)
@@ -636,6 +649,10 @@ __device__ __forceinline__ void emit_quarter(uint32_t* __restrict__ s, const Enc
                     c23 = __builtin_amdgcn_perm(0u, e4, 0x0c0c0203u);
                     l01 = 16;
                     l23 = 16;
+                }
+                if (!FULL && absent) {
+                    c01 = c23 = 0;
+                    l01 = l23 = 0;
                 }
                 if (__ballot(l01 + l23 > 32u) == 0) {
                     emit_bits(s, acc, nacc, wi, (c01 << l23) | c23, l01 + l23);
@@ -801,6 +818,12 @@ __device__ __forceinline__ void compress_tile_back(const TileCtx& x, uint32_t (&
     // 5. wave 0: the tile's offset, the stream, the index arrays
     const uint32_t toff_w = look_back_resolve(status, x.item, x.t, x.first, lane, epoch, x.src,
                                               x.n, sh.tb.len, spin_limit);
+    // the inclusive prefix goes out at once: later tiles stop their walks
+    // at it instead of summing further back
+    if (x.t != 0 && lane == 0)
+        __hip_atomic_store(&status[x.item * kStatusStride],
+                           status_word(epoch, kFlagInc, toff_w + tile_words), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t toff = toff_w * 4, tile_bytes = tile_words * 4;
     // stores never leave the chunk's bound, whatever the offsets say (a
     // correct stream always fits; this only keeps a fault impossible)
@@ -818,17 +841,11 @@ __device__ __forceinline__ void compress_tile_back(const TileCtx& x, uint32_t (&
                 gstream[r0 + i * kLanes + lane] = v[i];
     }
     write_tile_index(x, toff, tile_bytes, emax, glen, comp_sizes);
-    // the inclusive prefix is published after the stores: published earlier,
-    // the store loop waited for that device-coherent write to complete
-    if (x.t != 0 && lane == 0)
-        __hip_atomic_store(&status[x.item * kStatusStride],
-                           status_word(epoch, kFlagInc, toff_w + tile_words), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Tiles that are partial (a chunk's last tile) or unaligned: kept out of
-// line so that their register needs do not constrain the full-tile path.
-__device__ __attribute__((noinline)) void compress_tile_partial(
+// Tiles that are partial (a chunk's last tile) or unaligned: the same
+// steps with the members past the chunk's end masked off.
+__device__ __forceinline__ void compress_tile_partial(
     TileCtx x, int64_t* __restrict__ comp_sizes, uint64_t* __restrict__ status,
     EncShared* sh, uint32_t epoch, uint32_t spin_limit)
 {
@@ -1060,20 +1077,25 @@ __device__ inline void put_values(uint16_t* __restrict__ dst, const uint8_t* __r
                                   uint32_t n, uint32_t i0, uint2 r, const uint32_t (&e8)[8],
                                   bool vec_out)
 {
-    // a partial tile takes the vector form for segments of 8 values wholly
-    // inside the chunk whose output is 16-byte aligned (the raw bytes are
-    // 8-byte aligned: stream slots, R and i0 are)
+    // in a partial tile, r holds the segment's sign+mantissa bytes when its
+    // 8 values lie wholly inside the chunk; they take the vector form when
+    // the output is 16-byte aligned, and the ragged end goes value by value
+    const bool whole = FULL || i0 + 8 <= n;
     const bool vec = FULL ? vec_out
-                          : (i0 + 8 <= n && (reinterpret_cast<uintptr_t>(dst + i0) & 15) == 0);
+                          : (whole && (reinterpret_cast<uintptr_t>(dst + i0) & 15) == 0);
     if (vec) {
-        if (!FULL)
-            r = ld_nt2(rsrc + i0);
         uint4 o;
         o.x = (__builtin_amdgcn_perm(r.x, r.x, 0x01010000u) & 0x807F807Fu) | (e8[0] << 7) | (e8[1] << 23);
         o.y = (__builtin_amdgcn_perm(r.x, r.x, 0x03030202u) & 0x807F807Fu) | (e8[2] << 7) | (e8[3] << 23);
         o.z = (__builtin_amdgcn_perm(r.y, r.y, 0x01010000u) & 0x807F807Fu) | (e8[4] << 7) | (e8[5] << 23);
         o.w = (__builtin_amdgcn_perm(r.y, r.y, 0x03030202u) & 0x807F807Fu) | (e8[6] << 7) | (e8[7] << 23);
         st_nt4(dst + i0, o);
+    } else if (whole) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t b = ((j < 4 ? r.x : r.y) >> (8 * (j & 3))) & 0xFFu;
+            dst[i0 + j] = static_cast<uint16_t>(((b & 0x80u) << 8) | ((e8[j] & 0xFF) << 7) | (b & 0x7Fu));
+        }
     } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -1119,11 +1141,16 @@ __device__ __forceinline__ void decode_group(const Win& win, const uint8_t* __re
     // flight and each wait leaves the younger loads and stores outstanding.
     constexpr int kRing = 1;
     static_assert(kSteps % kRing == 0, "whole rounds of the prefetch ring");
+    // (in a partial tile, only segments wholly inside the chunk are read)
     const uint2* rsrc2 = reinterpret_cast<const uint2*>(rsrc + base) + lane;
+    auto raw_at = [&](int k) {
+        return (FULL || base + k * 512 + lane * 8 + 8 <= n) ? ld_nt2(rsrc2 + k * 64)
+                                                            : make_uint2(0, 0);
+    };
     uint2 ring[kRing];
 #pragma unroll
     for (int j = 0; j < kRing; ++j)
-        ring[j] = FULL ? ld_nt2(rsrc2 + j * 64) : make_uint2(0, 0);
+        ring[j] = raw_at(j);
 #pragma unroll 1
     for (int k0 = 0; k0 < kSteps; k0 += kRing)
 #pragma unroll
@@ -1194,8 +1221,8 @@ __device__ __forceinline__ void decode_group(const Win& win, const uint8_t* __re
             }
         }
         put_values<FULL>(dst, rsrc, n, base + k * 512 + lane * 8, ring[kj], e8, vec_out);
-        if (FULL)   // the last round reloads the last row (in bounds, unused)
-            ring[kj] = ld_nt2(rsrc2 + min(k + kRing, kSteps - 1) * 64);
+        // the last round reloads the last row (in bounds, unused)
+        ring[kj] = raw_at(min(k + kRing, kSteps - 1));
     }
 }
 
@@ -1409,8 +1436,8 @@ __device__ __forceinline__ void decompress_tile(const uint8_t* __restrict__ src,
 }
 
 // A chunk's last, partial tile, or any tile of an output that is not 16-byte
-// aligned, kept out of line (see compress_tile_partial).
-__device__ __attribute__((noinline)) void decompress_tile_partial(
+// aligned: the same steps with the values past the chunk's end masked off.
+__device__ __forceinline__ void decompress_tile_partial(
     const uint8_t* __restrict__ src, uint16_t* __restrict__ dst, int32_t* __restrict__ status,
     int c, uint32_t n, uint32_t t, uint64_t bavail, uint32_t lane, uint32_t* __restrict__ s,
     const uint8_t* __restrict__ s_lut8, const uint16_t* __restrict__ s_tail,

@@ -13,3 +13,12 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_per_config_rejects_the_headline_workload():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "2",
+                        "--per-config", "1,2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "--per-config" in r.stderr
+    assert r.stdout == ""
