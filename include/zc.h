@@ -280,10 +280,17 @@ int zc_decompress_dev(const void* d_in, size_t in_bytes,
  *   d_out       device fp32[n], 16-byte aligned
  *   d_status    device int32, 0 on entry; as for zc_decompress.  If it is
  *               nonzero after the stream has run, d_out is undefined.
- *   d_scratch   device, 16-byte aligned, scratch_bytes >= 2 n num_chunks:
- *               the decoded bf16 contributions are staged there (stream c at
- *               element offset c n); caller-owned, contents undefined after
- *   stream      hipStream_t; both launches (decode, then sum) are queued on it
+ *   d_scratch   device, 16-byte aligned, scratch_bytes >=
+ *               zc_reduce_scratch_bytes(n, num_chunks): the decoded bf16
+ *               contributions are staged there one slab at a time;
+ *               caller-owned, contents undefined after
+ *   stream      hipStream_t; every launch (per slab: decode, then sum) is
+ *               queued on it
+ * The shard is processed in slabs of whole 8192-value tiles: each slab of
+ * every stream is decoded into the scratch buffer and summed before the next
+ * slab is decoded, so the staged values (about 128 MiB per slab over all
+ * streams) are read back while they are still in the device's 256 MB
+ * last-level cache.
  * Returns ZC_OK once queued; ZC_EINVAL for a bad argument, ZC_ENOSPC for a
  * short scratch buffer (nothing queued), ZC_EHIP if a launch fails.
  */
@@ -291,6 +298,17 @@ int zc_decompress_reduce(const void* d_in, size_t in_bytes,
                          const int64_t* in_offsets, int64_t n,
                          int32_t num_chunks, float* d_out, int32_t* d_status,
                          void* d_scratch, size_t scratch_bytes, void* stream);
+
+/*
+ * Scratch bytes that zc_decompress_reduce and zc_decompress_reduce_bf16 need
+ * for num_chunks streams of n values: 2 num_chunks s, where s (values per
+ * stream per slab) is n rounded up to 8 when one slab holds the whole shard,
+ * else the slab's whole tiles.  At most about 128 MiB whatever n (more only
+ * when 2 num_chunks 8192 bytes, one tile per stream, exceed it); 0 for
+ * n == 0 or an argument out of range.  A property of this library's slab
+ * size, not of the stream format.
+ */
+size_t zc_reduce_scratch_bytes(int64_t n, int32_t num_chunks);
 
 /*
  * zc_decompress_reduce delivering bf16: the same chunk-order fp32 sums,

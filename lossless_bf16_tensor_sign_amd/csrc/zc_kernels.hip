@@ -133,6 +133,7 @@ struct ChunkTable {
     int32_t chunk_base;            // index of the launch's first chunk in the call (status reports)
     uint32_t nitems;
     uint32_t spin_limit;           // compress: look-back polls before recomputing
+    uint32_t tile0;                // decompress: index of each chunk's first tile in the launch
     uint32_t item_begin[kMaxChunks + 1];
     uint32_t n[kMaxChunks];
     uint64_t voff[kMaxChunks];     // value offset of the chunk (bf16 side)
@@ -1483,7 +1484,7 @@ __device__ __forceinline__ void decompress_body(const uint8_t* __restrict__ in,
     if (live) {
         c = find_chunk(tab, item);
         n = tab.n[c];
-        t = item - tab.item_begin[c];
+        t = tab.tile0 + item - tab.item_begin[c];
         const Geom G = geometry(n);
         if (n != 0 && G.X <= tab.bavail[c])
             meta = load_meta(in + tab.boff[c], G, t, lane);
@@ -1593,15 +1594,15 @@ __device__ inline uint32_t f32_to_bf16_rne(float f)
 
 // Receive side of a reduce-scatter (pith.science, Figure 5: zipccl
 // ReduceScatter): num_chunks decoded contributions of n bf16 values each
-// (contribution c at x + c n) summed element by element in fp32, in chunk
-// order, from +0; BF16OUT rounds each sum once to bf16 (to nearest even).
-// Each thread owns 8 consecutive elements; rows are read with 16-byte
-// nontemporal loads, 8 contributions in flight at a time, and the sums are
-// added strictly in chunk order.
+// (contribution c at x + c stride) summed element by element in fp32, in
+// chunk order, from +0; BF16OUT rounds each sum once to bf16 (to nearest
+// even).  Each thread owns 8 consecutive elements; rows are read with
+// 16-byte nontemporal loads, 8 contributions in flight at a time, and the
+// sums are added strictly in chunk order.
 template <bool BF16OUT>
 __global__ __launch_bounds__(kBlock)
-void zc_reduce_kernel(const uint16_t* __restrict__ x, uint64_t n, int32_t num_chunks,
-                      void* __restrict__ out)
+void zc_reduce_kernel(const uint16_t* __restrict__ x, uint64_t n, uint64_t stride,
+                      int32_t num_chunks, void* __restrict__ out)
 {
     const uint64_t i0 = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) * 8;
     if (i0 >= n)
@@ -1610,20 +1611,20 @@ void zc_reduce_kernel(const uint16_t* __restrict__ x, uint64_t n, int32_t num_ch
 #pragma unroll
     for (int j = 0; j < 8; ++j)
         acc[j] = 0.0f;
-    if ((n & 7) == 0) {
+    if (i0 + 8 <= n && (stride & 7) == 0) {
         const uint16_t* p = x + i0;
         int32_t c = 0;
         for (; c + 8 <= num_chunks; c += 8) {
             uint4 v[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-                v[u] = ld_nt4(p + static_cast<uint64_t>(c + u) * n);
+                v[u] = ld_nt4(p + static_cast<uint64_t>(c + u) * stride);
 #pragma unroll
             for (int u = 0; u < 8; ++u)
                 add8(acc, v[u]);
         }
         for (; c < num_chunks; ++c)
-            add8(acc, ld_nt4(p + static_cast<uint64_t>(c) * n));
+            add8(acc, ld_nt4(p + static_cast<uint64_t>(c) * stride));
         if (BF16OUT) {
             uint32_t h[8];
 #pragma unroll
@@ -1643,7 +1644,7 @@ void zc_reduce_kernel(const uint16_t* __restrict__ x, uint64_t n, int32_t num_ch
         for (int j = 0; j < 8 && i0 + j < n; ++j) {
             float a = 0.0f;
             for (int32_t c = 0; c < num_chunks; ++c)
-                a = a + bf16_lo(x[static_cast<uint64_t>(c) * n + i0 + j]);
+                a = a + bf16_lo(x[static_cast<uint64_t>(c) * stride + i0 + j]);
             if (BF16OUT)
                 static_cast<uint16_t*>(out)[i0 + j] = static_cast<uint16_t>(f32_to_bf16_rne(a));
             else
@@ -1751,6 +1752,7 @@ void zc_plan_kernel(const int64_t* __restrict__ counts, int32_t num_chunks, int3
         tab->chunk_base = c0;
         tab->nitems = bad ? 0u : items;
         tab->spin_limit = spin_limit;
+        tab->tile0 = 0;
         if (decode && bad && status)
             atomicCAS(status, 0, (ZC_REASON_SIZE << 24) | (c0 & 0xFFFFFF));
     }
@@ -1997,11 +1999,34 @@ uint64_t dev_tables_offset(int64_t total, int32_t num_chunks)
 
 namespace {
 
+// Staged bytes of one slab of zc_decompress_reduce, over all contributions:
+// small enough to stay in the 256 MB last-level cache while it is summed,
+// large enough that a slab's decode fills the device.
+constexpr uint64_t kReduceSlabBytes = 128ull << 20;
+
+// Values per contribution in one slab (also the contributions' spacing in
+// the scratch buffer): whole tiles, or all n values rounded up to 8 when
+// they fit in one slab.
+uint64_t reduce_stride(uint64_t n, int32_t num_chunks)
+{
+    const uint64_t c = num_chunks > 0 ? static_cast<uint64_t>(num_chunks) : 1u;
+    const uint64_t tiles = std::max<uint64_t>(1, kReduceSlabBytes / (2 * c) / kTile);
+    return std::min<uint64_t>(tiles * kTile, (n + 7) & ~7ull);
+}
+
+// A slab of a decode: tiles tile0 .. tile0 + tiles - 1 of every chunk, value
+// i of chunk c written at c stride + i - tile0 kTile of the output.
+struct Slab {
+    uint32_t tile0, tiles;
+    uint64_t stride;
+};
+
 // zc_decompress; reported chunk indices start at chunk_base (zc_pipeline
 // decodes group by group and reports indices of the whole call).
 int decompress_chunks(const void* d_in, size_t in_bytes, const int64_t* in_offsets,
                       const int64_t* counts, int32_t num_chunks, uint16_t* d_out,
-                      int32_t* d_status, void* stream, int32_t chunk_base)
+                      int32_t* d_status, void* stream, int32_t chunk_base,
+                      const Slab* slab = nullptr)
 {
     const Counts k = check_counts(counts, num_chunks);
     if (!k.ok)
@@ -2033,12 +2058,23 @@ int decompress_chunks(const void* d_in, size_t in_bytes, const int64_t* in_offse
             tab.voff[m] = voff;
             tab.boff[m] = static_cast<uint64_t>(off);
             tab.bavail[m] = in_bytes - static_cast<uint64_t>(off);
-            items += static_cast<uint32_t>(T ? T : 1);
+            if (slab) {
+                // tiles tile0 .. tile0 + tiles - 1 of every chunk (all of n
+                // values); value i of chunk c lands at c stride + i - s0,
+                // an offset that wraps below zero only before the slab's
+                // first value, which is never written
+                tab.voff[m] = static_cast<uint64_t>(c) * slab->stride -
+                              static_cast<uint64_t>(slab->tile0) * kTile;
+                items += slab->tiles;
+            } else {
+                items += static_cast<uint32_t>(T ? T : 1);
+            }
             voff += n;
             slot += align256(chunk_bound(n));
         }
         tab.nchunks = m;
         tab.chunk_base = chunk_base + c0;
+        tab.tile0 = slab ? slab->tile0 : 0u;
         tab.nitems = items;
         tab.item_begin[m] = items;
         hipLaunchKernelGGL(zc_decompress_kernel, dim3((items + kWaves - 1) / kWaves), dim3(kBlock), 0, s, in,
@@ -2049,8 +2085,10 @@ int decompress_chunks(const void* d_in, size_t in_bytes, const int64_t* in_offse
     return ZC_OK;
 }
 
-// Decode num_chunks streams of n values into the staging buffer, then sum
-// them (fp32 output, or bf16 when `bf16`).
+// Decode num_chunks streams of n values and sum them (fp32 output, or bf16
+// when `bf16`), slab by slab: each slab is a run of whole tiles of every
+// stream, decoded into the scratch buffer (contribution c at c stride) and
+// summed while it is still in the device's last-level cache.
 int decompress_reduce(const void* d_in, size_t in_bytes, const int64_t* in_offsets, int64_t n,
                       int32_t num_chunks, void* d_out, bool bf16, int32_t* d_status,
                       void* d_scratch, size_t scratch_bytes, void* stream)
@@ -2063,26 +2101,38 @@ int decompress_reduce(const void* d_in, size_t in_bytes, const int64_t* in_offse
         return ZC_EINVAL;
     if ((reinterpret_cast<uintptr_t>(d_out) & 15) || (reinterpret_cast<uintptr_t>(d_scratch) & 15))
         return ZC_EINVAL;
-    if (scratch_bytes < 2ull * static_cast<uint64_t>(n) * static_cast<uint64_t>(num_chunks))
+    const uint64_t stride = reduce_stride(static_cast<uint64_t>(n), num_chunks);
+    if (scratch_bytes < 2ull * stride * static_cast<uint64_t>(num_chunks))
         return ZC_ENOSPC;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (num_chunks > 0) {
-        std::vector<int64_t> counts(static_cast<size_t>(num_chunks), n);
-        const int r = decompress_chunks(d_in, in_bytes, in_offsets, counts.data(), num_chunks,
-                                        static_cast<uint16_t*>(d_scratch), d_status, stream, 0);
-        if (r != ZC_OK)
-            return r;
-    }
-    const uint64_t threads = (static_cast<uint64_t>(n) + 7) / 8;
-    const dim3 grid(static_cast<uint32_t>((threads + kBlock - 1) / kBlock));
+    const std::vector<int64_t> counts(static_cast<size_t>(num_chunks), n);
     const uint16_t* x = static_cast<const uint16_t*>(d_scratch);
-    if (bf16)
-        hipLaunchKernelGGL(zc_reduce_kernel<true>, grid, dim3(kBlock), 0, s, x,
-                           static_cast<uint64_t>(n), num_chunks, d_out);
-    else
-        hipLaunchKernelGGL(zc_reduce_kernel<false>, grid, dim3(kBlock), 0, s, x,
-                           static_cast<uint64_t>(n), num_chunks, d_out);
-    return hipGetLastError() == hipSuccess ? ZC_OK : ZC_EHIP;
+    const uint64_t T = (static_cast<uint64_t>(n) + kTile - 1) / kTile;
+    const uint64_t slab_tiles = (stride + kTile - 1) / kTile;
+    for (uint64_t t0 = 0; t0 < T; t0 += slab_tiles) {
+        const uint64_t s0 = t0 * kTile;
+        const uint64_t len = std::min<uint64_t>(static_cast<uint64_t>(n) - s0, stride);
+        if (num_chunks > 0) {
+            const Slab slab{static_cast<uint32_t>(t0),
+                            static_cast<uint32_t>(std::min<uint64_t>(slab_tiles, T - t0)), stride};
+            const int r = decompress_chunks(d_in, in_bytes, in_offsets, counts.data(), num_chunks,
+                                            static_cast<uint16_t*>(d_scratch), d_status, stream, 0,
+                                            &slab);
+            if (r != ZC_OK)
+                return r;
+        }
+        const uint64_t threads = (len + 7) / 8;
+        const dim3 grid(static_cast<uint32_t>((threads + kBlock - 1) / kBlock));
+        if (bf16)
+            hipLaunchKernelGGL(zc_reduce_kernel<true>, grid, dim3(kBlock), 0, s, x, len, stride,
+                               num_chunks, static_cast<void*>(static_cast<uint16_t*>(d_out) + s0));
+        else
+            hipLaunchKernelGGL(zc_reduce_kernel<false>, grid, dim3(kBlock), 0, s, x, len, stride,
+                               num_chunks, static_cast<void*>(static_cast<float*>(d_out) + s0));
+        if (hipGetLastError() != hipSuccess)
+            return ZC_EHIP;
+    }
+    return ZC_OK;
 }
 
 }  // namespace
@@ -2315,6 +2365,14 @@ int zc_estimate(const uint16_t* d_in, const int64_t* d_counts, int32_t num_chunk
                        static_cast<hipStream_t>(stream), d_in, d_counts, num_chunks, total_values,
                        samples_per_chunk, d_est);
     return hipGetLastError() == hipSuccess ? ZC_OK : ZC_EHIP;
+}
+
+size_t zc_reduce_scratch_bytes(int64_t n, int32_t num_chunks)
+{
+    if (n < 0 || n > ZC_MAX_CHUNK_VALUES || num_chunks < 0 || num_chunks > ZC_MAX_CHUNKS)
+        return 0;
+    return static_cast<size_t>(2ull * reduce_stride(static_cast<uint64_t>(n), num_chunks) *
+                               static_cast<uint64_t>(num_chunks));
 }
 
 int zc_decompress_reduce(const void* d_in, size_t in_bytes, const int64_t* in_offsets,

@@ -89,6 +89,8 @@ def lib():
                                            ct.c_int32, ct.c_void_p, ct.c_void_p, ct.c_void_p,
                                            ct.c_size_t, ct.c_void_p]
         L.zc_decompress_reduce.restype = ct.c_int
+        L.zc_reduce_scratch_bytes.argtypes = [ct.c_int64, ct.c_int32]
+        L.zc_reduce_scratch_bytes.restype = ct.c_size_t
         L.zc_decompress_reduce_bf16.argtypes = L.zc_decompress_reduce.argtypes
         L.zc_decompress_reduce_bf16.restype = ct.c_int
         L.zc_pipeline.argtypes = [ct.c_void_p, i64p, ct.c_int32, ct.c_int32, ct.c_void_p,
@@ -242,6 +244,11 @@ def zc_decompress_dev(d_in, d_counts, total_values, d_out, d_status, d_ws, d_in_
                                        _ptr(d_status), _ptr(d_ws), wsb, _stream(stream)))
 
 
+def zc_reduce_scratch_bytes(n, num_chunks) -> int:
+    """Scratch bytes zc_decompress_reduce needs (0 for n == 0 or a bad argument)."""
+    return int(lib().zc_reduce_scratch_bytes(int(n), int(num_chunks)))
+
+
 def zc_decompress_reduce(d_in, n, num_chunks, d_out, d_status, d_scratch, in_offsets=None,
                          stream=None, in_bytes=None, scratch_bytes=None, bf16=False) -> int:
     """Queue decode of num_chunks streams of n values and their fp32 sum
@@ -379,8 +386,8 @@ def decompress_reduce(buf, n, num_chunks, in_offsets=None, stream=None, check=Tr
         out = torch.empty(max(int(n), 8), dtype=torch.int16 if bf16 else torch.float32,
                           device=dev)
         status = torch.zeros(1, dtype=torch.int32, device=dev)
-        scratch = torch.empty(max(2 * int(n) * int(num_chunks), 16), dtype=torch.uint8,
-                              device=dev)
+        scratch = torch.empty(max(zc_reduce_scratch_bytes(n, num_chunks), 16),
+                              dtype=torch.uint8, device=dev)
         r = zc_decompress_reduce(buf, n, num_chunks, out, status, scratch,
                                  in_offsets=in_offsets, stream=stream, bf16=bf16)
         if r != ZC_OK:

@@ -61,6 +61,27 @@ def test_workspace_bytes():
     assert zc.zc_workspace_bytes([8192 * 5] * 2) == head + slot * 10
 
 
+def test_reduce_scratch_bytes():
+    # one slab holds the whole shard: every contribution at its length
+    # rounded up to 8 values
+    assert zc.zc_reduce_scratch_bytes(4096, 4) == 2 * 4096 * 4
+    assert zc.zc_reduce_scratch_bytes(20003, 8) == 2 * 20008 * 8
+    assert zc.zc_reduce_scratch_bytes(1, 5) == 2 * 8 * 5
+    # otherwise one slab of whole 8192-value tiles per stream, about
+    # 128 MiB over all streams, whatever the shard length
+    slab = 128 << 20
+    for n, c in [(1 << 22, 64), (1 << 26, 64), ((1 << 22) + 77, 64), (1 << 25, 3),
+                 (1 << 27, 1), (1 << 22, 4096)]:
+        b = zc.zc_reduce_scratch_bytes(n, c)
+        per = b // (2 * c)
+        assert b == 2 * c * per and per % 8192 == 0 and 8192 <= per < n, (n, c)
+        assert b <= max(slab, 2 * c * 8192), (n, c)
+    assert zc.zc_reduce_scratch_bytes(1 << 22, 64) == slab
+    assert zc.zc_reduce_scratch_bytes(0, 4) == 0
+    assert zc.zc_reduce_scratch_bytes(-1, 4) == 0
+    assert zc.zc_reduce_scratch_bytes(10, -1) == 0
+
+
 def test_code_table_matches_oracle(oracle):
     L, C, P = zc.zc_code_table(1)
     p, l, c = oracle.table(1)

@@ -111,9 +111,11 @@ def test_reduce_argument_errors():
     buf, _ = zc.compress(to_dev(w), [n] * c)
     out = torch.empty(n + 4, dtype=torch.float32, device=DEV)
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
-    scratch = torch.empty(2 * n * c, dtype=torch.uint8, device=DEV)
+    need = zc.zc_reduce_scratch_bytes(n, c)
+    assert need == 2 * n * c                 # one slab holds this shard
+    scratch = torch.empty(need, dtype=torch.uint8, device=DEV)
     assert zc.zc_decompress_reduce(buf, n, c, out, status, scratch,
-                                   scratch_bytes=2 * n * c - 1) == zc.ZC_ENOSPC
+                                   scratch_bytes=need - 1) == zc.ZC_ENOSPC
     assert zc.zc_decompress_reduce(buf, n, c, out[1:], status, scratch) == zc.ZC_EINVAL
     assert zc.zc_decompress_reduce(buf, -1, c, out, status, scratch) == zc.ZC_EINVAL
     assert zc.zc_decompress_reduce(buf, n, -1, out, status, scratch) == zc.ZC_EINVAL
@@ -133,6 +135,39 @@ def test_reduce_reports_corrupt_stream(oracle):
     torch.cuda.synchronize()
     st = int(status.item())
     assert st >> 24 == 1 and (st & 0xFFFFFF) == 2, hex(st)
+
+
+def test_reduce_ragged_slabs(oracle):
+    # 64 streams of a shard longer than one slab (1 Mi values per stream at
+    # 64 streams), ending in a partial tile: two slabs, the second ragged
+    c = 64
+    n = (1 << 20) + 3 * 8192 + 77
+    assert zc.zc_reduce_scratch_bytes(n, c) == 2 * c * (1 << 20)
+    w = special_mix(n * c, 77)
+    say("reduce ragged slabs n=%d chunks=%d" % (n, c))
+    st, got = gpu_reduce(w, n, c)
+    assert st == 0, "status %#x" % st
+    same_f32(got, oracle.reduce_bf16_f32(w, n, c))
+
+
+def test_reduce_reports_corrupt_stream_in_a_later_slab(oracle):
+    # a broken tile index entry in the second slab of stream 5
+    c = 64
+    n = (1 << 20) + 4 * 8192
+    w = synth.gaussian_bits(n * c, 0.02, 9)
+    buf, sizes = zc.compress(to_dev(w), [n] * c)
+    torch.cuda.synchronize()
+    hb = buf.cpu().numpy().copy()
+    off, _ = oracle.slot_offsets([n] * c)
+    T = (n + 8191) // 8192
+    t = T - 1                                # the last tile (second slab)
+    p = off[5] + 32 + 4 * t                  # its offset in the tile index
+    hb[p:p + 4] = np.frombuffer(np.uint32(0xFFFFFF00).tobytes(), np.uint8)
+    say("reduce corrupt tile %d of stream 5" % t)
+    out, status = zc.decompress_reduce(torch.from_numpy(hb).to(DEV), n, c, check=False)
+    torch.cuda.synchronize()
+    st = int(status.item())
+    assert st != 0 and (st & 0xFFFFFF) == 5, hex(st)
 
 
 def test_reduce_full_size_gradient_buffer(oracle):
