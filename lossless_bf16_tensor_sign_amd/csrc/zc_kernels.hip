@@ -273,6 +273,11 @@ __device__ inline uint2 ld_nt2(const void* p)
     return make_uint2(v.x, v.y);
 }
 __device__ inline uint32_t ld_nt1(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+// A plain (cached) 8-byte load.  The sign+mantissa section starts 16-byte
+// aligned, so its 512-byte rows straddle 128-byte lines; where a row is read
+// in two halves at different times, the line they share can still be in L2
+// for the second half.
+__device__ inline uint2 ld2(const void* p) { return *reinterpret_cast<const uint2*>(p); }
 __device__ inline void st_nt4(void* p, uint4 v)
 {
     __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(p));
@@ -1279,7 +1284,7 @@ __device__ inline void decode_all_raw(const uint32_t* __restrict__ gstream,
                     st.seen_max = max(st.seen_max, e8[j]);
                     st.raw_coded += s_len[(emax - e8[j]) & 0xFF];
                 }
-                put_values<true>(dst, rsrc, n, base + k * 512 + lane * 8, ld_nt2(rsrc2 + k * 64), e8, vec_out);
+                put_values<true>(dst, rsrc, n, base + k * 512 + lane * 8, ld2(rsrc2 + k * 64), e8, vec_out);
             }
             st.pos += 1024;
         }
