@@ -187,24 +187,6 @@ __device__ inline uint32_t wave_excl_scan(uint32_t x, uint32_t lane, uint32_t* t
     return incl - x;
 }
 
-// Inclusive prefix sum over the wave with DPP row operations (no LDS round
-// trip, no per-lane address): shifts by 1, 2, 4 and 8 lanes inside each row
-// of 16 (out-of-row sources read 0), then row 0's last lane is added to row 1
-// and row 2's to row 3, then lane 31 to rows 2 and 3.  Returns the exclusive
-// prefix; *total is lane 63's sum, read into a scalar register.
-__device__ inline uint32_t wave_excl_scan_dpp(uint32_t x, uint32_t* total)
-{
-    int v = static_cast<int>(x);
-    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
-    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
-    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
-    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
-    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
-    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
-    *total = static_cast<uint32_t>(__builtin_amdgcn_readlane(v, kLanes - 1));
-    return static_cast<uint32_t>(v) - x;
-}
-
 __device__ inline uint32_t wave_sum(uint32_t x)
 {
 #pragma unroll
