@@ -18,7 +18,8 @@ roofline.traffic is read from the committed counter summary of this workload
 the value recorded there; otherwise it is null.
 
 With the default workload, workloads 1, 3, 4 and 5 are then timed the same
-way (compress and decompress only) and reported under per_config.
+way (compress and decompress only, same warm-up and step counts) and
+reported under per_config.
 
 The oracle (plain C, test infrastructure) is timed on the host cores over the
 same workload for the cpu_baseline field.
@@ -315,7 +316,8 @@ def main():
                     help="comma-separated other workloads to time after the headline "
                          "one (compress and decompress only), reported under per_config; "
                          "default 1,3,4,5 for workload 2 and none otherwise; '' for none")
-    ap.add_argument("--per-config-steps", type=int, default=10)
+    ap.add_argument("--per-config-steps", type=int, default=None,
+                    help="timed steps per other workload (default: --steps, after --warmup)")
     args = ap.parse_args()
     if args.per_config is None:
         args.per_config = "1,3,4,5" if args.workload == 2 else ""
@@ -570,7 +572,7 @@ def main():
         for wl in others:
             log("per-config workload %d (%s)" % (wl, synth.NAMES[wl]))
             line["per_config"][synth.NAMES[wl]] = measure_workload(
-                wl, args.per_config_steps, 2, dev, stream, evict, ev)
+                wl, args.per_config_steps or args.steps, args.warmup, dev, stream, evict, ev)
 
     if not args.no_cpu_baseline:
         threads = max(1, min(args.cpu_threads, os.cpu_count() or 1, len(counts)))
