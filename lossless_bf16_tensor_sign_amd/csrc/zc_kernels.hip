@@ -651,8 +651,10 @@ __device__ __forceinline__ void emit_quarter(uint32_t* __restrict__ s, const Enc
             }
         } else {
             // escape step: each member's word from the escape table; the
-            // quad's words are combined in 32 bits, which is exact when they
-            // fit; otherwise they are looked up again, pair by pair
+            // quad's words are combined in 64 bits and go out in one append
+            // when they fit in 32 bits on every lane, else in two; a quad of
+            // more than 64 bits (three escapes) is looked up again, pair by
+            // pair
             auto member = [&](int u, uint32_t w, int jj, uint32_t& c, uint32_t& L) {
                 const uint32_t d = (w >> (8 * u)) & 0xFF;
                 uint32_t ent = tb.esc[d];
@@ -667,7 +669,8 @@ __device__ __forceinline__ void emit_quarter(uint32_t* __restrict__ s, const Enc
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const uint32_t w = d4[h];
-                uint32_t cq = 0, lq = 0;
+                uint64_t cq = 0;
+                uint32_t lq = 0;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     uint32_t c, L;
@@ -676,7 +679,13 @@ __device__ __forceinline__ void emit_quarter(uint32_t* __restrict__ s, const Enc
                     lq += L;
                 }
                 if (__ballot(lq > 32u) == 0) {
-                    emit_bits(s, acc, nacc, wi, cq, lq);
+                    emit_bits(s, acc, nacc, wi, lo32(cq), lq);
+                } else if (__ballot(lq > 64u) == 0) {
+                    // at most 64 bits on every lane: the bits above the low
+                    // 32 first, then the low 32
+                    const bool two = lq > 32u;
+                    emit_bits(s, acc, nacc, wi, hi32(cq), two ? lq - 32u : 0u);
+                    emit_bits(s, acc, nacc, wi, lo32(cq), two ? 32u : lq);
                 } else {
 #pragma unroll
                     for (int u = 0; u < 4; u += 2) {
