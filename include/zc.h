@@ -282,15 +282,15 @@ int zc_decompress_dev(const void* d_in, size_t in_bytes,
  *               nonzero after the stream has run, d_out is undefined.
  *   d_scratch   device, 16-byte aligned, scratch_bytes >=
  *               zc_reduce_scratch_bytes(n, num_chunks): the decoded bf16
- *               contributions are staged there one slab at a time;
+ *               contributions are staged there, one or two slabs at a time;
  *               caller-owned, contents undefined after
- *   stream      hipStream_t; every launch (per slab: decode, then sum) is
- *               queued on it
- * The shard is processed in slabs of whole 8192-value tiles: each slab of
- * every stream is decoded into the scratch buffer and summed before the next
- * slab is decoded, so the staged values (about 128 MiB per slab over all
- * streams) are read back while they are still in the device's 256 MB
- * last-level cache.
+ *   stream      hipStream_t; every launch is queued on it
+ * The shard is processed in slabs of whole 8192-value tiles, about 128 MiB
+ * of staged values per slab over all streams, so that a slab is summed
+ * while it is still in the device's 256 MB last-level cache.  With at most
+ * 64 streams and more than one slab, launch i decodes slab i into one of
+ * two slab buffers and sums slab i - 1 from the other; with more streams,
+ * each slab is decoded and then summed.
  * Returns ZC_OK once queued; ZC_EINVAL for a bad argument, ZC_ENOSPC for a
  * short scratch buffer (nothing queued), ZC_EHIP if a launch fails.
  */
@@ -301,12 +301,13 @@ int zc_decompress_reduce(const void* d_in, size_t in_bytes,
 
 /*
  * Scratch bytes that zc_decompress_reduce and zc_decompress_reduce_bf16 need
- * for num_chunks streams of n values: 2 num_chunks s, where s (values per
- * stream per slab) is n rounded up to 8 when one slab holds the whole shard,
- * else the slab's whole tiles.  At most about 128 MiB whatever n (more only
- * when 2 num_chunks 8192 bytes, one tile per stream, exceed it); 0 for
- * n == 0 or an argument out of range.  A property of this library's slab
- * size, not of the stream format.
+ * for num_chunks streams of n values: 2 num_chunks s per slab buffer, where
+ * s (values per stream per slab) is n rounded up to 8 when one slab holds
+ * the whole shard (one buffer), else the slab's whole tiles (two buffers
+ * for at most 64 streams, one for more).  At most about 256 MiB whatever n
+ * (more only when one tile per stream exceeds a slab); 0 for n == 0 or an
+ * argument out of range.  A property of this library's slab size, not of
+ * the stream format.
  */
 size_t zc_reduce_scratch_bytes(int64_t n, int32_t num_chunks);
 

@@ -1596,11 +1596,11 @@ __device__ inline uint32_t f32_to_bf16_rne(float f)
 // 16-byte nontemporal loads, 8 contributions in flight at a time, and the
 // sums are added strictly in chunk order.
 template <bool BF16OUT>
-__global__ __launch_bounds__(kBlock)
-void zc_reduce_kernel(const uint16_t* __restrict__ x, uint64_t n, uint64_t stride,
-                      int32_t num_chunks, void* __restrict__ out)
+__device__ __forceinline__ void reduce_body(const uint16_t* __restrict__ x, uint64_t n,
+                                            uint64_t stride, int32_t num_chunks,
+                                            void* __restrict__ out, uint32_t block)
 {
-    const uint64_t i0 = (static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x) * 8;
+    const uint64_t i0 = (static_cast<uint64_t>(block) * kBlock + threadIdx.x) * 8;
     if (i0 >= n)
         return;
     float acc[8];
@@ -1647,6 +1647,31 @@ void zc_reduce_kernel(const uint16_t* __restrict__ x, uint64_t n, uint64_t strid
                 static_cast<float*>(out)[i0 + j] = a;
         }
     }
+}
+
+template <bool BF16OUT>
+__global__ __launch_bounds__(kBlock)
+void zc_reduce_kernel(const uint16_t* __restrict__ x, uint64_t n, uint64_t stride,
+                      int32_t num_chunks, void* __restrict__ out)
+{
+    reduce_body<BF16OUT>(x, n, stride, num_chunks, out, blockIdx.x);
+}
+
+// One slab's decode and the previous slab's sum in one launch: the first
+// dec_blocks workgroups decode (as zc_decompress_kernel) into one slab
+// buffer, the rest sum the other (as zc_reduce_kernel).  The sum
+// workgroups come last in the grid, so they run while the decode drains.
+template <bool BF16OUT>
+__global__ __launch_bounds__(kBlock, kMinWavesDec)
+void zc_decode_sum_kernel(const uint8_t* __restrict__ in, uint16_t* __restrict__ dec,
+                          int32_t* __restrict__ status, ChunkTable tab, uint32_t dec_blocks,
+                          const uint16_t* __restrict__ x, uint64_t n, uint64_t stride,
+                          int32_t num_chunks, void* __restrict__ out)
+{
+    if (blockIdx.x < dec_blocks)
+        decompress_body(in, dec, status, tab);
+    else
+        reduce_body<BF16OUT>(x, n, stride, num_chunks, out, blockIdx.x - dec_blocks);
 }
 
 // ------------------------------------------------------------ device-resident split
@@ -1996,8 +2021,9 @@ uint64_t dev_tables_offset(int64_t total, int32_t num_chunks)
 namespace {
 
 // Staged bytes of one slab of zc_decompress_reduce, over all contributions:
-// small enough to stay in the 256 MB last-level cache while it is summed,
-// large enough that a slab's decode fills the device.
+// large enough that a slab's decode fills the device, and small enough that
+// two of them (one being decoded, one being summed) fit the 256 MB
+// last-level cache.
 constexpr uint64_t kReduceSlabBytes = 128ull << 20;
 
 // Values per contribution in one slab (also the contributions' spacing in
@@ -2008,6 +2034,20 @@ uint64_t reduce_stride(uint64_t n, int32_t num_chunks)
     const uint64_t c = num_chunks > 0 ? static_cast<uint64_t>(num_chunks) : 1u;
     const uint64_t tiles = std::max<uint64_t>(1, kReduceSlabBytes / (2 * c) / kTile);
     return std::min<uint64_t>(tiles * kTile, (n + 7) & ~7ull);
+}
+
+// More than one slab of at most 64 streams: each launch decodes one slab
+// and sums the one before, so two slab buffers alternate.
+bool reduce_pipelined(uint64_t n, int32_t num_chunks)
+{
+    return num_chunks > 0 && num_chunks <= kMaxChunks && n > reduce_stride(n, num_chunks);
+}
+
+// Scratch bytes of zc_decompress_reduce.
+uint64_t reduce_scratch(uint64_t n, int32_t num_chunks)
+{
+    return 2ull * reduce_stride(n, num_chunks) * static_cast<uint64_t>(num_chunks) *
+           (reduce_pipelined(n, num_chunks) ? 2u : 1u);
 }
 
 // A slab of a decode: tiles tile0 .. tile0 + tiles - 1 of every chunk, value
@@ -2083,8 +2123,11 @@ int decompress_chunks(const void* d_in, size_t in_bytes, const int64_t* in_offse
 
 // Decode num_chunks streams of n values and sum them (fp32 output, or bf16
 // when `bf16`), slab by slab: each slab is a run of whole tiles of every
-// stream, decoded into the scratch buffer (contribution c at c stride) and
-// summed while it is still in the device's last-level cache.
+// stream, decoded into a slab buffer (contribution c at c stride) and summed
+// while it is still in the device's last-level cache.  With up to 64
+// streams, launch i decodes slab i into buffer i % 2 and sums slab i - 1
+// from the other buffer (the sum's workgroups run as the decode drains);
+// with more, each slab is decoded (64 streams per launch) and then summed.
 int decompress_reduce(const void* d_in, size_t in_bytes, const int64_t* in_offsets, int64_t n,
                       int32_t num_chunks, void* d_out, bool bf16, int32_t* d_status,
                       void* d_scratch, size_t scratch_bytes, void* stream)
@@ -2098,13 +2141,72 @@ int decompress_reduce(const void* d_in, size_t in_bytes, const int64_t* in_offse
     if ((reinterpret_cast<uintptr_t>(d_out) & 15) || (reinterpret_cast<uintptr_t>(d_scratch) & 15))
         return ZC_EINVAL;
     const uint64_t stride = reduce_stride(static_cast<uint64_t>(n), num_chunks);
-    if (scratch_bytes < 2ull * stride * static_cast<uint64_t>(num_chunks))
+    const uint64_t T = (static_cast<uint64_t>(n) + kTile - 1) / kTile;
+    const uint64_t slab_tiles = (stride + kTile - 1) / kTile;
+    const uint64_t slabs = (T + slab_tiles - 1) / slab_tiles;
+    const uint64_t buf_values = stride * static_cast<uint64_t>(num_chunks);
+    if (scratch_bytes < reduce_scratch(static_cast<uint64_t>(n), num_chunks))
         return ZC_ENOSPC;
+    if (reduce_pipelined(static_cast<uint64_t>(n), num_chunks)) {
+        const uint8_t* in = static_cast<const uint8_t*>(d_in);
+        const uint64_t slot_bytes = align256(chunk_bound(static_cast<uint64_t>(n)));
+        for (int32_t c = 0; c < num_chunks; ++c) {
+            const int64_t off = in_offsets ? in_offsets[c] : static_cast<int64_t>(c * slot_bytes);
+            if (off < 0 || (off & 15) || static_cast<uint64_t>(off) + 32 > in_bytes)
+                return ZC_EINVAL;
+        }
+        if ((reinterpret_cast<uintptr_t>(d_in) & 15) || (reinterpret_cast<uintptr_t>(d_status) & 3))
+            return ZC_EINVAL;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        for (uint64_t i = 0; i <= slabs; ++i) {
+            ChunkTable tab;
+            std::memset(&tab, 0, sizeof tab);
+            uint32_t dec_blocks = 0;
+            uint16_t* dec = static_cast<uint16_t*>(d_scratch) + (i & 1) * buf_values;
+            if (i < slabs) {
+                const uint64_t t0 = i * slab_tiles;
+                const uint32_t tiles = static_cast<uint32_t>(std::min<uint64_t>(slab_tiles, T - t0));
+                uint32_t items = 0;
+                for (int32_t c = 0; c < num_chunks; ++c) {
+                    const uint64_t off = in_offsets ? static_cast<uint64_t>(in_offsets[c]) : c * slot_bytes;
+                    tab.item_begin[c] = items;
+                    tab.n[c] = static_cast<uint32_t>(n);
+                    tab.voff[c] = static_cast<uint64_t>(c) * stride - t0 * kTile;
+                    tab.boff[c] = off;
+                    tab.bavail[c] = in_bytes - off;
+                    items += tiles;
+                }
+                tab.nchunks = num_chunks;
+                tab.chunk_base = 0;
+                tab.tile0 = static_cast<uint32_t>(t0);
+                tab.nitems = items;
+                tab.item_begin[num_chunks] = items;
+                dec_blocks = (items + kWaves - 1) / kWaves;
+            }
+            const uint16_t* x = static_cast<const uint16_t*>(d_scratch) + ((i + 1) & 1) * buf_values;
+            uint64_t len = 0, s0 = 0;
+            if (i >= 1) {
+                s0 = (i - 1) * slab_tiles * kTile;
+                len = std::min<uint64_t>(static_cast<uint64_t>(n) - s0, stride);
+            }
+            const uint32_t sum_blocks = static_cast<uint32_t>(((len + 7) / 8 + kBlock - 1) / kBlock);
+            const dim3 grid(dec_blocks + sum_blocks);
+            if (bf16)
+                hipLaunchKernelGGL(zc_decode_sum_kernel<true>, grid, dim3(kBlock), 0, s,
+                                   in, dec, d_status, tab, dec_blocks, x, len, stride, num_chunks,
+                                   static_cast<void*>(static_cast<uint16_t*>(d_out) + s0));
+            else
+                hipLaunchKernelGGL(zc_decode_sum_kernel<false>, grid, dim3(kBlock), 0, s,
+                                   in, dec, d_status, tab, dec_blocks, x, len, stride, num_chunks,
+                                   static_cast<void*>(static_cast<float*>(d_out) + s0));
+            if (hipGetLastError() != hipSuccess)
+                return ZC_EHIP;
+        }
+        return ZC_OK;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     const std::vector<int64_t> counts(static_cast<size_t>(num_chunks), n);
     const uint16_t* x = static_cast<const uint16_t*>(d_scratch);
-    const uint64_t T = (static_cast<uint64_t>(n) + kTile - 1) / kTile;
-    const uint64_t slab_tiles = (stride + kTile - 1) / kTile;
     for (uint64_t t0 = 0; t0 < T; t0 += slab_tiles) {
         const uint64_t s0 = t0 * kTile;
         const uint64_t len = std::min<uint64_t>(static_cast<uint64_t>(n) - s0, stride);
@@ -2367,8 +2469,7 @@ size_t zc_reduce_scratch_bytes(int64_t n, int32_t num_chunks)
 {
     if (n < 0 || n > ZC_MAX_CHUNK_VALUES || num_chunks < 0 || num_chunks > ZC_MAX_CHUNKS)
         return 0;
-    return static_cast<size_t>(2ull * reduce_stride(static_cast<uint64_t>(n), num_chunks) *
-                               static_cast<uint64_t>(num_chunks));
+    return static_cast<size_t>(reduce_scratch(static_cast<uint64_t>(n), num_chunks));
 }
 
 int zc_decompress_reduce(const void* d_in, size_t in_bytes, const int64_t* in_offsets,

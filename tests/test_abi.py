@@ -63,20 +63,21 @@ def test_workspace_bytes():
 
 def test_reduce_scratch_bytes():
     # one slab holds the whole shard: every contribution at its length
-    # rounded up to 8 values
+    # rounded up to 8 values, one buffer
     assert zc.zc_reduce_scratch_bytes(4096, 4) == 2 * 4096 * 4
     assert zc.zc_reduce_scratch_bytes(20003, 8) == 2 * 20008 * 8
     assert zc.zc_reduce_scratch_bytes(1, 5) == 2 * 8 * 5
-    # otherwise one slab of whole 8192-value tiles per stream, about
-    # 128 MiB over all streams, whatever the shard length
+    # otherwise slabs of whole 8192-value tiles per stream, about 128 MiB
+    # over all streams: two slab buffers for at most 64 streams, one for more
     slab = 128 << 20
     for n, c in [(1 << 22, 64), (1 << 26, 64), ((1 << 22) + 77, 64), (1 << 25, 3),
-                 (1 << 27, 1), (1 << 22, 4096)]:
+                 (1 << 27, 1), (1 << 22, 65), (1 << 22, 4096)]:
         b = zc.zc_reduce_scratch_bytes(n, c)
-        per = b // (2 * c)
-        assert b == 2 * c * per and per % 8192 == 0 and 8192 <= per < n, (n, c)
-        assert b <= max(slab, 2 * c * 8192), (n, c)
-    assert zc.zc_reduce_scratch_bytes(1 << 22, 64) == slab
+        bufs = 2 if c <= 64 else 1
+        per = b // (2 * c * bufs)
+        assert b == 2 * c * per * bufs and per % 8192 == 0 and 8192 <= per < n, (n, c)
+        assert per * 2 * c <= max(slab, 2 * c * 8192), (n, c)
+    assert zc.zc_reduce_scratch_bytes(1 << 22, 64) == 2 * slab
     assert zc.zc_reduce_scratch_bytes(0, 4) == 0
     assert zc.zc_reduce_scratch_bytes(-1, 4) == 0
     assert zc.zc_reduce_scratch_bytes(10, -1) == 0

@@ -139,12 +139,26 @@ def test_reduce_reports_corrupt_stream(oracle):
 
 def test_reduce_ragged_slabs(oracle):
     # 64 streams of a shard longer than one slab (1 Mi values per stream at
-    # 64 streams), ending in a partial tile: two slabs, the second ragged
+    # 64 streams), ending in a partial tile: two slabs, the second ragged,
+    # decoded and summed in alternating slab buffers
     c = 64
     n = (1 << 20) + 3 * 8192 + 77
-    assert zc.zc_reduce_scratch_bytes(n, c) == 2 * c * (1 << 20)
+    assert zc.zc_reduce_scratch_bytes(n, c) == 2 * 2 * c * (1 << 20)
     w = special_mix(n * c, 77)
     say("reduce ragged slabs n=%d chunks=%d" % (n, c))
+    st, got = gpu_reduce(w, n, c)
+    assert st == 0, "status %#x" % st
+    same_f32(got, oracle.reduce_bf16_f32(w, n, c))
+
+
+def test_reduce_more_than_64_streams_in_slabs(oracle):
+    # 65 streams: each slab is decoded in two launches (64 + 1 streams),
+    # then summed; two slabs, the second ragged
+    c = 65
+    n = 126 * 8192 + 3 * 8192 + 5
+    assert zc.zc_reduce_scratch_bytes(n, c) == 2 * c * 126 * 8192
+    w = special_mix(n * c, 78)
+    say("reduce 65 streams in slabs n=%d" % n)
     st, got = gpu_reduce(w, n, c)
     assert st == 0, "status %#x" % st
     same_f32(got, oracle.reduce_bf16_f32(w, n, c))
