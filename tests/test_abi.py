@@ -48,7 +48,7 @@ def test_bounds_match_oracle(oracle):
 
 
 def test_workspace_bytes():
-    # a fixed header (per-chunk ticket counters), then one status slot per
+    # a fixed header (launch tag and completion counters), then one status slot per
     # tile of the largest launch (at most 64 chunks per launch)
     one = zc.zc_workspace_bytes([0])          # header + 1 slot
     three = zc.zc_workspace_bytes([8193, 1])  # header + 3 slots
