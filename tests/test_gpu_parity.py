@@ -184,6 +184,53 @@ def test_workload_full_size(oracle, cfg):
         assert ratio > 1.3
 
 
+def test_largest_chunk(oracle):
+    # one chunk of ZC_MAX_CHUNK_VALUES (2^31 - 1) values: 262 144 tiles, the
+    # last one ragged, streams past 4 GiB.  A tile's stream, group maxima,
+    # group lengths and raw bytes depend only on its own values, so sampled
+    # tiles are compared byte for byte with the oracle's stream of a chunk
+    # made of those values alone; the whole chunk round-trips through the
+    # strict decoder, which accepts only the unique encoding.
+    n = (1 << 31) - 1
+    T = (n + 8191) // 8192
+    say("largest chunk: %d values, %d tiles" % (n, T))
+    g = torch.Generator(device=DEV)
+    g.manual_seed(20260131)
+    x = (torch.randn(n, device=DEV, generator=g) * 0.02).to(torch.bfloat16).view(torch.int16)
+    x[::997] = 0                                   # exact zeros: escapes
+    mid = T // 2
+    x[mid * 8192:(mid + 1) * 8192] = torch.randint(-32768, 32768, (8192,), device=DEV,
+                                                   generator=g, dtype=torch.int32).to(torch.int16)
+    buf, sizes = zc.compress(x, [n])
+    torch.cuda.synchronize()
+    comp = int(sizes[0].item())
+    Tg, _, R, X = oracle.geometry(n)
+    assert Tg == T and X < comp <= oracle.chunk_bound(n)
+    hdr = buf[:32].cpu().numpy().view(np.uint32)
+    assert hdr[4] == n and (int(hdr[6]) | (int(hdr[7]) << 32)) == comp
+    toff = buf[32:32 + 4 * T].cpu().numpy().view(np.uint32).astype(np.int64)
+    assert toff[0] == 0 and np.all(np.diff(toff) >= 0)
+    for t in (0, 1, mid, T - 2, T - 1):
+        m = min(8192, n - 8192 * t)
+        w = x[8192 * t:8192 * t + m].cpu().numpy().view(np.uint16)
+        ref = oracle.compress_chunk(w)
+        _, _, R1, X1 = oracle.geometry(m)
+        end = toff[t + 1] if t + 1 < T else comp - X
+        got_stream = buf[X + toff[t]:X + end].cpu().numpy()
+        assert np.array_equal(got_stream, ref[X1:]), "tile %d stream" % t
+        emax = buf[32 + 4 * T + 64 * t:32 + 4 * T + 64 * (t + 1)].cpu().numpy()
+        assert np.array_equal(emax, ref[36:100]), "tile %d emax" % t
+        glen = buf[32 + 68 * T + 128 * t:32 + 68 * T + 128 * (t + 1)].cpu().numpy()
+        assert np.array_equal(glen, ref[100:228]), "tile %d glen" % t
+        raw = buf[R + 8192 * t:R + 8192 * t + m].cpu().numpy()
+        assert np.array_equal(raw, ref[R1:R1 + m]), "tile %d raw bytes" % t
+    say("largest chunk: decompress")
+    y, status = zc.decompress(buf, [n], check=False)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert torch.equal(x, y)
+
+
 # ------------------------------------------------ look-back fallback ---
 
 @pytest.mark.parametrize("layout", ["equal", "ragged"])
