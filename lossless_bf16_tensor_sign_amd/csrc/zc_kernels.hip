@@ -1244,42 +1244,58 @@ __device__ inline void stage_words(uint32_t* __restrict__ s, const uint32_t* __r
 
 // A full tile whose 64 groups are all raw: every group stream is 1024 bits
 // of plain exponents at bit 1024 * lane.  The 8 KiB tile stream is staged in
-// two halves, each decoded by the 32 lanes that own it.
+// two halves of 32 groups, each decoded by all 64 lanes, two per group.
 __device__ inline void decode_all_raw(const uint32_t* __restrict__ gstream,
                                       uint32_t* __restrict__ s, const uint8_t* __restrict__ s_len,
                                       const uint8_t* __restrict__ rsrc, uint16_t* __restrict__ dst,
                                       uint32_t n, uint32_t base, uint32_t lane, uint32_t emax,
                                       bool vec_out, DecState& st)
 {
-    const uint2* rsrc2 = reinterpret_cast<const uint2*>(rsrc + base) + lane;
+    uint32_t seen = 0, coded = 0;
 #pragma unroll 1
     for (int h = 0; h < 2; ++h) {
         wave_lds_sync();
         stage_words(s, gstream + h * kStageWords, kStageWords, lane);
         wave_lds_sync();
-        if ((lane >> 5) == static_cast<uint32_t>(h)) {
-            const uint32_t* mine = s + (lane & 31) * 32;
+        // lane l takes group 32 h + l % 32, steps 8 (l / 32) .. 8 (l / 32) + 7:
+        // a raw group's members sit at fixed bit positions, so its two lanes
+        // need nothing from each other until the checks
+        const uint32_t g = 32u * static_cast<uint32_t>(h) + (lane & 31);
+        const uint32_t k0 = (lane >> 5) * 8;
+        const uint32_t eg = __shfl(emax, g);
+        const uint32_t* mine = s + (lane & 31) * 32 + 2 * k0;
+        const uint2* rsrc2 = reinterpret_cast<const uint2*>(rsrc + base) + g;
+        uint32_t sm = 0, rc = 0;
 #pragma unroll 2
-            for (int k = 0; k < kSteps; ++k) {
-                const uint2 ew = *reinterpret_cast<const uint2*>(mine + 2 * k);
-                const uint32_t e4a = __builtin_amdgcn_perm(ew.x, ew.x, 0x00010203u);
-                const uint32_t e4b = __builtin_amdgcn_perm(ew.y, ew.y, 0x00010203u);
-                uint32_t e8[8];
+        for (int k = 0; k < kSteps / 2; ++k) {
+            const uint2 ew = *reinterpret_cast<const uint2*>(mine + 2 * k);
+            const uint32_t e4a = __builtin_amdgcn_perm(ew.x, ew.x, 0x00010203u);
+            const uint32_t e4b = __builtin_amdgcn_perm(ew.y, ew.y, 0x00010203u);
+            uint32_t e8[8];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    e8[j] = (e4a >> (8 * j)) & 0xFF;
-                    e8[4 + j] = (e4b >> (8 * j)) & 0xFF;
-                }
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    st.seen_max = max(st.seen_max, e8[j]);
-                    st.raw_coded += s_len[(emax - e8[j]) & 0xFF];
-                }
-                put_values<true>(dst, rsrc, n, base + k * 512 + lane * 8, ld2(rsrc2 + k * 64), e8, vec_out);
+            for (int j = 0; j < 4; ++j) {
+                e8[j] = (e4a >> (8 * j)) & 0xFF;
+                e8[4 + j] = (e4b >> (8 * j)) & 0xFF;
             }
-            st.pos += 1024;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                sm = max(sm, e8[j]);
+                rc += s_len[(eg - e8[j]) & 0xFF];
+            }
+            const uint32_t ks = k0 + static_cast<uint32_t>(k);
+            put_values<true>(dst, rsrc, n, base + ks * 512 + g * 8, ld2(rsrc2 + ks * 64), e8, vec_out);
+        }
+        // the group's two halves meet; lane l keeps the totals of group l
+        const uint32_t sm2 = max(sm, static_cast<uint32_t>(__shfl_xor(sm, 32)));
+        const uint32_t rc2 = rc + static_cast<uint32_t>(__shfl_xor(rc, 32));
+        if ((lane >> 5) == static_cast<uint32_t>(h)) {
+            seen = sm2;
+            coded = rc2;
         }
     }
+    st.seen_max = max(st.seen_max, seen);
+    st.raw_coded += coded;
+    st.pos += 1024;
 }
 
 // A tile's header word, offsets and group metadata, loaded together (only
