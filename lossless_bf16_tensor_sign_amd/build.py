@@ -26,7 +26,7 @@ HIP_FLAGS = [
     # a single-lane atomic stays one atomic whose result is waited for where
     # it is used (the optimizer's wave reduction waits at once)
     "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
-    "-Wall", "-Wno-unused-function",
+    "-Wall",
 ]
 
 

@@ -268,7 +268,6 @@ __device__ inline void st_nt2(void* p, uint2 v)
 {
     __builtin_nontemporal_store(v2u{v.x, v.y}, reinterpret_cast<v2u*>(p));
 }
-__device__ inline void st_nt1(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
 
 // ------------------------------------------------------------ compress
 
