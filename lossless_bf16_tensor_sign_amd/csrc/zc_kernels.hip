@@ -35,7 +35,8 @@
 //  * no value is carried in a register that a memory load must refill inside
 //    a loop or across the encoder's emission: on this hardware the wait for
 //    such a load also waits for every older store of the wave.
-// No floating point runs on the device.
+// The codec itself is integer arithmetic; only the decode + sum of a
+// reduce-scatter's received copies adds in fp32.
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
