@@ -169,6 +169,29 @@ def test_deterministic_repeat(oracle):
                 assert np.array_equal(streams[c], first[c]), c
 
 
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_deterministic_repeat_full_size(cfg):
+    # The gradient workload (escape steps and raw groups in most tiles) and
+    # the MoE layout (chunk-end tiles), compressed four times into zeroed
+    # buffers: every byte of every call equals the first call's.
+    w, cnt = synth.make(cfg, workers=8)
+    x = to_dev(w)
+    bound = zc.zc_bound(cnt)
+    ws = torch.zeros(zc.zc_workspace_bytes(cnt), dtype=torch.uint8, device=x.device)
+    say("determinism workload %d x4" % cfg)
+    first = None
+    for _ in range(4):
+        out = torch.zeros(bound, dtype=torch.uint8, device=x.device)
+        sizes = torch.zeros(len(cnt), dtype=torch.int64, device=x.device)
+        assert zc.zc_compress(x, cnt, out, sizes, ws) == zc.ZC_OK
+        torch.cuda.synchronize()
+        if first is None:
+            first = (out, sizes)
+        else:
+            assert torch.equal(sizes, first[1])
+            assert torch.equal(out, first[0])
+
+
 # ------------------------------------------------------- workloads ---
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
