@@ -360,8 +360,9 @@ def main():
     ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
     y = torch.empty(n, dtype=torch.int16, device=dev)
     if args.reduce:
-        y = torch.empty(zc.zc_reduce_scratch_bytes(shard, len(counts)) // 2, dtype=torch.int16,
-                        device=dev)
+        # the decode + sum scratch (none when it runs as one kernel)
+        y = torch.empty(max(zc.zc_reduce_scratch_bytes(shard, len(counts)) // 2, 8),
+                        dtype=torch.int16, device=dev)
     red = torch.empty(shard if args.reduce else 4, dtype=torch.float32, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -420,7 +421,7 @@ def main():
     tc = np.array([a.elapsed_time(b) for a, b, _, _ in times]) * 1e-3
     td = np.array([c.elapsed_time(d) for _, _, c, d in times]) * 1e-3
     st = int(status.item())
-    # (with --reduce, y is the slab scratch and holds no whole decode)
+    # (with --reduce, y is the scratch and holds no whole decode)
     ok = st == 0 and (args.reduce or torch.equal(x, y))
     if args.reduce:
         acc = torch.zeros(shard, dtype=torch.float32, device=dev)

@@ -281,16 +281,20 @@ int zc_decompress_dev(const void* d_in, size_t in_bytes,
  *   d_status    device int32, 0 on entry; as for zc_decompress.  If it is
  *               nonzero after the stream has run, d_out is undefined.
  *   d_scratch   device, 16-byte aligned, scratch_bytes >=
- *               zc_reduce_scratch_bytes(n, num_chunks): the decoded bf16
- *               contributions are staged there, one or two slabs at a time;
- *               caller-owned, contents undefined after
+ *               zc_reduce_scratch_bytes(n, num_chunks) (may be NULL when
+ *               that is 0): the decoded bf16 contributions are staged
+ *               there, one or two slabs at a time; caller-owned, contents
+ *               undefined after
  *   stream      hipStream_t; every launch is queued on it
- * The shard is processed in slabs of whole 8192-value tiles, about 128 MiB
- * of staged values per slab over all streams, so that a slab is summed
- * while it is still in the device's 256 MB last-level cache.  With at most
- * 64 streams and more than one slab, launch i decodes slab i into one of
- * two slab buffers and sums slab i - 1 from the other; with more streams,
- * each slab is decoded and then summed.
+ * With 8 to 64 streams of at least 512 tiles (n > 511 * 8192), one launch
+ * decodes and sums with nothing staged: a workgroup per tile position
+ * decodes that tile of eight streams at a time and adds them in LDS, in
+ * chunk order.  Otherwise the shard is processed in slabs of whole
+ * 8192-value tiles, about 128 MiB of staged values per slab over all
+ * streams, so that a slab is summed while it is still in the device's
+ * 256 MB last-level cache.  With at most 64 streams and more than one slab,
+ * launch i decodes slab i into one of two slab buffers and sums slab i - 1
+ * from the other; with more streams, each slab is decoded and then summed.
  * Returns ZC_OK once queued; ZC_EINVAL for a bad argument, ZC_ENOSPC for a
  * short scratch buffer (nothing queued), ZC_EHIP if a launch fails.
  */
@@ -301,13 +305,14 @@ int zc_decompress_reduce(const void* d_in, size_t in_bytes,
 
 /*
  * Scratch bytes that zc_decompress_reduce and zc_decompress_reduce_bf16 need
- * for num_chunks streams of n values: 2 num_chunks s per slab buffer, where
- * s (values per stream per slab) is n rounded up to 8 when one slab holds
- * the whole shard (one buffer), else the slab's whole tiles (two buffers
- * for at most 64 streams, one for more).  At most about 256 MiB whatever n
- * (more only when one tile per stream exceeds a slab); 0 for n == 0 or an
- * argument out of range.  A property of this library's slab size, not of
- * the stream format.
+ * for num_chunks streams of n values: 0 when one launch decodes and sums (8
+ * to 64 streams of at least 512 tiles); otherwise 2 num_chunks s per slab
+ * buffer, where s (values per stream per slab) is n rounded up to 8 when
+ * one slab holds the whole shard (one buffer), else the slab's whole tiles
+ * (two buffers for at most 64 streams, one for more).  At most about
+ * 256 MiB whatever n (more only when one tile per stream exceeds a slab); 0
+ * for n == 0 or an argument out of range.  A property of this library's
+ * kernels and slab size, not of the stream format.
  */
 size_t zc_reduce_scratch_bytes(int64_t n, int32_t num_chunks);
 

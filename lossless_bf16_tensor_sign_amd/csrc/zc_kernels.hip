@@ -1223,6 +1223,83 @@ __device__ __forceinline__ void decode_group(const Win& win, const uint8_t* __re
     }
 }
 
+// The symbols of step k of this lane's group, as in decode_group's loop: the
+// 8 exponents in e8, and the bit position, the largest exponent and (raw
+// groups) the coded length advanced in st.  The fused decode + sum below
+// takes its steps from here; decode_group keeps its own copy of the loop,
+// whose code generation the plain decompress is tuned on.
+template <bool FULL, int kSym, bool MIXED, class Win>
+__device__ __forceinline__ void decode_step(const Win& win, const uint8_t* __restrict__ s_lut8,
+                                            const uint16_t* __restrict__ s_tail,
+                                            const uint8_t* __restrict__ s_len, const LaneCode& q,
+                                            int k, uint32_t ng, uint32_t emax, bool raw_mode,
+                                            DecState& st, uint32_t (&e8)[8])
+{
+    // kSym symbols per 64-bit window; a lane whose code words overrun
+    // the window (several escapes) decodes them again one at a time
+#pragma unroll
+    for (int h = 0; h < 8 / kSym; ++h) {
+        const uint32_t pos0 = st.pos;
+        uint64_t W = win(pos0);
+        uint32_t used = 0;
+        int32_t esc_w = 255;
+#pragma unroll
+        for (int jj = 0; jj < kSym; ++jj) {
+            const int j = h * kSym + jj;
+            const bool valid = FULL || static_cast<uint32_t>(k * 8 + j) < ng;
+            uint32_t sym, sh;
+            decode_sym(s_lut8, s_tail, hi32(W), q, emax, valid, esc_w, sym, sh);
+            if (!FULL && !valid)
+                sh = 0;
+            e8[j] = q.emax_eff - sym;
+            W <<= sh;
+            used += sh;
+        }
+        const bool slow = used > 64;
+        if (!slow)
+            st.esc_min = min(st.esc_min, esc_w);
+        if (__ballot(slow)) {
+            if (slow) {
+                uint32_t p = pos0;
+                int32_t esc_h = 255;
+#pragma unroll
+                for (int jj = 0; jj < kSym; ++jj) {
+                    const int j = h * kSym + jj;
+                    const bool valid = FULL || static_cast<uint32_t>(k * 8 + j) < ng;
+                    uint32_t sym, sh;
+                    decode_sym(s_lut8, s_tail, hi32(win(p)), q, emax, valid, esc_h, sym, sh);
+                    if (!FULL && !valid)
+                        sh = 0;
+                    e8[j] = q.emax_eff - sym;
+                    p += sh;
+                }
+                used = p - pos0;
+                st.esc_min = min(st.esc_min, esc_h);
+            }
+        }
+        st.pos = pos0 + used;
+    }
+    if (FULL) {
+        st.seen_max = max(st.seen_max, max3(e8[0], e8[1], e8[2]));
+        st.seen_max = max(st.seen_max, max3(e8[3], e8[4], e8[5]));
+        st.seen_max = max(st.seen_max, max(e8[6], e8[7]));
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (static_cast<uint32_t>(k * 8 + j) < ng)
+                st.seen_max = max(st.seen_max, e8[j]);
+    }
+    if (MIXED) {
+        // a raw group must not have been codable in fewer bits
+        if (raw_mode) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (FULL || static_cast<uint32_t>(k * 8 + j) < ng)
+                    st.raw_coded += s_len[(emax - e8[j]) & 0xFF];
+        }
+    }
+}
+
 // Copies `words` (1..1024) tile-stream words from global memory into LDS.
 // Every load of a lane is issued before the first is written, so the copy
 // costs one memory round trip; rows past the end are skipped as a whole and
@@ -1690,6 +1767,327 @@ void zc_decode_sum_kernel(const uint8_t* __restrict__ in, uint16_t* __restrict__
         reduce_body<BF16OUT>(x, n, stride, num_chunks, out, blockIdx.x - dec_blocks);
 }
 
+// ------------------------------------------------------------ decode and sum in one kernel
+
+// One workgroup per tile position t: its eight waves decode tile t of eight
+// streams at a time, one stream each.  After every two steps the waves'
+// 1024 values each meet in LDS, and each thread adds two values of one of
+// the two steps, over the streams in stream order, to its accumulators.
+// Rounds of eight streams follow each other, so every sum takes the streams
+// in chunk order; nothing decoded leaves the workgroup.
+constexpr int kSumWaves = 8;                     // streams decoded together
+constexpr int kSumBlock = kSumWaves * kLanes;    // threads: two values of one of two steps each
+constexpr int kSumMinWaves = 4;                  // occupancy target, waves per SIMD
+// The fused form is taken for 8 to 64 streams of at least this many tiles:
+// two workgroups for each of the 256 compute units.  Its parallelism is
+// 8 waves per tile position, and each wave decodes ceil(C / 8) tiles one
+// after another, so short shards (fewer positions) are faster staged.
+constexpr uint64_t kSumMinTiles = 512;
+
+// The streams of one fused call.
+struct SumTable {
+    int32_t nstreams;
+    uint32_t n;                       // values per stream
+    uint64_t boff[kMaxChunks];        // byte offset of stream c
+    uint64_t bavail[kMaxChunks];      // readable bytes from boff[c]
+};
+
+// Per-thread place in the step exchange.
+struct SumCtx {
+    uint16_t* buf;        // LDS: two exchange buffers of kSumWaves x 2 x 512 values
+    uint32_t wave, tid;
+    uint32_t nround;      // streams of this round (waves 0 .. nround - 1)
+};
+
+// One exchange, steps k and k + 1 (k even): this wave's values of the two
+// steps go into buffer (k / 2) % 2, and after the barrier thread tid adds
+// values 2p and 2p + 1 (p = tid % 256) of step k + tid / 256 of the round's
+// streams, in stream order, to acc[k] and acc[k + 1] (so acc[k + j] of
+// thread tid sums value 2p + j of step k + tid / 256).  Two buffers need one
+// barrier per exchange: a buffer is written again one exchange later, after
+// every thread has passed the barrier in between, and so has finished
+// reading it.
+__device__ __forceinline__ void sum_step(const SumCtx& sc, float (&acc)[kSteps], int k, uint4 v0,
+                                         uint4 v1)
+{
+    constexpr int kV = kLanes * 8;       // values per step
+    uint16_t* b = sc.buf + ((k >> 1) & 1) * (kSumWaves * 2 * kV);
+    uint16_t* mine = b + sc.wave * (2 * kV) + (sc.tid & (kLanes - 1)) * 8;
+    *reinterpret_cast<uint4*>(mine) = v0;
+    *reinterpret_cast<uint4*>(mine + kV) = v1;
+    __syncthreads();
+    const uint32_t* b32 = reinterpret_cast<const uint32_t*>(b) + (sc.tid >> 8) * (kV / 2) + (sc.tid & 255);
+    const int e = k >> 1;
+    float a0 = acc[2 * e], a1 = acc[2 * e + 1];
+#pragma unroll
+    for (int s = 0; s < kSumWaves; ++s)
+        if (static_cast<uint32_t>(s) < sc.nround) {
+            const uint32_t w = b32[s * kV];
+            a0 = a0 + bf16_lo(w);
+            a1 = a1 + bf16_hi(w);
+        }
+    acc[2 * e] = a0;
+    acc[2 * e + 1] = a1;
+}
+
+// The 8 values of a segment as 16-bit words (the join of put_values); in a
+// partial tile the ragged segment's sign+mantissa bytes are read one by one,
+// and values past the end are left 0.
+template <bool FULL>
+__device__ __forceinline__ uint4 join_values(const uint8_t* __restrict__ rsrc, uint32_t n,
+                                             uint32_t i0, uint2 r, const uint32_t (&e8)[8])
+{
+    if (!FULL && i0 < n && i0 + 8 > n) {
+        uint32_t w[2] = {0, 0};
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (i0 + j < n)
+                w[j >> 2] |= static_cast<uint32_t>(rsrc[i0 + j]) << (8 * (j & 3));
+        r = make_uint2(w[0], w[1]);
+    }
+    uint4 o;
+    o.x = (__builtin_amdgcn_perm(r.x, r.x, 0x01010000u) & 0x807F807Fu) | ((e8[0] & 0xFF) << 7) | ((e8[1] & 0xFF) << 23);
+    o.y = (__builtin_amdgcn_perm(r.x, r.x, 0x03030202u) & 0x807F807Fu) | ((e8[2] & 0xFF) << 7) | ((e8[3] & 0xFF) << 23);
+    o.z = (__builtin_amdgcn_perm(r.y, r.y, 0x01010000u) & 0x807F807Fu) | ((e8[4] & 0xFF) << 7) | ((e8[5] & 0xFF) << 23);
+    o.w = (__builtin_amdgcn_perm(r.y, r.y, 0x03030202u) & 0x807F807Fu) | ((e8[6] & 0xFF) << 7) | ((e8[7] & 0xFF) << 23);
+    return o;
+}
+
+// decode_group with every two steps handed to the exchange instead of
+// stored; the sign+mantissa bytes are prefetched two steps ahead.
+template <bool FULL, int kSym, bool MIXED, class Win>
+__device__ __forceinline__ void decode_group_sum(const Win& win, const uint8_t* __restrict__ s_lut8,
+                                                 const uint16_t* __restrict__ s_tail,
+                                                 const uint8_t* __restrict__ s_len,
+                                                 const uint8_t* __restrict__ rsrc, uint32_t n,
+                                                 uint32_t base, uint32_t lane, uint32_t ng,
+                                                 uint32_t emax, bool raw_mode, DecState& st,
+                                                 const SumCtx& sc, float (&acc)[kSteps])
+{
+    const bool raw = MIXED && raw_mode;
+    LaneCode q;
+    q.ish = raw ? 24u : static_cast<uint32_t>(32 - kLutBits);
+    q.base = raw ? static_cast<uint32_t>(kLutRaw) : 0u;
+    q.sym_sh = raw ? 0u : 4u;
+    q.smask = raw ? 0u : 15u;
+    q.sor = raw ? 8u : 0u;
+    q.lmark = raw ? 256u : 0u;
+    q.emax_eff = raw ? 255u : emax;
+    const uint2* rsrc2 = reinterpret_cast<const uint2*>(rsrc + base) + lane;
+    auto raw_at = [&](int k) {
+        return (FULL || base + k * 512 + lane * 8 + 8 <= n) ? ld_nt2(rsrc2 + k * 64)
+                                                            : make_uint2(0, 0);
+    };
+    uint2 ring[2] = {raw_at(0), raw_at(1)};
+#pragma unroll 1
+    for (int k = 0; k < kSteps; k += 2) {
+        uint32_t e8[8];
+        decode_step<FULL, kSym, MIXED>(win, s_lut8, s_tail, s_len, q, k, ng, emax, raw_mode, st, e8);
+        const uint4 v0 = join_values<FULL>(rsrc, n, base + k * 512 + lane * 8, ring[0], e8);
+        ring[0] = raw_at(min(k + 2, kSteps - 1));
+        decode_step<FULL, kSym, MIXED>(win, s_lut8, s_tail, s_len, q, k + 1, ng, emax, raw_mode, st, e8);
+        const uint4 v1 = join_values<FULL>(rsrc, n, base + (k + 1) * 512 + lane * 8, ring[1], e8);
+        ring[1] = raw_at(min(k + 3, kSteps - 1));
+        sum_step(sc, acc, k, v0, v1);
+    }
+}
+
+// A wave with no stream this round (or one whose tile failed a check) still
+// takes part in every step of the exchange.
+__device__ __forceinline__ void idle_sum(const SumCtx& sc, float (&acc)[kSteps])
+{
+#pragma unroll 1
+    for (int k = 0; k < kSteps; k += 2)
+        sum_step(sc, acc, k, make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0));
+}
+
+// decompress_tile's checks and decode for one stream's tile t, feeding the
+// exchange; every path runs the 16 steps of the exchange exactly once.
+template <bool FULL>
+__device__ __forceinline__ void decode_tile_sum(const uint8_t* __restrict__ src,
+                                                int32_t* __restrict__ status, int c, uint32_t n,
+                                                uint32_t t, uint64_t bavail, uint32_t lane,
+                                                uint32_t* __restrict__ s,
+                                                const uint8_t* __restrict__ s_lut8,
+                                                const uint16_t* __restrict__ s_tail,
+                                                const uint8_t* __restrict__ s_len,
+                                                const SumCtx& sc, float (&acc)[kSteps])
+{
+    const Geom G = geometry(n);
+    const uint32_t base = t * kTile;
+    const uint32_t rem = min(n - base, static_cast<uint32_t>(kTile));
+    const uint32_t ng = FULL ? 128u : group_members(rem, lane);
+    int fail = 0;
+    TileMeta meta = {0, 0, 0, 0, 0};
+    if (G.X > bavail)
+        fail = ZC_REASON_SIZE;
+    else
+        meta = load_meta(src, G, t, lane);
+    const uint32_t hw = meta.hw, toff = meta.toff, tnext = meta.tnext, emax = meta.emax,
+                   glen = meta.glen;
+    const uint32_t h0 = __shfl(hw, 0), h1 = __shfl(hw, 1), h2 = __shfl(hw, 2),
+                   h3 = __shfl(hw, 3), h4 = __shfl(hw, 4), h5 = __shfl(hw, 5),
+                   h6 = __shfl(hw, 6), h7 = __shfl(hw, 7);
+    if (!fail && (h0 != kMagic || h1 != kVerTable || h2 != 0 || h3 != 0 || h4 != n || h5 != 0))
+        fail = ZC_REASON_HEADER;
+    const uint64_t comp = h6 | (static_cast<uint64_t>(h7) << 32);
+    if (!fail && (comp < G.X || comp > bavail || comp > chunk_bound(n)))
+        fail = ZC_REASON_SIZE;
+    const uint64_t next = (t + 1 < G.T) ? tnext : comp - G.X;
+    if (!fail && ((t == 0 && toff != 0) || toff > next || next > comp - G.X))
+        fail = ZC_REASON_TILE;
+    if (!fail && __ballot(glen > 8 * ng || (ng == 0 && emax != 0)))
+        fail = ZC_REASON_GROUP;
+    uint32_t tile_bits;
+    const uint32_t off = wave_excl_scan(glen, lane, &tile_bits);
+    // uniform: it chooses between paths that hold barriers
+    tile_bits = __builtin_amdgcn_readfirstlane(tile_bits);
+    const uint32_t tile_words = (tile_bits + 31) >> 5;
+    if (!fail && static_cast<uint32_t>(next - toff) != 4 * tile_words)
+        fail = ZC_REASON_TILE;
+    fail = __builtin_amdgcn_readfirstlane(fail);
+    if (fail) {
+        if (lane == 0)
+            report(status, fail, c);
+        idle_sum(sc, acc);
+        return;
+    }
+
+    const uint32_t* gstream = reinterpret_cast<const uint32_t*>(src + G.X + toff);
+    int err = 0;
+    if (t == 0) {
+        const uint64_t g1 = 32 + 196ull * G.T;
+        if (g1 + lane < G.R && src[g1 + lane] != 0)
+            err = ZC_REASON_GAP;
+    }
+    if (t == G.T - 1) {
+        if (G.R + n + lane < G.X && src[G.R + n + lane] != 0)
+            err = ZC_REASON_GAP;
+    }
+    if ((tile_bits & 31) && lane == 0) {
+        const uint32_t last = gstream[tile_words - 1];
+        if (last & ((1u << (32 - (tile_bits & 31))) - 1))
+            err = ZC_REASON_PADDING;
+    }
+    const bool raw_mode = ng > 0 && glen == 8 * ng;
+    const uint64_t raw_lanes = __ballot(raw_mode);
+    const uint8_t* rsrc = src + G.R;
+    DecState st;
+    st.pos = off;
+    st.seen_max = 0;
+    st.raw_coded = 0;
+    st.esc_min = 255;
+    if (tile_words <= static_cast<uint32_t>(kStageWords)) {
+        wave_lds_sync();
+        stage_words(s, gstream, tile_words, lane);
+        if (lane < 4)
+            s[tile_words + lane] = 0;
+        wave_lds_sync();
+        const LdsWindow lw{s, tile_words};
+        if (__ballot(!raw_mode && glen > 5 * ng) == 0) {
+            if (raw_lanes == 0)
+                decode_group_sum<FULL, 8, false>(lw, s_lut8, s_tail, s_len, rsrc, n, base, lane,
+                                                 ng, emax, raw_mode, st, sc, acc);
+            else
+                decode_group_sum<FULL, 8, true>(lw, s_lut8, s_tail, s_len, rsrc, n, base, lane,
+                                                ng, emax, raw_mode, st, sc, acc);
+        } else {
+            if (raw_lanes == 0)
+                decode_group_sum<FULL, 4, false>(lw, s_lut8, s_tail, s_len, rsrc, n, base, lane,
+                                                 ng, emax, raw_mode, st, sc, acc);
+            else
+                decode_group_sum<FULL, 4, true>(lw, s_lut8, s_tail, s_len, rsrc, n, base, lane,
+                                                ng, emax, raw_mode, st, sc, acc);
+        }
+    } else {
+        decode_group_sum<FULL, 4, true>(GlobalWindow{gstream, tile_words}, s_lut8, s_tail, s_len,
+                                        rsrc, n, base, lane, ng, emax, raw_mode, st, sc, acc);
+    }
+    if (err == 0 && ng > 0) {
+        if (st.pos != off + glen)
+            err = ZC_REASON_LENGTH;
+        else if (st.seen_max != emax)
+            err = ZC_REASON_EMAX;
+        else if (!raw_mode && st.esc_min < kEsc)
+            err = ZC_REASON_ESCAPE;
+        else if (raw_mode && st.raw_coded < 8 * ng)
+            err = ZC_REASON_RAWMODE;
+    }
+    const uint64_t bad = __ballot(err != 0);
+    if (bad) {
+        const int first = __ffsll(static_cast<unsigned long long>(bad)) - 1;
+        const int reason = __shfl(err, first);
+        if (lane == 0)
+            report(status, reason, c);
+    }
+}
+
+// Tile position blockIdx.x of every stream in tab, decoded and summed in
+// chunk order (fp32 sums, or each rounded once to bf16).  128 VGPRs (four
+// waves per SIMD) and 68 KiB of LDS: two workgroups per compute unit.
+template <bool BF16OUT>
+__global__ __launch_bounds__(kSumBlock, kSumMinWaves)
+void zc_decode_sum_fused_kernel(const uint8_t* __restrict__ in, int32_t* __restrict__ status,
+                                SumTable tab, void* __restrict__ out)
+{
+    __shared__ __align__(16) uint32_t s_stage[kSumWaves][kStageAlloc];
+    __shared__ __align__(16) uint16_t s_step[2 * kSumWaves * 2 * kLanes * 8];
+    __shared__ __align__(16) uint8_t s_lut8[kLutRaw + 256];
+    __shared__ uint16_t s_tail[1 << kTailBits];
+    __shared__ uint8_t s_len[256];
+
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & (kLanes - 1);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kLanes);
+    for (uint32_t i = tid; i < static_cast<uint32_t>(kLutWords); i += kSumBlock)
+        reinterpret_cast<uint32_t*>(s_lut8)[i] = reinterpret_cast<const uint32_t*>(c_lut)[i];
+    if (tid < 256) {
+        s_lut8[kLutRaw + tid] = static_cast<uint8_t>(255u - tid);
+        const uint32_t sy = tid < static_cast<uint32_t>(kEsc) ? tid : static_cast<uint32_t>(kEsc);
+        s_len[tid] = static_cast<uint8_t>(len_of(sy) + (sy == static_cast<uint32_t>(kEsc) ? 8 : 0));
+    }
+    if (tid < (1u << kTailBits))
+        s_tail[tid] = static_cast<uint16_t>(tail_of(tid));
+    __syncthreads();
+
+    const uint32_t n = tab.n;
+    const uint32_t t = blockIdx.x;
+    const bool full = n - t * kTile >= static_cast<uint32_t>(kTile);
+    float acc[kSteps];
+#pragma unroll
+    for (int k = 0; k < kSteps; ++k)
+        acc[k] = 0.0f;
+    for (int32_t r0 = 0; r0 < tab.nstreams; r0 += kSumWaves) {
+        const int32_t c = r0 + static_cast<int32_t>(wave);
+        const SumCtx sc{s_step, wave, tid, static_cast<uint32_t>(min(kSumWaves, tab.nstreams - r0))};
+        if (c < tab.nstreams) {
+            const uint8_t* src = in + tab.boff[c];
+            if (full)
+                decode_tile_sum<true>(src, status, c, n, t, tab.bavail[c], lane, s_stage[wave],
+                                      s_lut8, s_tail, s_len, sc, acc);
+            else
+                decode_tile_sum<false>(src, status, c, n, t, tab.bavail[c], lane, s_stage[wave],
+                                       s_lut8, s_tail, s_len, sc, acc);
+        } else {
+            idle_sum(sc, acc);
+        }
+    }
+    // acc[2e], acc[2e + 1]: values 2p, 2p + 1 of step 2e + tid / 256
+#pragma unroll
+    for (int e = 0; e < kSteps / 2; ++e) {
+        const uint32_t i = t * kTile + (2 * e + (tid >> 8)) * 512 + 2 * (tid & 255);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (i + j < n) {
+                if (BF16OUT)
+                    static_cast<uint16_t*>(out)[i + j] = static_cast<uint16_t>(f32_to_bf16_rne(acc[2 * e + j]));
+                else
+                    __builtin_nontemporal_store(acc[2 * e + j], static_cast<float*>(out) + i + j);
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------ device-resident split
 
 __device__ inline uint64_t wave_excl_scan64(uint64_t x, uint32_t lane, uint64_t* total)
@@ -2052,6 +2450,13 @@ uint64_t reduce_stride(uint64_t n, int32_t num_chunks)
     return std::min<uint64_t>(tiles * kTile, (n + 7) & ~7ull);
 }
 
+// Decode and sum in one kernel, nothing staged (zc_decode_sum_fused_kernel).
+bool reduce_fused(uint64_t n, int32_t num_chunks)
+{
+    return num_chunks >= kSumWaves && num_chunks <= kMaxChunks &&
+           (n + kTile - 1) / kTile >= kSumMinTiles;
+}
+
 // More than one slab of at most 64 streams: each launch decodes one slab
 // and sums the one before, so two slab buffers alternate.
 bool reduce_pipelined(uint64_t n, int32_t num_chunks)
@@ -2059,9 +2464,11 @@ bool reduce_pipelined(uint64_t n, int32_t num_chunks)
     return num_chunks > 0 && num_chunks <= kMaxChunks && n > reduce_stride(n, num_chunks);
 }
 
-// Scratch bytes of zc_decompress_reduce.
+// Scratch bytes of zc_decompress_reduce (none for the fused form).
 uint64_t reduce_scratch(uint64_t n, int32_t num_chunks)
 {
+    if (reduce_fused(n, num_chunks))
+        return 0;
     return 2ull * reduce_stride(n, num_chunks) * static_cast<uint64_t>(num_chunks) *
            (reduce_pipelined(n, num_chunks) ? 2u : 1u);
 }
@@ -2138,12 +2545,14 @@ int decompress_chunks(const void* d_in, size_t in_bytes, const int64_t* in_offse
 }
 
 // Decode num_chunks streams of n values and sum them (fp32 output, or bf16
-// when `bf16`), slab by slab: each slab is a run of whole tiles of every
-// stream, decoded into a slab buffer (contribution c at c stride) and summed
-// while it is still in the device's last-level cache.  With up to 64
-// streams, launch i decodes slab i into buffer i % 2 and sums slab i - 1
-// from the other buffer (the sum's workgroups run as the decode drains);
-// with more, each slab is decoded (64 streams per launch) and then summed.
+// when `bf16`).  With 8 to 64 streams of at least kSumMinTiles tiles, one
+// launch decodes and sums with nothing staged.  Otherwise slab by slab: each
+// slab is a run of whole tiles of every stream, decoded into a slab buffer
+// (contribution c at c stride) and summed while it is still in the device's
+// last-level cache.  With up to 64 streams, launch i decodes slab i into
+// buffer i % 2 and sums slab i - 1 from the other buffer (the sum's
+// workgroups run as the decode drains); with more, each slab is decoded (64
+// streams per launch) and then summed.
 int decompress_reduce(const void* d_in, size_t in_bytes, const int64_t* in_offsets, int64_t n,
                       int32_t num_chunks, void* d_out, bool bf16, int32_t* d_status,
                       void* d_scratch, size_t scratch_bytes, void* stream)
@@ -2152,17 +2561,44 @@ int decompress_reduce(const void* d_in, size_t in_bytes, const int64_t* in_offse
         return ZC_EINVAL;
     if (n == 0)
         return ZC_OK;
-    if (!d_out || !d_status || (num_chunks > 0 && (!d_in || !d_scratch)))
+    const uint64_t need = reduce_scratch(static_cast<uint64_t>(n), num_chunks);
+    if (!d_out || !d_status || (num_chunks > 0 && (!d_in || (need > 0 && !d_scratch))))
         return ZC_EINVAL;
     if ((reinterpret_cast<uintptr_t>(d_out) & 15) || (reinterpret_cast<uintptr_t>(d_scratch) & 15))
         return ZC_EINVAL;
+    if (scratch_bytes < need)
+        return ZC_ENOSPC;
+    if (reduce_fused(static_cast<uint64_t>(n), num_chunks)) {
+        const uint8_t* in = static_cast<const uint8_t*>(d_in);
+        const uint64_t slot_bytes = align256(chunk_bound(static_cast<uint64_t>(n)));
+        SumTable tab;
+        std::memset(&tab, 0, sizeof tab);
+        tab.nstreams = num_chunks;
+        tab.n = static_cast<uint32_t>(n);
+        for (int32_t c = 0; c < num_chunks; ++c) {
+            const int64_t off = in_offsets ? in_offsets[c] : static_cast<int64_t>(c * slot_bytes);
+            if (off < 0 || (off & 15) || static_cast<uint64_t>(off) + 32 > in_bytes)
+                return ZC_EINVAL;
+            tab.boff[c] = static_cast<uint64_t>(off);
+            tab.bavail[c] = in_bytes - static_cast<uint64_t>(off);
+        }
+        if ((reinterpret_cast<uintptr_t>(d_in) & 15) || (reinterpret_cast<uintptr_t>(d_status) & 3))
+            return ZC_EINVAL;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        const dim3 grid(static_cast<uint32_t>((static_cast<uint64_t>(n) + kTile - 1) / kTile));
+        if (bf16)
+            hipLaunchKernelGGL(zc_decode_sum_fused_kernel<true>, grid, dim3(kSumBlock), 0, s, in,
+                               d_status, tab, d_out);
+        else
+            hipLaunchKernelGGL(zc_decode_sum_fused_kernel<false>, grid, dim3(kSumBlock), 0, s, in,
+                               d_status, tab, d_out);
+        return hipGetLastError() == hipSuccess ? ZC_OK : ZC_EHIP;
+    }
     const uint64_t stride = reduce_stride(static_cast<uint64_t>(n), num_chunks);
     const uint64_t T = (static_cast<uint64_t>(n) + kTile - 1) / kTile;
     const uint64_t slab_tiles = (stride + kTile - 1) / kTile;
     const uint64_t slabs = (T + slab_tiles - 1) / slab_tiles;
     const uint64_t buf_values = stride * static_cast<uint64_t>(num_chunks);
-    if (scratch_bytes < reduce_scratch(static_cast<uint64_t>(n), num_chunks))
-        return ZC_ENOSPC;
     if (reduce_pipelined(static_cast<uint64_t>(n), num_chunks)) {
         const uint8_t* in = static_cast<const uint8_t*>(d_in);
         const uint64_t slot_bytes = align256(chunk_bound(static_cast<uint64_t>(n)));

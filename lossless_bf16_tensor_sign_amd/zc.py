@@ -254,7 +254,10 @@ def zc_decompress_reduce(d_in, n, num_chunks, d_out, d_status, d_scratch, in_off
     """Queue decode of num_chunks streams of n values and their fp32 sum
     (rounded once to bf16 into a 16-bit d_out when bf16=True)."""
     nb = d_in.numel() * d_in.element_size() if in_bytes is None else in_bytes
-    sb = d_scratch.numel() * d_scratch.element_size() if scratch_bytes is None else scratch_bytes
+    if scratch_bytes is None:
+        sb = 0 if d_scratch is None else d_scratch.numel() * d_scratch.element_size()
+    else:
+        sb = scratch_bytes
     off, op = _offsets(in_offsets, num_chunks)
     fn = lib().zc_decompress_reduce_bf16 if bf16 else lib().zc_decompress_reduce
     return int(fn(_ptr(d_in), nb, op, int(n), int(num_chunks), _ptr(d_out), _ptr(d_status),
@@ -386,8 +389,8 @@ def decompress_reduce(buf, n, num_chunks, in_offsets=None, stream=None, check=Tr
         out = torch.empty(max(int(n), 8), dtype=torch.int16 if bf16 else torch.float32,
                           device=dev)
         status = torch.zeros(1, dtype=torch.int32, device=dev)
-        scratch = torch.empty(max(zc_reduce_scratch_bytes(n, num_chunks), 16),
-                              dtype=torch.uint8, device=dev)
+        need = zc_reduce_scratch_bytes(n, num_chunks)
+        scratch = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
         r = zc_decompress_reduce(buf, n, num_chunks, out, status, scratch,
                                  in_offsets=in_offsets, stream=stream, bf16=bf16)
         if r != ZC_OK:

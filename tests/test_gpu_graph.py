@@ -95,11 +95,13 @@ def test_graph_replays_compress_and_decompress():
         assert torch.equal(other, out_e), r
 
 
+@pytest.mark.parametrize("n", [(1 << 20) + 8192 + 33, 512 * 8192])
 @pytest.mark.parametrize("bf16", [False, True])
-def test_graph_replays_decode_sum(bf16):
+def test_graph_replays_decode_sum(bf16, n):
     # the receive side of a compressed reduce-scatter: 8 contributions of one
-    # shard with a ragged end, decoded and summed in chunk order
-    n, c = (1 << 20) + 8192 + 33, 8
+    # shard, decoded and summed in chunk order (a ragged shard in slabs, and
+    # one of 512 tiles decoded and summed in one kernel)
+    c = 8
     w = np.concatenate([synth.chunk(3, i)[:n] for i in range(c)])
     x = torch.from_numpy(np.ascontiguousarray(w).view(np.int16)).to(DEV)
     cnt = np.full(c, n, np.int64)

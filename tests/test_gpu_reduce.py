@@ -265,3 +265,77 @@ def test_reduce_bf16_full_size_gradient_buffer(oracle):
     # every position against the oracle
     got = out.cpu().numpy().view(np.uint16)
     assert np.array_equal(got, oracle.reduce_bf16_bf16(w, n, c))
+
+
+# ---- decode and sum in one kernel (8 to 64 streams of at least 512 tiles) ----
+
+FUSED_N = 512 * 8192 - 77                 # 512 tile positions, the last one partial
+
+
+def test_reduce_fused_two_rounds_ragged(oracle):
+    # 13 streams: a round of 8 and a round of 5 with three waves idle, a
+    # partial last tile, special values and random patterns (raw groups,
+    # escapes); fp32 and bf16 sums at every position
+    c, n = 13, FUSED_N
+    assert zc.zc_reduce_scratch_bytes(n, c) == 0
+    w = special_mix(n * c, 79)
+    say("reduce fused n=%d chunks=%d" % (n, c))
+    buf, _ = zc.compress(to_dev(w), [n] * c)
+    out, st = zc.decompress_reduce(buf, n, c, check=False)
+    out16, st16 = zc.decompress_reduce(buf, n, c, check=False, bf16=True)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and int(st16.item()) == 0
+    same_f32(out.cpu().numpy(), oracle.reduce_bf16_f32(w, n, c))
+    assert np.array_equal(out16.cpu().numpy().view(np.uint16), oracle.reduce_bf16_bf16(w, n, c))
+
+
+def test_reduce_fused_all_raw_tiles(oracle):
+    # uniform random bits: every group raw, every tile stream 8 KiB, decoded
+    # from global memory
+    c, n = 8, 512 * 8192
+    w = np.random.default_rng(80).integers(0, 1 << 16, n * c, dtype=np.uint16)
+    say("reduce fused, random bits, n=%d chunks=%d" % (n, c))
+    st, got = gpu_reduce(w, n, c)
+    assert st == 0, "status %#x" % st
+    same_f32(got, oracle.reduce_bf16_f32(w, n, c))
+
+
+def test_reduce_fused_streams_at_given_offsets(oracle):
+    # the streams taken in another order through in_offsets: the sums follow
+    # the call's order
+    c, n = 9, FUSED_N
+    w = synth.gaussian_bits(n * c, 0.02, 81)
+    buf, _ = zc.compress(to_dev(w), [n] * c)
+    off, _ = oracle.slot_offsets([n] * c)
+    perm = np.array([4, 0, 8, 2, 7, 1, 5, 3, 6])
+    say("reduce fused, permuted offsets")
+    out, st = zc.decompress_reduce(buf, n, c, in_offsets=np.asarray(off)[perm], check=False)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    wp = w.reshape(c, n)[perm].reshape(-1)
+    same_f32(out.cpu().numpy(), oracle.reduce_bf16_f32(wp, n, c))
+
+
+@pytest.mark.parametrize("stream,what", [(3, "header"), (10, "tile")])
+def test_reduce_fused_reports_corrupt_stream(oracle, stream, what):
+    # a broken header in the first round, a broken tile index entry of the
+    # last tile in the second round
+    c, n = 13, FUSED_N
+    w = synth.gaussian_bits(n * c, 0.02, 82)
+    buf, _ = zc.compress(to_dev(w), [n] * c)
+    torch.cuda.synchronize()
+    hb = buf.cpu().numpy().copy()
+    off, _ = oracle.slot_offsets([n] * c)
+    T = (n + 8191) // 8192
+    if what == "header":
+        hb[off[stream]] ^= 0xFF
+    else:
+        p = off[stream] + 32 + 4 * (T - 1)
+        hb[p:p + 4] = np.frombuffer(np.uint32(0xFFFFFF00).tobytes(), np.uint8)
+    say("reduce fused, corrupt %s of stream %d" % (what, stream))
+    out, status = zc.decompress_reduce(torch.from_numpy(hb).to(DEV), n, c, check=False)
+    torch.cuda.synchronize()
+    st = int(status.item())
+    assert st != 0 and (st & 0xFFFFFF) == stream, hex(st)
+    if what == "header":
+        assert st >> 24 == 1, hex(st)
