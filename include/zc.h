@@ -286,10 +286,11 @@ int zc_decompress_dev(const void* d_in, size_t in_bytes,
  *               there, one or two slabs at a time; caller-owned, contents
  *               undefined after
  *   stream      hipStream_t; every launch is queued on it
- * With 8 to 64 streams of at least 512 tiles (n > 511 * 8192), one launch
- * decodes and sums with nothing staged: a workgroup per tile position
- * decodes that tile of eight streams at a time and adds them in LDS, in
- * chunk order.  Otherwise the shard is processed in slabs of whole
+ * With 8 to 64 streams of T = ceil(n / 8192) >= 512 tiles, where T is at
+ * least 27/32 of ceil(T / 512) * 512 (a launch runs 512 tile positions at
+ * once), one launch decodes and sums with nothing staged: a workgroup per
+ * tile position decodes that tile of eight streams at a time and adds them
+ * in LDS, in chunk order.  Otherwise the shard is processed in slabs of whole
  * 8192-value tiles, about 128 MiB of staged values per slab over all
  * streams, so that a slab is summed while it is still in the device's
  * 256 MB last-level cache.  With at most 64 streams and more than one slab,
@@ -305,8 +306,8 @@ int zc_decompress_reduce(const void* d_in, size_t in_bytes,
 
 /*
  * Scratch bytes that zc_decompress_reduce and zc_decompress_reduce_bf16 need
- * for num_chunks streams of n values: 0 when one launch decodes and sums (8
- * to 64 streams of at least 512 tiles); otherwise 2 num_chunks s per slab
+ * for num_chunks streams of n values: 0 when one launch decodes and sums
+ * (see zc_decompress_reduce); otherwise 2 num_chunks s per slab
  * buffer, where s (values per stream per slab) is n rounded up to 8 when
  * one slab holds the whole shard (one buffer), else the slab's whole tiles
  * (two buffers for at most 64 streams, one for more).  At most about

@@ -1778,10 +1778,13 @@ void zc_decode_sum_kernel(const uint8_t* __restrict__ in, uint16_t* __restrict__
 constexpr int kSumWaves = 8;                     // streams decoded together
 constexpr int kSumBlock = kSumWaves * kLanes;    // threads: two values of one of two steps each
 constexpr int kSumMinWaves = 4;                  // occupancy target, waves per SIMD
-// The fused form is taken for 8 to 64 streams of at least this many tiles:
-// two workgroups for each of the 256 compute units.  Its parallelism is
-// 8 waves per tile position, and each wave decodes ceil(C / 8) tiles one
-// after another, so short shards (fewer positions) are faster staged.
+// Tile positions that run at once: two workgroups for each of the 256
+// compute units.  The fused form's parallelism is 8 waves per tile
+// position, and each wave decodes ceil(C / 8) tiles one after another, so a
+// launch takes about the same time for every generation of 512 positions,
+// however full; the staged form's time grows with the tile count.  The
+// fused form is taken for 8 to 64 streams when its generations are at
+// least 27/32 full (measured break-even: 864 positions, 2 generations).
 constexpr uint64_t kSumMinTiles = 512;
 
 // The streams of one fused call.
@@ -2453,8 +2456,10 @@ uint64_t reduce_stride(uint64_t n, int32_t num_chunks)
 // Decode and sum in one kernel, nothing staged (zc_decode_sum_fused_kernel).
 bool reduce_fused(uint64_t n, int32_t num_chunks)
 {
-    return num_chunks >= kSumWaves && num_chunks <= kMaxChunks &&
-           (n + kTile - 1) / kTile >= kSumMinTiles;
+    const uint64_t T = (n + kTile - 1) / kTile;
+    const uint64_t gens = (T + kSumMinTiles - 1) / kSumMinTiles;
+    return num_chunks >= kSumWaves && num_chunks <= kMaxChunks && T >= kSumMinTiles &&
+           T * 32 >= gens * kSumMinTiles * 27;
 }
 
 // More than one slab of at most 64 streams: each launch decodes one slab
@@ -2545,8 +2550,9 @@ int decompress_chunks(const void* d_in, size_t in_bytes, const int64_t* in_offse
 }
 
 // Decode num_chunks streams of n values and sum them (fp32 output, or bf16
-// when `bf16`).  With 8 to 64 streams of at least kSumMinTiles tiles, one
-// launch decodes and sums with nothing staged.  Otherwise slab by slab: each
+// when `bf16`).  With 8 to 64 streams of at least kSumMinTiles tiles that
+// fill the fused kernel's generations (reduce_fused), one launch decodes and
+// sums with nothing staged.  Otherwise slab by slab: each
 // slab is a run of whole tiles of every stream, decoded into a slab buffer
 // (contribution c at c stride) and summed while it is still in the device's
 // last-level cache.  With up to 64 streams, launch i decodes slab i into

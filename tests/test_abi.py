@@ -67,17 +67,19 @@ def test_reduce_scratch_bytes():
     assert zc.zc_reduce_scratch_bytes(4096, 4) == 2 * 4096 * 4
     assert zc.zc_reduce_scratch_bytes(20003, 8) == 2 * 20008 * 8
     assert zc.zc_reduce_scratch_bytes(1, 5) == 2 * 8 * 5
-    # 8 to 64 streams of at least 512 tiles are decoded and summed in one
-    # kernel with nothing staged
+    # 8 to 64 streams of at least 512 tiles, in generations of 512 tile
+    # positions at least 27/32 full, are decoded and summed in one kernel
+    # with nothing staged
     tiles512 = 512 * 8192
     for n, c in [(tiles512, 8), (tiles512 - 8191, 64), (1 << 22, 64), (1 << 26, 13),
-                 ((1 << 31) - 1, 64)]:
+                 ((1 << 31) - 1, 64), (864 * 8192, 64), (1408 * 8192 - 5, 8)]:
         assert zc.zc_reduce_scratch_bytes(n, c) == 0, (n, c)
     # otherwise slabs of whole 8192-value tiles per stream, about 128 MiB
     # over all streams: two slab buffers for at most 64 streams, one for more
     slab = 128 << 20
     for n, c in [(tiles512 - 8192, 64), ((1 << 21) + 77, 64), (1 << 25, 3), (1 << 27, 1),
-                 (1 << 22, 7), (1 << 22, 65), (1 << 22, 4096)]:
+                 (1 << 22, 7), (1 << 22, 65), (1 << 22, 4096), (600 * 8192, 64),
+                 (863 * 8192, 64), (1152 * 8192, 16)]:
         b = zc.zc_reduce_scratch_bytes(n, c)
         bufs = 2 if c <= 64 else 1
         per = b // (2 * c * bufs)
