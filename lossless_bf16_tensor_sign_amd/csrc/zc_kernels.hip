@@ -36,7 +36,11 @@
 //    a loop or across the encoder's emission: on this hardware the wait for
 //    such a load also waits for every older store of the wave.
 // The codec itself is integer arithmetic; only the decode + sum of a
-// reduce-scatter's received copies adds in fp32.
+// reduce-scatter's received copies adds in fp32.  For a long shard of 8 to
+// 64 received copies that sum runs in one kernel: a workgroup per tile
+// position decodes that tile of eight copies at a time and adds them
+// through LDS in chunk order, with nothing staged in memory; other shapes
+// decode into slab buffers and sum them.
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -278,7 +282,6 @@ __device__ inline void st_nt2(void* p, uint2 v)
 struct __align__(16) EncTables {
     uint32_t esc[256];
     uint32_t pcode[256];  // member pair (d0, d1 < 16) at index d0 | d1 << 4: code words back to back
-    uint16_t code[256];   // code word of d (the escape code for d >= 16)
     uint8_t len[256];     // coded length of d, escape payload included
     uint8_t plen[256];    // the pair's total length (at most 28)
 };
@@ -292,7 +295,6 @@ __host__ __device__ constexpr EncTables make_enc_tables()
     for (int i = 0; i < 256; ++i) {
         const int sym = i < kEsc ? i : kEsc;
         uint32_t code = kCodeT1[sym], len = kLenT1[sym];
-        t.code[i] = static_cast<uint16_t>(code);
         if (sym == kEsc) {      // escape: code word, then 8 exponent bits
             code <<= 8;
             len += 8;
