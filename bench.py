@@ -96,6 +96,27 @@ def read_traffic(workload_name):
     return out
 
 
+def device_info():
+    """The GPU and the software of the run; the peak engine and memory clocks
+    come from the HIP runtime (hipDeviceAttributeClockRate = 5 and
+    hipDeviceAttributeMemoryClockRate = 60 in hip_runtime_api.h, kHz)."""
+    import ctypes
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "gcn_arch": p.gcnArchName, "compute_units": p.multi_processor_count,
+            "hbm_GiB": round(p.total_memory / 2**30, 1), "l2_MiB": round(p.L2_cache_size / 2**20, 1),
+            "hip_runtime": torch.version.hip, "torch": torch.__version__}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int()
+        for key, attr in (("peak_engine_clock_MHz", 5), ("peak_memory_clock_MHz", 60)):
+            if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, 0) == 0:
+                info[key] = v.value // 1000
+    except OSError:
+        pass
+    return info
+
+
 def host_cpu():
     """CPU model name and core counts of this host (from /proc/cpuinfo and the
     scheduler's affinity mask)."""
@@ -502,6 +523,8 @@ def main():
         "decompress_ms": round(d_mean * 1e3, 4),
         "compress_ms_median": round(float(np.median(tc)) * 1e3, 4),
         "decompress_ms_median": round(float(np.median(td)) * 1e3, 4),
+        "compress_ms_min": round(float(np.min(tc)) * 1e3, 4),
+        "decompress_ms_min": round(float(np.min(td)) * 1e3, 4),
         "ratio": round(ratio, 5),
         "saving": round(1.0 - comp / in_bytes, 5),
         "comp_bytes": comp,
@@ -528,6 +551,7 @@ def main():
         },
         "wall_s_timed_region": round(t_wall, 4),
         "kernel_sources_sha256": kernel_sources_sha256(),
+        "device": device_info(),
     }
 
     # sampled size estimate (8 tiles per chunk) and the switch's break-even
