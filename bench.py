@@ -249,7 +249,11 @@ def time_pipeline(args, x, counts, dev, evict, ev):
 def measure_workload(wl, steps, warmup, dev, stream, evict, ev):
     """Compress and decompress timings of workload wl with host chunk counts,
     measured the way the headline workload is (cache flush before each call,
-    HIP events on the library's stream), and its round trip checked."""
+    HIP events on the library's stream), and its round trip checked.  For a
+    workload of equal chunks (the gradient reduce-scatter buffer) the decode
+    and chunk-order fp32 sum of its streams (zc_decompress_reduce, the
+    receive side of a compressed reduce-scatter) is timed the same way and
+    checked against chunk-order PyTorch fp32 additions."""
     import numpy as np
     import torch
     from lossless_bf16_tensor_sign_amd import synth, zc
@@ -303,6 +307,40 @@ def measure_workload(wl, steps, warmup, dev, stream, evict, ev):
             "decompress": round(100 * alg / d_s / 1e9 / HBM_PEAK_GBPS, 2),
         },
     }
+    if wl == 3 and np.all(counts == counts[0]):
+        shard, c = int(counts[0]), int(len(counts))
+        need = zc.zc_reduce_scratch_bytes(shard, c)
+        scratch = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+        red = torch.empty(shard, dtype=torch.float32, device=dev)
+        tr = []
+        for i in range(warmup + steps):
+            evict(i + 33)
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            r = zc.zc_decompress_reduce(buf, shard, c, red, status, scratch, stream=stream)
+            e1.record(stream)
+            if r != zc.ZC_OK:
+                raise zc.ZcError(r, "zc_decompress_reduce")
+            if i >= warmup:
+                tr.append((e0, e1))
+        torch.cuda.synchronize()
+        acc = torch.zeros(shard, dtype=torch.float32, device=dev)
+        for k in range(c):
+            acc = acc + (x[k * shard:(k + 1) * shard].to(torch.int32) << 16).view(torch.float32)
+        same = (acc.view(torch.int32) == red.view(torch.int32)) | (acc.isnan() & red.isnan())
+        if int(status.item()) != 0 or not bool(same.all()):
+            log("DECODE + SUM FAILED on workload %d" % wl)
+            sys.exit(1)
+        r_s = float(np.mean([a.elapsed_time(b) for a, b in tr])) * 1e-3
+        out["decode_sum"] = {
+            "streams": c,
+            "values_per_stream": shard,
+            "form": "one kernel" if need == 0 else "slabs",
+            "scratch_bytes": need,
+            "ms": round(r_s * 1e3, 4),
+            "ms_median": round(float(np.median([a.elapsed_time(b) for a, b in tr])), 4),
+            "GBps_received": round(2 * n / r_s / 1e9, 2),
+        }
     log("workload %d: %s" % (wl, out))
     return out
 
